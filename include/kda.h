@@ -1,0 +1,178 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention layer library.
+ *
+ * The layer (TensorFold issue #850, "Ling-3.1-flash on CUDA", the comment that
+ * describes the shared KDA module; onnxruntime-genai PR #2843, the op list in
+ * its description) takes a model's projected rows and runs, per head:
+ *   1. a causal short conv over the q, k and v rows, with the last W-1 rows
+ *      carried across calls in a conv state (CausalConvWithState /
+ *      VarlenCausalConvWithState in PR #2843), then SiLU;
+ *   2. L2 normalisation of q and k over the key dimension;
+ *   3. a per-key-dimension log-decay gate g (softplus: g = -softplus(x); safe:
+ *      g = lower_bound * sigmoid(x), PR #2843 gate_activation='sigmoid' with
+ *      gate_lower_bound), decay a = e^g, and a per-head beta = sigmoid(x_b);
+ *   4. the gated delta rule on one fp32 d_k x d_v state per (sequence, head):
+ *        S_t = (I - beta_t k_t k_t^T) Diag(a_t) S_{t-1} + beta_t k_t v_t^T,
+ *        o_t = S_t^T q_t;
+ *   5. the sigmoid-gated output RMSNorm y = o / sqrt(mean(o^2) + eps) * w *
+ *      sigmoid(z) (GatedRMSNorm with activation 'sigmoid' in PR #2843).
+ * Prompt rows run chunk-parallel (64-row chunks anchored at each sequence's
+ * first row); decode rows and speculative verify windows run row by row, and a
+ * verify window logs each row's decay, normalised key and update so that a
+ * later call can commit the accepted rows (TensorFold #850: a window's rows
+ * replay from that log with the same bits as rows decoded one at a time).
+ *
+ * Conventions shared by every entry point
+ *   - Memory: the caller owns every buffer (device memory unless stated); the
+ *     library never allocates.  Scratch comes from a caller workspace.
+ *   - Streams: every call is enqueued on `stream` and returns without waiting.
+ *   - Layouts: row-major, token-major packed rows.
+ *       q, k, g rows      [T, H, d_k]      v, z, o rows   [T, H, d_v]
+ *       beta logits       [T, H]
+ *       state             [S_slots, H, d_k, d_v]  fp32, d_v contiguous
+ *       conv channels     C = H*(2*d_k + d_v), ordered [q: H*d_k | k: H*d_k | v: H*d_v]
+ *       conv weight       [C, 4] fp32, tap 3 multiplies the current row
+ *       conv state        [S_slots, 3, C] in the raw-row dtype, oldest row first
+ *   - Slots: `slots` (int32 [num_seqs or batch], device) maps sequence n to its
+ *     row of `state` / `conv_state`; NULL means slot n.  A negative slot skips
+ *     the sequence: nothing of it is read or written.
+ *   - Alignment: buffers the kernels move with 128-bit accesses must be 16-byte
+ *     aligned: the state, the fp32 rows q_hat/k_hat/v/g of the prompt path, the
+ *     outputs o of decode and verify, a log's u, and every buffer of
+ *     gated_rmsnorm_out.  Every other pointer needs its element alignment.
+ *   - Errors: each call returns KDA_OK or one KDA_E_* code.  All validation
+ *     happens before the first launch; on error nothing is enqueued and no
+ *     output is written.  kda_last_error() gives a message (thread-local).
+ *   - Device-side contents (cu_seqlens monotone with cu[0]=0 and cu[N]=T, slots
+ *     below the pool size, commit counts within the logged window) are
+ *     preconditions the library does not read back.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+enum kda_status {
+  KDA_OK = 0,
+  KDA_E_ARG = 1,       /* null pointer or negative size */
+  KDA_E_GEOMETRY = 2,  /* d_k or d_v not in {64, 128}, conv width != 4, window not in [0, 8] */
+  KDA_E_ALIGN = 3,     /* a pointer is not aligned as its access needs (see Alignment) */
+  KDA_E_GATE = 4,      /* unknown gate mode, or safe mode with a lower bound that is not finite and < 0 */
+  KDA_E_DTYPE = 5,     /* unknown dtype, activation or precision policy */
+  KDA_E_WORKSPACE = 6, /* workspace missing or smaller than kda_prefill_workspace_bytes() */
+  KDA_E_HIP = 7        /* a HIP launch failed */
+};
+
+enum kda_dtype { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 };
+enum kda_gate { KDA_GATE_SOFTPLUS = 0, KDA_GATE_SAFE = 1 };
+enum kda_act { KDA_ACT_NONE = 0, KDA_ACT_SILU = 1 };
+/* Arithmetic of the chunked prompt path's matrix products (all accumulate in fp32):
+ *   FP32   fp32 matrix-core products;
+ *   BF16X3 each fp32 operand split into bf16 hi + lo and the product formed as
+ *          hi*hi + hi*lo + lo*hi (relative error about 2^-16 per product). */
+enum kda_precision { KDA_PREC_FP32 = 0, KDA_PREC_BF16X3 = 1 };
+
+typedef struct kda_dims {
+  int32_t num_heads;  /* H >= 1 */
+  int32_t head_dim_k; /* d_k in {64, 128} */
+  int32_t head_dim_v; /* d_v in {64, 128} */
+  int32_t conv_width; /* must be 4 */
+  int32_t in_dtype;   /* kda_dtype of raw rows (q, k, v, g, beta logits) and of the conv state */
+  int32_t conv_act;   /* kda_act applied after the conv */
+  int32_t precision;  /* kda_precision of the prompt path's matrix products */
+} kda_dims;
+
+/* Log of a verify window: everything a later call needs to commit its rows.
+ * Device buffers; `window` is the row count they were written with. */
+typedef struct kda_log {
+  float* a;        /* [B, window, H, d_k] per-row decay e^g */
+  float* k_hat;    /* [B, window, H, d_k] per-row L2-normalised key */
+  float* u;        /* [B, window, H, d_v] per-row update beta*(v - (Diag(a)S)^T k_hat) */
+  void* conv_rows; /* [B, window, C] raw conv input rows (in_dtype), conv channel order */
+  int32_t window;  /* rows per sequence in this log, 0..8 */
+} kda_log;
+
+/* kda_prep -- preamble of the prompt path (parts 1-3 above) for packed varlen rows.
+ *   cu_seqlens      int32 [num_seqs+1] device, packed row offsets
+ *   slots           int32 [num_seqs] device or NULL (conv_state row of each sequence)
+ *   q_raw,k_raw     [t_tot, H, d_k] in_dtype;  v_raw [t_tot, H, d_v];  g_raw [t_tot, H, d_k]
+ *   beta_logit      [t_tot, H] in_dtype
+ *   conv_weight     [C, 4] fp32
+ *   conv_state_in   [slots, 3, C] in_dtype, read;  conv_state_out  same shape, written
+ *                   after all reads (the two may be the same buffer)
+ *   gate_mode       kda_gate;  lower_bound used in safe mode only (finite, < 0)
+ *   outputs (fp32): q_hat, k_hat [t_tot,H,d_k]; v_out [t_tot,H,d_v]; g_out (log decay)
+ *                   [t_tot,H,d_k]; beta_out [t_tot,H]
+ * The outputs are what kda_prefill_varlen consumes. */
+int kda_prep(const kda_dims* d, int32_t num_seqs, int64_t t_tot, const int32_t* cu_seqlens, const int32_t* slots,
+             const void* q_raw, const void* k_raw, const void* v_raw, const float* conv_weight,
+             const void* conv_state_in, void* conv_state_out, const void* g_raw, const void* beta_logit,
+             int32_t gate_mode, float lower_bound, float* q_hat, float* k_hat, float* v_out, float* g_out,
+             float* beta_out, hipStream_t stream);
+
+/* Bytes of workspace kda_prefill_varlen needs for this geometry (an upper
+ * bound that depends only on num_seqs and t_tot). */
+size_t kda_prefill_workspace_bytes(const kda_dims* d, int32_t num_seqs, int64_t t_tot);
+
+/* kda_prefill_varlen -- the delta rule (part 4) over packed prompt rows, in
+ * 64-row chunks anchored at each sequence's first row (WY/UT form with an
+ * intra-chunk lower-triangular solve, then a sequential pass over chunks).
+ *   q_hat, k_hat, v, g, beta   fp32 outputs of kda_prep (g is the log decay)
+ *   state   fp32 [slots, H, d_k, d_v], read as the initial state and
+ *           overwritten with the final state of each sequence
+ *   o       fp32 [t_tot, H, d_v], pre-norm output
+ *   workspace  device scratch of at least kda_prefill_workspace_bytes(), 256-byte aligned
+ * A prompt cut at a multiple of 64 rows, with the state carried, gives the same
+ * bits as the uncut prompt. */
+int kda_prefill_varlen(const kda_dims* d, int32_t num_seqs, int64_t t_tot, const int32_t* cu_seqlens,
+                       const int32_t* slots, const float* q_hat, const float* k_hat, const float* v,
+                       const float* g, const float* beta, float* state, float* o, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
+/* kda_decode -- one row per sequence (parts 1-4 fused): conv step on the conv
+ * state, gates, norms, state step, readout.
+ *   q_raw,k_raw,g_raw [batch,H,d_k], v_raw [batch,H,d_v], beta_logit [batch,H]  (in_dtype)
+ *   state [slots,H,d_k,d_v] fp32 and conv_state [slots,3,C] (in_dtype) updated in place
+ *   o     fp32 [batch, H, d_v] */
+int kda_decode(const kda_dims* d, int32_t batch, const int32_t* slots, float* state, void* conv_state,
+               const float* conv_weight, const void* q_raw, const void* k_raw, const void* v_raw, const void* g_raw,
+               const void* beta_logit, int32_t gate_mode, float lower_bound, float* o, hipStream_t stream);
+
+/* kda_verify_window -- speculative verify window on top of committed state.
+ * First commits n_commit[b] rows (0..log_in->window) of the previous window
+ * from log_in: S = Diag(a) S + k_hat u^T per row and the conv state advances
+ * by those raw rows, bit for bit as kda_decode would have left them.  Then it
+ * runs `window` new rows per sequence row by row on a private copy of the
+ * committed state, writes their outputs o [batch, window, H, d_v] (same bits
+ * as kda_decode on those rows) and their log to log_out.  The state and conv
+ * state stay at the committed point.  window = 0 only commits.
+ *   n_commit  int32 [batch] device, or NULL when log_in is NULL (nothing to commit)
+ *   rows      q_raw,k_raw,g_raw [batch,window,H,d_k], v_raw [batch,window,H,d_v],
+ *             beta_logit [batch,window,H]  (in_dtype)
+ *   log_out   buffers sized for `window`; must not overlap log_in. */
+int kda_verify_window(const kda_dims* d, int32_t batch, int32_t window, const int32_t* slots, float* state,
+                      void* conv_state, const float* conv_weight, const int32_t* n_commit, const kda_log* log_in,
+                      const kda_log* log_out, const void* q_raw, const void* k_raw, const void* v_raw,
+                      const void* g_raw, const void* beta_logit, int32_t gate_mode, float lower_bound, float* o,
+                      hipStream_t stream);
+
+/* gated_rmsnorm_out -- part 5: y = o / sqrt(mean(o^2) + eps) * w * sigmoid(z)
+ * over rows of d_v values.
+ *   o fp32 [rows, d_v];  z [rows, d_v] of z_dtype;  w fp32 [d_v];  y [rows, d_v] of y_dtype */
+int gated_rmsnorm_out(int64_t rows, int32_t d_v, const float* o, const void* z, int32_t z_dtype, const float* w,
+                      float eps, void* y, int32_t y_dtype, hipStream_t stream);
+
+/* Message for the last error returned on this thread ("" if none). */
+const char* kda_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H */

@@ -1,0 +1,267 @@
+"""kimi_delta_attention_prep_amd -- Python binding of the gfx950 KDA library (libkda.so).
+
+Argument marshalling only: each function checks shapes and dtypes of torch
+tensors, passes their device pointers and torch's current HIP stream to the
+C entry point of the same name (include/kda.h), and raises KdaError on a
+non-zero status.  Every step of the layer runs in the library's HIP kernels;
+there is no fallback of any kind -- a missing library is an error.
+
+The layer (TensorFold issue #850, the shared KDA module; onnxruntime-genai PR
+#2843, the KDA ops): causal short conv with carried state + SiLU, q/k L2
+norms, softplus or lower-bounded sigmoid ("safe") log-decay gate, sigmoid
+beta, the gated delta rule S_t = (I - b k k^T) Diag(a) S_{t-1} + b k v^T with
+o_t = S_t^T q_t, and the sigmoid-gated output RMSNorm.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkda.so")
+
+KDA_OK, KDA_E_ARG, KDA_E_GEOMETRY, KDA_E_ALIGN, KDA_E_GATE, KDA_E_DTYPE, KDA_E_WORKSPACE, KDA_E_HIP = range(8)
+DTYPE_F32, DTYPE_BF16 = 0, 1
+GATE_SOFTPLUS, GATE_SAFE = 0, 1
+ACT_NONE, ACT_SILU = 0, 1
+PREC_FP32, PREC_BF16X3 = 0, 1
+EXPORTS = ("kda_prep", "kda_prefill_workspace_bytes", "kda_prefill_varlen", "kda_decode", "kda_verify_window",
+           "gated_rmsnorm_out", "kda_last_error")
+
+
+class KdaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"KDA error {code}: {msg}")
+        self.code = code
+
+
+class KdaDims(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("head_dim_k", ctypes.c_int32), ("head_dim_v", ctypes.c_int32),
+                ("conv_width", ctypes.c_int32), ("in_dtype", ctypes.c_int32), ("conv_act", ctypes.c_int32),
+                ("precision", ctypes.c_int32)]
+
+
+class KdaLog(ctypes.Structure):
+    _fields_ = [("a", ctypes.c_void_p), ("k_hat", ctypes.c_void_p), ("u", ctypes.c_void_p),
+                ("conv_rows", ctypes.c_void_p), ("window", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libkda.so (built by build.py); raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with `python -m kimi_delta_attention_prep_amd.build`")
+        lib = ctypes.CDLL(path)
+        vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+        D = ctypes.POINTER(KdaDims)
+        Lg = ctypes.POINTER(KdaLog)
+        lib.kda_prep.argtypes = [D, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp, vp, vp, vp, vp]
+        lib.kda_prefill_workspace_bytes.argtypes = [D, i32, i64]
+        lib.kda_prefill_workspace_bytes.restype = ctypes.c_size_t
+        lib.kda_prefill_varlen.argtypes = [D, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        lib.kda_decode.argtypes = [D, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp]
+        lib.kda_verify_window.argtypes = [D, i32, i32, vp, vp, vp, vp, vp, Lg, Lg, vp, vp, vp, vp, vp, i32, f32, vp, vp]
+        lib.gated_rmsnorm_out.argtypes = [i64, i32, vp, vp, i32, vp, f32, vp, i32, vp]
+        lib.kda_last_error.restype = ctypes.c_char_p
+        for f in ("kda_prep", "kda_prefill_varlen", "kda_decode", "kda_verify_window", "gated_rmsnorm_out"):
+            getattr(lib, f).restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _check(rc: int):
+    if rc != KDA_OK:
+        raise KdaError(rc, load_library().kda_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return DTYPE_F32
+    if dt == torch.bfloat16:
+        return DTYPE_BF16
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def _need(t, name, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+@dataclass(frozen=True)
+class Dims:
+    num_heads: int
+    head_dim_k: int
+    head_dim_v: int
+    in_dtype: torch.dtype = torch.bfloat16
+    conv_act: int = ACT_SILU
+    precision: int | None = None  # default: FP32 for fp32 rows, BF16X3 for bf16 rows
+
+    def c(self) -> KdaDims:
+        prec = self.precision
+        if prec is None:
+            prec = PREC_FP32 if self.in_dtype == torch.float32 else PREC_BF16X3
+        return KdaDims(self.num_heads, self.head_dim_k, self.head_dim_v, 4, _dtype_code(self.in_dtype), self.conv_act,
+                       prec)
+
+    @property
+    def conv_channels(self) -> int:
+        return self.num_heads * (2 * self.head_dim_k + self.head_dim_v)
+
+
+def kda_prep(d: Dims, cu_seqlens, q_raw, k_raw, v_raw, conv_weight, conv_state_in, conv_state_out, g_raw,
+             beta_logit, gate_mode, lower_bound, q_hat, k_hat, v_out, g_out, beta_out, slots=None):
+    lib = load_library()
+    T = q_raw.shape[0]
+    N = cu_seqlens.numel() - 1
+    H, dk, dv, dt = d.num_heads, d.head_dim_k, d.head_dim_v, d.in_dtype
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    for name, t, shp in (("q_raw", q_raw, (T, H, dk)), ("k_raw", k_raw, (T, H, dk)), ("v_raw", v_raw, (T, H, dv)),
+                         ("g_raw", g_raw, (T, H, dk)), ("beta_logit", beta_logit, (T, H))):
+        _need(t, name, dt, shp)
+    _need(conv_weight, "conv_weight", torch.float32, (d.conv_channels, 4))
+    _need(conv_state_in, "conv_state_in", dt)
+    _need(conv_state_out, "conv_state_out", dt, conv_state_in.shape)
+    for name, t, shp in (("q_hat", q_hat, (T, H, dk)), ("k_hat", k_hat, (T, H, dk)), ("v_out", v_out, (T, H, dv)),
+                         ("g_out", g_out, (T, H, dk)), ("beta_out", beta_out, (T, H))):
+        _need(t, name, torch.float32, shp)
+    if slots is not None:
+        _need(slots, "slots", torch.int32, (N,))
+    dims = d.c()
+    _check(lib.kda_prep(ctypes.byref(dims), N, T, _ptr(cu_seqlens), _ptr(slots), _ptr(q_raw), _ptr(k_raw),
+                        _ptr(v_raw), _ptr(conv_weight), _ptr(conv_state_in), _ptr(conv_state_out), _ptr(g_raw),
+                        _ptr(beta_logit), int(gate_mode), float(lower_bound), _ptr(q_hat), _ptr(k_hat), _ptr(v_out),
+                        _ptr(g_out), _ptr(beta_out), _stream()))
+
+
+def kda_prefill_workspace_bytes(d: Dims, num_seqs: int, t_tot: int) -> int:
+    dims = d.c()
+    return int(load_library().kda_prefill_workspace_bytes(ctypes.byref(dims), int(num_seqs), int(t_tot)))
+
+
+def kda_prefill_varlen(d: Dims, cu_seqlens, q_hat, k_hat, v, g, beta, state, o, workspace, slots=None):
+    lib = load_library()
+    T = q_hat.shape[0]
+    N = cu_seqlens.numel() - 1
+    H, dk, dv = d.num_heads, d.head_dim_k, d.head_dim_v
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    for name, t, shp in (("q_hat", q_hat, (T, H, dk)), ("k_hat", k_hat, (T, H, dk)), ("v", v, (T, H, dv)),
+                         ("g", g, (T, H, dk)), ("beta", beta, (T, H)), ("o", o, (T, H, dv))):
+        _need(t, name, torch.float32, shp)
+    _need(state, "state", torch.float32)
+    if state.dim() != 4 or tuple(state.shape[1:]) != (H, dk, dv):
+        raise ValueError(f"state must be [slots, {H}, {dk}, {dv}]")
+    _need(workspace, "workspace")
+    if slots is not None:
+        _need(slots, "slots", torch.int32, (N,))
+    dims = d.c()
+    _check(lib.kda_prefill_varlen(ctypes.byref(dims), N, T, _ptr(cu_seqlens), _ptr(slots), _ptr(q_hat), _ptr(k_hat),
+                                  _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream()))
+
+
+def kda_decode(d: Dims, state, conv_state, conv_weight, q_raw, k_raw, v_raw, g_raw, beta_logit, gate_mode,
+               lower_bound, o, slots=None):
+    lib = load_library()
+    B = q_raw.shape[0]
+    H, dk, dv, dt = d.num_heads, d.head_dim_k, d.head_dim_v, d.in_dtype
+    for name, t, shp in (("q_raw", q_raw, (B, H, dk)), ("k_raw", k_raw, (B, H, dk)), ("v_raw", v_raw, (B, H, dv)),
+                         ("g_raw", g_raw, (B, H, dk)), ("beta_logit", beta_logit, (B, H))):
+        _need(t, name, dt, shp)
+    _need(state, "state", torch.float32)
+    _need(conv_state, "conv_state", dt)
+    _need(conv_weight, "conv_weight", torch.float32, (d.conv_channels, 4))
+    _need(o, "o", torch.float32, (B, H, dv))
+    if slots is not None:
+        _need(slots, "slots", torch.int32, (B,))
+    dims = d.c()
+    _check(lib.kda_decode(ctypes.byref(dims), B, _ptr(slots), _ptr(state), _ptr(conv_state), _ptr(conv_weight),
+                          _ptr(q_raw), _ptr(k_raw), _ptr(v_raw), _ptr(g_raw), _ptr(beta_logit), int(gate_mode),
+                          float(lower_bound), _ptr(o), _stream()))
+
+
+@dataclass
+class VerifyLog:
+    """Device buffers of one verify window's log (see kda_log in include/kda.h)."""
+    a: torch.Tensor  # [B, W, H, dk] fp32
+    k_hat: torch.Tensor  # [B, W, H, dk] fp32
+    u: torch.Tensor  # [B, W, H, dv] fp32
+    conv_rows: torch.Tensor  # [B, W, C] raw dtype
+
+    @property
+    def window(self) -> int:
+        return self.a.shape[1]
+
+    @staticmethod
+    def empty(d: Dims, batch: int, window: int, device="cuda") -> "VerifyLog":
+        H, dk, dv = d.num_heads, d.head_dim_k, d.head_dim_v
+        f = dict(device=device, dtype=torch.float32)
+        return VerifyLog(torch.empty(batch, window, H, dk, **f), torch.empty(batch, window, H, dk, **f),
+                         torch.empty(batch, window, H, dv, **f),
+                         torch.empty(batch, window, d.conv_channels, device=device, dtype=d.in_dtype))
+
+    def c(self) -> KdaLog:
+        return KdaLog(self.a.data_ptr(), self.k_hat.data_ptr(), self.u.data_ptr(), self.conv_rows.data_ptr(),
+                      self.window)
+
+
+def kda_verify_window(d: Dims, state, conv_state, conv_weight, n_commit, log_in, log_out, q_raw, k_raw, v_raw,
+                      g_raw, beta_logit, gate_mode, lower_bound, o, slots=None, batch=None):
+    lib = load_library()
+    H, dk, dv, dt = d.num_heads, d.head_dim_k, d.head_dim_v, d.in_dtype
+    W = 0 if q_raw is None else q_raw.shape[1]
+    B = batch if batch is not None else (q_raw.shape[0] if q_raw is not None else n_commit.numel())
+    if W > 0:
+        for name, t, shp in (("q_raw", q_raw, (B, W, H, dk)), ("k_raw", k_raw, (B, W, H, dk)),
+                             ("v_raw", v_raw, (B, W, H, dv)), ("g_raw", g_raw, (B, W, H, dk)),
+                             ("beta_logit", beta_logit, (B, W, H))):
+            _need(t, name, dt, shp)
+        _need(o, "o", torch.float32, (B, W, H, dv))
+    _need(state, "state", torch.float32)
+    _need(conv_state, "conv_state", dt)
+    _need(conv_weight, "conv_weight", torch.float32, (d.conv_channels, 4))
+    if n_commit is not None:
+        _need(n_commit, "n_commit", torch.int32, (B,))
+    if slots is not None:
+        _need(slots, "slots", torch.int32, (B,))
+    dims = d.c()
+    lin = log_in.c() if log_in is not None else None
+    lout = log_out.c() if log_out is not None else None
+    _check(lib.kda_verify_window(ctypes.byref(dims), B, W, _ptr(slots), _ptr(state), _ptr(conv_state),
+                                 _ptr(conv_weight), _ptr(n_commit), ctypes.byref(lin) if lin else None,
+                                 ctypes.byref(lout) if lout else None, _ptr(q_raw), _ptr(k_raw), _ptr(v_raw),
+                                 _ptr(g_raw), _ptr(beta_logit), int(gate_mode), float(lower_bound), _ptr(o),
+                                 _stream()))
+
+
+def gated_rmsnorm_out(o, z, w, eps, y):
+    lib = load_library()
+    dv = o.shape[-1]
+    rows = o.numel() // dv
+    _need(o, "o", torch.float32)
+    _need(z, "z", shape=o.shape)
+    _need(w, "w", torch.float32, (dv,))
+    _need(y, "y", shape=o.shape)
+    _check(lib.gated_rmsnorm_out(rows, dv, _ptr(o), _ptr(z), _dtype_code(z.dtype), _ptr(w), float(eps), _ptr(y),
+                                 _dtype_code(y.dtype), _stream()))

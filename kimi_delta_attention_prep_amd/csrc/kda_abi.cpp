@@ -1,0 +1,243 @@
+// kda_abi.cpp -- the C ABI declared in include/kda.h: argument validation
+// (before any launch, so an error enqueues nothing and writes nothing) and
+// dispatch to the gfx950 kernels.  TensorFold issue #850 asks the shared KDA
+// module to reject unsupported head widths and tap counts before launch; the
+// checks here do that for every entry point.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "kda.h"
+#include "kda_launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return KDA_OK;
+}
+
+bool aligned(const void* p, unsigned a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1u)) == 0; }
+unsigned elem_bytes(int32_t dtype) { return dtype == KDA_DTYPE_BF16 ? 2u : 4u; }
+
+int check_dims(const kda_dims* d) {
+  if (!d) return fail(KDA_E_ARG, "dims is NULL");
+  if (d->num_heads < 1) return fail(KDA_E_ARG, "num_heads must be >= 1 (got %d)", d->num_heads);
+  if (!((d->head_dim_k == 64 || d->head_dim_k == 128) && (d->head_dim_v == 64 || d->head_dim_v == 128)))
+    return fail(KDA_E_GEOMETRY, "head dims (%d, %d) unsupported: d_k and d_v must be 64 or 128", d->head_dim_k,
+                d->head_dim_v);
+  if (d->conv_width != 4) return fail(KDA_E_GEOMETRY, "conv width %d unsupported: must be 4", d->conv_width);
+  if (d->in_dtype != KDA_DTYPE_F32 && d->in_dtype != KDA_DTYPE_BF16)
+    return fail(KDA_E_DTYPE, "unknown in_dtype %d", d->in_dtype);
+  if (d->conv_act != KDA_ACT_NONE && d->conv_act != KDA_ACT_SILU)
+    return fail(KDA_E_DTYPE, "unknown conv_act %d", d->conv_act);
+  if (d->precision != KDA_PREC_FP32 && d->precision != KDA_PREC_BF16X3)
+    return fail(KDA_E_DTYPE, "unknown precision %d", d->precision);
+  return KDA_OK;
+}
+
+int check_gate(int32_t gate_mode, float lb) {
+  if (gate_mode == KDA_GATE_SOFTPLUS) return KDA_OK;  // the bound is ignored outside safe mode
+  if (gate_mode != KDA_GATE_SAFE) return fail(KDA_E_GATE, "unknown gate mode %d", gate_mode);
+  if (!std::isfinite(lb) || !(lb < 0.0f))
+    return fail(KDA_E_GATE, "safe gate needs a finite lower bound < 0 (got %g)", (double)lb);
+  return KDA_OK;
+}
+
+// all listed pointers non-null and aligned to `align` bytes (16 where the
+// kernels use 128-bit accesses, else the element size)
+int check_ptrs(const char* what, std::initializer_list<const void*> ps, unsigned align = 16) {
+  int i = 0;
+  for (const void* p : ps) {
+    if (!p) return fail(KDA_E_ARG, "%s: pointer argument %d is NULL", what, i);
+    if (!aligned(p, align)) return fail(KDA_E_ALIGN, "%s: pointer argument %d is not %u-byte aligned", what, i, align);
+    ++i;
+  }
+  return KDA_OK;
+}
+
+int check_opt_ptr(const char* what, const void* p) {
+  if (p && !aligned(p, 4)) return fail(KDA_E_ALIGN, "%s is not 4-byte aligned", what);
+  return KDA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(KDA_E_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+#define KDA_TRY(expr)          \
+  do {                         \
+    const int rc_ = (expr);    \
+    if (rc_ != KDA_OK) return rc_; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_last_error(void) { return g_err; }
+
+int kda_prep(const kda_dims* d, int32_t num_seqs, int64_t t_tot, const int32_t* cu_seqlens, const int32_t* slots,
+             const void* q_raw, const void* k_raw, const void* v_raw, const float* conv_weight,
+             const void* conv_state_in, void* conv_state_out, const void* g_raw, const void* beta_logit,
+             int32_t gate_mode, float lower_bound, float* q_hat, float* k_hat, float* v_out, float* g_out,
+             float* beta_out, hipStream_t stream) {
+  KDA_TRY(check_dims(d));
+  KDA_TRY(check_gate(gate_mode, lower_bound));
+  if (num_seqs < 0 || t_tot < 0) return fail(KDA_E_ARG, "kda_prep: negative size");
+  if (num_seqs == 0 && t_tot > 0) return fail(KDA_E_ARG, "kda_prep: rows without sequences");
+  KDA_TRY(check_opt_ptr("kda_prep: slots", slots));
+  const unsigned eb = elem_bytes(d->in_dtype);
+  if (num_seqs > 0) {
+    KDA_TRY(check_ptrs("kda_prep", {cu_seqlens, conv_weight}, 4));
+    KDA_TRY(check_ptrs("kda_prep: conv state", {conv_state_in, conv_state_out}, eb));
+  }
+  if (t_tot > 0) {
+    KDA_TRY(check_ptrs("kda_prep: rows", {q_raw, k_raw, v_raw, g_raw, beta_logit}, eb));
+    KDA_TRY(check_ptrs("kda_prep: outputs", {q_hat, k_hat, v_out, g_out, beta_out}, 4));
+  }
+  kda::PrepLaunch L{d->num_heads, d->head_dim_k, d->head_dim_v, d->in_dtype, d->conv_act, gate_mode, num_seqs, t_tot,
+                    lower_bound, cu_seqlens, slots, q_raw, k_raw, v_raw, g_raw, beta_logit, conv_weight,
+                    conv_state_in, conv_state_out, q_hat, k_hat, v_out, g_out, beta_out};
+  return hip_status(kda::launch_prep(L, stream), "kda_prep");
+}
+
+size_t kda_prefill_workspace_bytes(const kda_dims* d, int32_t num_seqs, int64_t t_tot) {
+  if (check_dims(d) != KDA_OK || num_seqs < 0 || t_tot < 0) return 0;
+  return kda::prefill_workspace_bytes(d->num_heads, d->head_dim_k, d->head_dim_v, num_seqs, t_tot);
+}
+
+int kda_prefill_varlen(const kda_dims* d, int32_t num_seqs, int64_t t_tot, const int32_t* cu_seqlens,
+                       const int32_t* slots, const float* q_hat, const float* k_hat, const float* v,
+                       const float* g, const float* beta, float* state, float* o, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  KDA_TRY(check_dims(d));
+  if (num_seqs < 0 || t_tot < 0) return fail(KDA_E_ARG, "kda_prefill_varlen: negative size");
+  if (num_seqs == 0 && t_tot > 0) return fail(KDA_E_ARG, "kda_prefill_varlen: rows without sequences");
+  KDA_TRY(check_opt_ptr("kda_prefill_varlen: slots", slots));
+  if (num_seqs > 0) {
+    KDA_TRY(check_ptrs("kda_prefill_varlen: cu_seqlens", {cu_seqlens}, 4));
+    KDA_TRY(check_ptrs("kda_prefill_varlen: state", {state}));
+  }
+  if (t_tot > 0) {
+    KDA_TRY(check_ptrs("kda_prefill_varlen", {q_hat, k_hat, v, g}));
+    KDA_TRY(check_ptrs("kda_prefill_varlen", {beta, o}, 4));
+  }
+  const size_t need = kda::prefill_workspace_bytes(d->num_heads, d->head_dim_k, d->head_dim_v, num_seqs, t_tot);
+  if (num_seqs > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(KDA_E_WORKSPACE, "kda_prefill_varlen: workspace of %zu bytes needed, %zu given", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return fail(KDA_E_ALIGN, "kda_prefill_varlen: workspace must be 256-byte aligned");
+  }
+  if (num_seqs == 0) return ok();
+  kda::PrefillLaunch L{d->num_heads, d->head_dim_k, d->head_dim_v, d->precision, num_seqs, t_tot, cu_seqlens, slots,
+                       q_hat, k_hat, v, g, beta, state, o, workspace, workspace_bytes};
+  return hip_status(kda::launch_prefill(L, stream), "kda_prefill_varlen");
+}
+
+int kda_decode(const kda_dims* d, int32_t batch, const int32_t* slots, float* state, void* conv_state,
+               const float* conv_weight, const void* q_raw, const void* k_raw, const void* v_raw, const void* g_raw,
+               const void* beta_logit, int32_t gate_mode, float lower_bound, float* o, hipStream_t stream) {
+  KDA_TRY(check_dims(d));
+  KDA_TRY(check_gate(gate_mode, lower_bound));
+  if (batch < 0) return fail(KDA_E_ARG, "kda_decode: negative batch");
+  if (batch == 0) return ok();
+  KDA_TRY(check_opt_ptr("kda_decode: slots", slots));
+  KDA_TRY(check_ptrs("kda_decode", {state, o}));
+  KDA_TRY(check_ptrs("kda_decode: conv weight", {conv_weight}, 4));
+  KDA_TRY(check_ptrs("kda_decode: rows", {conv_state, q_raw, k_raw, v_raw, g_raw, beta_logit}, elem_bytes(d->in_dtype)));
+  kda::RowsLaunch L{};
+  L.H = d->num_heads; L.dk = d->head_dim_k; L.dv = d->head_dim_v; L.in_dtype = d->in_dtype; L.act = d->conv_act;
+  L.gate_mode = gate_mode; L.batch = batch; L.window = 1; L.lb = lower_bound; L.slots = slots; L.state = state;
+  L.conv_state = conv_state; L.conv_w = conv_weight; L.q = q_raw; L.k = k_raw; L.v = v_raw; L.g = g_raw;
+  L.beta = beta_logit; L.o = o;
+  return hip_status(kda::launch_rows(L, false, stream), "kda_decode");
+}
+
+int kda_verify_window(const kda_dims* d, int32_t batch, int32_t window, const int32_t* slots, float* state,
+                      void* conv_state, const float* conv_weight, const int32_t* n_commit, const kda_log* log_in,
+                      const kda_log* log_out, const void* q_raw, const void* k_raw, const void* v_raw,
+                      const void* g_raw, const void* beta_logit, int32_t gate_mode, float lower_bound, float* o,
+                      hipStream_t stream) {
+  KDA_TRY(check_dims(d));
+  KDA_TRY(check_gate(gate_mode, lower_bound));
+  if (batch < 0) return fail(KDA_E_ARG, "kda_verify_window: negative batch");
+  if (window < 0 || window > 8) return fail(KDA_E_GEOMETRY, "kda_verify_window: window %d not in [0, 8]", window);
+  const bool commit = n_commit != nullptr;
+  if (commit && !log_in) return fail(KDA_E_ARG, "kda_verify_window: n_commit given without log_in");
+  if (commit && (log_in->window < 0 || log_in->window > 8))
+    return fail(KDA_E_GEOMETRY, "kda_verify_window: log_in window %d not in [0, 8]", log_in->window);
+  if (window > 0 && !log_out) return fail(KDA_E_ARG, "kda_verify_window: window rows need log_out");
+  if (window > 0 && log_out->window != window)
+    return fail(KDA_E_GEOMETRY, "kda_verify_window: log_out sized for %d rows, window is %d", log_out->window, window);
+  if (batch == 0) return ok();
+  KDA_TRY(check_opt_ptr("kda_verify_window: slots", slots));
+  const unsigned eb = elem_bytes(d->in_dtype);
+  KDA_TRY(check_ptrs("kda_verify_window: state", {state}));
+  KDA_TRY(check_ptrs("kda_verify_window: conv weight", {conv_weight}, 4));
+  KDA_TRY(check_ptrs("kda_verify_window: conv state", {conv_state}, eb));
+  if (commit) {
+    KDA_TRY(check_ptrs("kda_verify_window: n_commit", {n_commit}, 4));
+    if (log_in->window > 0) {
+      KDA_TRY(check_ptrs("kda_verify_window: log_in", {log_in->a, log_in->k_hat}, 4));
+      KDA_TRY(check_ptrs("kda_verify_window: log_in u", {log_in->u}));
+      KDA_TRY(check_ptrs("kda_verify_window: log_in rows", {log_in->conv_rows}, eb));
+    }
+  }
+  if (window > 0) {
+    KDA_TRY(check_ptrs("kda_verify_window: rows", {q_raw, k_raw, v_raw, g_raw, beta_logit}, eb));
+    KDA_TRY(check_ptrs("kda_verify_window: o", {o}));
+    KDA_TRY(check_ptrs("kda_verify_window: log_out", {log_out->a, log_out->k_hat}, 4));
+    KDA_TRY(check_ptrs("kda_verify_window: log_out u", {log_out->u}));
+    KDA_TRY(check_ptrs("kda_verify_window: log_out rows", {log_out->conv_rows}, eb));
+    if (commit && log_in->window > 0 &&
+        (log_in->a == log_out->a || log_in->k_hat == log_out->k_hat || log_in->u == log_out->u ||
+         log_in->conv_rows == log_out->conv_rows))
+      return fail(KDA_E_ARG, "kda_verify_window: log_in and log_out must not share buffers");
+  }
+  if (!commit && window == 0) return ok();
+  kda::RowsLaunch L{};
+  L.H = d->num_heads; L.dk = d->head_dim_k; L.dv = d->head_dim_v; L.in_dtype = d->in_dtype; L.act = d->conv_act;
+  L.gate_mode = gate_mode; L.batch = batch; L.window = window; L.lb = lower_bound; L.slots = slots; L.state = state;
+  L.conv_state = conv_state; L.conv_w = conv_weight; L.q = q_raw; L.k = k_raw; L.v = v_raw; L.g = g_raw;
+  L.beta = beta_logit; L.o = o;
+  L.n_commit = n_commit;
+  if (commit) {
+    L.in_a = log_in->a; L.in_k = log_in->k_hat; L.in_u = log_in->u; L.in_rows = log_in->conv_rows;
+    L.in_window = log_in->window;
+  }
+  if (window > 0) {
+    L.out_a = log_out->a; L.out_k = log_out->k_hat; L.out_u = log_out->u; L.out_rows = log_out->conv_rows;
+  }
+  return hip_status(kda::launch_rows(L, true, stream), "kda_verify_window");
+}
+
+int gated_rmsnorm_out(int64_t rows, int32_t d_v, const float* o, const void* z, int32_t z_dtype, const float* w,
+                      float eps, void* y, int32_t y_dtype, hipStream_t stream) {
+  if (rows < 0) return fail(KDA_E_ARG, "gated_rmsnorm_out: negative rows");
+  if (d_v != 64 && d_v != 128) return fail(KDA_E_GEOMETRY, "gated_rmsnorm_out: d_v %d not in {64, 128}", d_v);
+  if ((z_dtype != KDA_DTYPE_F32 && z_dtype != KDA_DTYPE_BF16) || (y_dtype != KDA_DTYPE_F32 && y_dtype != KDA_DTYPE_BF16))
+    return fail(KDA_E_DTYPE, "gated_rmsnorm_out: unknown dtype");
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(KDA_E_ARG, "gated_rmsnorm_out: eps must be finite and >= 0");
+  if (rows == 0) return ok();
+  KDA_TRY(check_ptrs("gated_rmsnorm_out", {o, z, w, y}));
+  kda::NormLaunch L{rows, d_v, z_dtype, y_dtype, o, z, w, eps, y};
+  return hip_status(kda::launch_gated_rmsnorm(L, stream), "gated_rmsnorm_out");
+}
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// kda_device.hpp -- device-side helpers shared by the KDA kernels (gfx950 only).
+//
+// Scalar functions of the layer (TensorFold issue #850, shared KDA module: conv
+// window, safe or softplus gate, beta, q/k L2 norms; onnxruntime-genai PR #2843:
+// gate_activation='sigmoid' with gate_lower_bound, GatedRMSNorm 'sigmoid').
+// Every kernel takes these from here, so a value computed by two kernels (the
+// prompt preamble and a fused variant, decode and a verify window) is computed
+// by the same instructions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kL2Eps = 1e-6f;  // inside the square root of the q/k L2 norms
+constexpr int kConvW = 4;        // conv taps; tap 3 multiplies the current row
+constexpr int kChunk = 64;       // prompt rows per chunk
+
+// raw rows arrive as fp32 or as bf16 bit patterns (uint16_t); widening is exact
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(uint16_t x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }
+
+__device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+// per-key-dim log decay g: softplus gate g = -softplus(x) = -(max(x,0) + log1p(e^-|x|));
+// safe gate g = lb * sigmoid(x), so a = e^g lies in (e^lb, 1)
+__device__ __forceinline__ float log_decay(float x, int gate_mode, float lb) {
+  if (gate_mode == 1) return lb * sigmoid(x);
+  return -(fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x))));
+}
+
+// depthwise causal conv over 4 taps (x0 oldest, x3 current row), then the activation
+__device__ __forceinline__ float conv4_act(float w0, float w1, float w2, float w3, float x0, float x1, float x2,
+                                           float x3, int act) {
+  float c = w0 * x0;
+  c = fmaf(w1, x1, c);
+  c = fmaf(w2, x2, c);
+  c = fmaf(w3, x3, c);
+  return act ? c * sigmoid(c) : c;
+}
+
+// sum over the 64 lanes of a wavefront; every lane receives lane 0's result so
+// all lanes hold identical bits
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return __shfl(x, 0, 64);
+}
+
+// one state element's step: S' = a * S, then S = S' + k * u (explicit fma).
+// decode, verify windows and the commit replay all use exactly this.
+__device__ __forceinline__ float decay(float s, float a) { return a * s; }
+__device__ __forceinline__ float rank1(float s_decayed, float k, float u) { return fmaf(k, u, s_decayed); }
+
+}  // namespace kda

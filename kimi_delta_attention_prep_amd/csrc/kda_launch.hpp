@@ -1,0 +1,66 @@
+// kda_launch.hpp -- internal launcher interface between the C ABI (kda_abi.cpp)
+// and the kernels.  Host-side plain structs; arguments are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct RowsLaunch {
+  int H, dk, dv, in_dtype, act, gate_mode, batch, window;
+  float lb;
+  const int32_t* slots;
+  float* state;
+  void* conv_state;
+  const float* conv_w;
+  const void *q, *k, *v, *g, *beta;
+  float* o;
+  const int32_t* n_commit;
+  const float *in_a, *in_k, *in_u;
+  const void* in_rows;
+  int in_window;
+  float *out_a, *out_k, *out_u;
+  void* out_rows;
+};
+hipError_t launch_rows(const RowsLaunch& L, bool verify, hipStream_t s);
+
+struct NormLaunch {
+  int64_t rows;
+  int dv, z_dtype, y_dtype;
+  const float* o;
+  const void* z;
+  const float* w;
+  float eps;
+  void* y;
+};
+hipError_t launch_gated_rmsnorm(const NormLaunch& L, hipStream_t s);
+
+struct PrepLaunch {
+  int H, dk, dv, in_dtype, act, gate_mode, num_seqs;
+  int64_t t_tot;
+  float lb;
+  const int32_t *cu_seqlens, *slots;
+  const void *q, *k, *v, *g, *beta;
+  const float* conv_w;
+  const void* cs_in;
+  void* cs_out;
+  float *q_hat, *k_hat, *v_out, *g_out, *beta_out;
+};
+hipError_t launch_prep(const PrepLaunch& L, hipStream_t s);
+
+struct PrefillLaunch {
+  int H, dk, dv, precision, num_seqs;
+  int64_t t_tot;
+  const int32_t *cu_seqlens, *slots;
+  const float *q_hat, *k_hat, *v, *g, *beta;
+  float* state;
+  float* o;
+  void* workspace;
+  size_t workspace_bytes;
+};
+size_t prefill_workspace_bytes(int H, int dk, int dv, int num_seqs, int64_t t_tot);
+hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t s);
+
+}  // namespace kda

@@ -1,0 +1,132 @@
+"""The C-ABI library loads on the host, exports every entry point its header
+declares, and rejects bad arguments before any launch (CPU only: every call
+here fails validation or has nothing to do, so no HIP work is issued)."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import kimi_delta_attention_prep_amd as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(K.LIB_PATH):
+        from kimi_delta_attention_prep_amd import build
+        build.build(verbose=False)
+    return K.load_library()
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^(?:int|size_t|const char\*)\s+(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert set(_declared()) == set(K.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", K.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in _declared():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+A = ctypes.c_void_p(0x10000)   # aligned, never dereferenced (validation fails first)
+MIS = ctypes.c_void_p(0x10001)  # misaligned for every element type
+MIS4 = ctypes.c_void_p(0x10004)  # element-aligned, not 16-byte aligned
+
+
+def dims(H=2, dk=128, dv=128, W=4, dt=K.DTYPE_BF16, act=K.ACT_SILU, prec=K.PREC_BF16X3):
+    return K.KdaDims(H, dk, dv, W, dt, act, prec)
+
+
+def decode(lib, d, *, q=A, gate=K.GATE_SAFE, lb=-5.0, batch=4, slots=None, state=A):
+    return lib.kda_decode(ctypes.byref(d), batch, slots, state, A, A, q, A, A, A, A, gate, lb, A, None)
+
+
+@pytest.mark.parametrize("d,code", [
+    (dims(dk=96), K.KDA_E_GEOMETRY), (dims(dv=32), K.KDA_E_GEOMETRY), (dims(W=3), K.KDA_E_GEOMETRY),
+    (dims(dt=7), K.KDA_E_DTYPE), (dims(act=3), K.KDA_E_DTYPE), (dims(prec=5), K.KDA_E_DTYPE),
+    (dims(H=0), K.KDA_E_ARG),
+])
+def test_geometry_and_dtype_rejected_before_launch(lib, d, code):
+    assert decode(lib, d) == code
+    assert lib.kda_last_error()  # a message is left
+
+
+@pytest.mark.parametrize("gate,lb,code", [
+    (9, -5.0, K.KDA_E_GATE), (K.GATE_SAFE, 0.0, K.KDA_E_GATE), (K.GATE_SAFE, 1.0, K.KDA_E_GATE),
+    (K.GATE_SAFE, float("nan"), K.KDA_E_GATE), (K.GATE_SAFE, -math.inf, K.KDA_E_GATE),
+])
+def test_gate_checks(lib, gate, lb, code):
+    assert decode(lib, dims(), gate=gate, lb=lb) == code
+
+
+def test_lower_bound_ignored_in_softplus_mode(lib):
+    # a nonsense bound passes the gate check in softplus mode; the misaligned row pointer then stops the call
+    assert decode(lib, dims(), gate=K.GATE_SOFTPLUS, lb=float("nan"), q=MIS) == K.KDA_E_ALIGN
+
+
+def test_pointer_checks(lib):
+    assert decode(lib, dims(), q=MIS) == K.KDA_E_ALIGN
+    assert decode(lib, dims(), state=MIS4) == K.KDA_E_ALIGN  # the state moves with 128-bit accesses
+    assert decode(lib, dims(), q=None) == K.KDA_E_ARG
+    assert decode(lib, dims(), slots=MIS) == K.KDA_E_ALIGN
+    assert decode(lib, dims(), batch=-1) == K.KDA_E_ARG
+    assert decode(lib, dims(), batch=0, q=None) == K.KDA_OK  # nothing to do, nothing launched
+
+
+def test_verify_window_checks(lib):
+    d = dims()
+    log = K.KdaLog(A.value, A.value, A.value, A.value, 4)
+    bad = K.KdaLog(A.value, A.value, A.value, A.value, 3)
+    call = lambda W, nc, lin, lout: lib.kda_verify_window(ctypes.byref(d), 4, W, None, A, A, A, nc, lin, lout, MIS, A,
+                                                           A, A, A, K.GATE_SAFE, -5.0, A, None)
+    assert call(9, None, None, ctypes.byref(log)) == K.KDA_E_GEOMETRY
+    assert call(-1, None, None, ctypes.byref(log)) == K.KDA_E_GEOMETRY
+    assert call(4, None, None, None) == K.KDA_E_ARG              # rows without a log to write
+    assert call(4, None, None, ctypes.byref(bad)) == K.KDA_E_GEOMETRY  # log sized for another window
+    assert call(4, A, None, ctypes.byref(log)) == K.KDA_E_ARG    # commit counts without a log
+    assert call(4, A, ctypes.byref(log), ctypes.byref(log)) == K.KDA_E_ALIGN  # misaligned q row first
+    assert call(0, None, None, None) == K.KDA_OK                 # nothing to commit, no rows
+
+
+def test_prep_and_prefill_checks(lib):
+    d = dims()
+    prep = lambda N, T, q: lib.kda_prep(ctypes.byref(d), N, T, A, None, q, A, A, A, A, A, A, A, K.GATE_SAFE, -5.0,
+                                        A, A, A, A, A, None)
+    assert prep(-1, 10, A) == K.KDA_E_ARG
+    assert prep(0, 10, A) == K.KDA_E_ARG
+    assert prep(2, 10, MIS) == K.KDA_E_ALIGN
+    need = lib.kda_prefill_workspace_bytes(ctypes.byref(d), 2, 1000)
+    assert need > 0
+    pf = lambda ws, nb: lib.kda_prefill_varlen(ctypes.byref(d), 2, 1000, A, None, A, A, A, A, A, A, A, ws, nb, None)
+    assert pf(A, need - 1) == K.KDA_E_WORKSPACE
+    assert pf(None, need) == K.KDA_E_WORKSPACE
+    assert pf(ctypes.c_void_p(0x10010), need) == K.KDA_E_ALIGN
+    assert lib.kda_prefill_workspace_bytes(ctypes.byref(dims(dk=96)), 2, 1000) == 0
+
+
+def test_norm_checks(lib):
+    nf = lambda dv, zt, eps, o: lib.gated_rmsnorm_out(10, dv, o, A, zt, A, eps, A, K.DTYPE_F32, None)
+    assert nf(96, K.DTYPE_F32, 1e-6, A) == K.KDA_E_GEOMETRY
+    assert nf(128, 4, 1e-6, A) == K.KDA_E_DTYPE
+    assert nf(128, K.DTYPE_F32, -1.0, A) == K.KDA_E_ARG
+    assert nf(128, K.DTYPE_F32, 1e-6, MIS) == K.KDA_E_ALIGN
+
+
+def test_binding_has_no_fallback(tmp_path, monkeypatch):
+    """A missing library is an error, never a silent substitute."""
+    monkeypatch.setattr(K, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        K.load_library(str(tmp_path / "nope.so"))

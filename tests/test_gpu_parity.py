@@ -1,0 +1,294 @@
+"""GPU parity of every entry point against the fp64 oracle (small and ragged
+shapes), plus the bit-exact invariants: carried conv state bytes, packed vs
+alone, prompt cut at a chunk multiple, and verify-window replay vs serial
+decode.  Everything goes through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import kimi_delta_attention_prep_amd as K
+from kimi_delta_attention_prep_amd import inputs as I
+from oracle import oracle as O
+
+from helpers import (EPS, TOL_BF16, TOL_FP32, dims_for, gpu_decode_steps, gpu_layer_prefill, gpu_prep,
+                     oracle_layer, rel, tol_for)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    K.load_library()  # must exist: no fallback
+
+
+def small(dtype=torch.bfloat16, lens=(70, 5, 0, 130), H=2, d=128, gate=I.GATE_SAFE, seed=3, dv=None):
+    return I.generate("small", lengths=list(lens), H=H, dk=d, dv=dv or d, dtype=dtype, gate_mode=gate,
+                      state_std=0.02, conv_state_std=1.0, seed=seed)
+
+
+# ---------------------------------------------------------------------------
+# output norm and preamble
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dv", [64, 128])
+@pytest.mark.parametrize("zdt,ydt", [(torch.float32, torch.float32), (torch.bfloat16, torch.float32),
+                                     (torch.bfloat16, torch.bfloat16)])
+def test_gated_rmsnorm(dv, zdt, ydt):
+    g = torch.Generator().manual_seed(1)
+    rows = 1037
+    o = torch.randn(rows, dv, generator=g)
+    z = torch.randn(rows, dv, generator=g).to(zdt)
+    w = torch.rand(dv, generator=g) + 0.5
+    y = torch.empty(rows, dv, dtype=ydt, device="cuda")
+    K.gated_rmsnorm_out(o.cuda(), z.cuda(), w.cuda(), EPS, y)
+    ref = O.gated_rmsnorm(o.double().numpy(), z.double().numpy(), w.double().numpy(), EPS)
+    assert rel(y, ref) < (4e-3 if ydt == torch.bfloat16 else 2e-6)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (64, 128)])
+@pytest.mark.parametrize("gate", [I.GATE_SAFE, I.GATE_SOFTPLUS])
+def test_prep_parity_and_conv_state_bytes(dtype, dk, dv, gate):
+    w = small(dtype, d=dk, dv=dv, gate=gate)
+    _, p = gpu_prep(w, dims_for(w))
+    ref = O.prep(w.f64("q"), w.f64("k"), w.f64("v"), w.f64("conv_w"), w.f64("conv_state0"), w.f64("g"),
+                 w.f64("beta"), w.cu_seqlens.numpy(), gate_mode=w.gate_mode, lower_bound=w.lower_bound)
+    for name, r in (("q_hat", ref.q_hat), ("k_hat", ref.k_hat), ("v", ref.v), ("g", ref.g), ("beta", ref.beta)):
+        assert rel(p[name], r) < 2e-6, name
+    # the carried conv state is a bit copy of raw rows
+    assert np.array_equal(p["conv_state"].cpu().double().numpy(), ref.conv_state)
+
+
+# ---------------------------------------------------------------------------
+# decode and verify windows
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float32, 64), (torch.bfloat16, 64)])
+def test_decode_parity(dtype, d):
+    steps = 9
+    w = I.generate("dec", lengths=[steps] * 6, H=3, dk=d, dv=d, dtype=dtype, gate_mode=I.GATE_SAFE,
+                   state_std=0.02, conv_state_std=1.0, seed=5)
+    r = gpu_decode_steps(w, steps)
+    ref = oracle_layer(w)
+    o = r["o"].transpose(0, 1).reshape(w.T, w.H, w.dv)  # [steps,B,..] -> packed rows
+    y = r["y"].transpose(0, 1).reshape(w.T, w.H, w.dv)
+    tol = tol_for(w)
+    assert rel(o, ref.o) < tol
+    assert rel(y, ref.y) < tol
+    assert rel(r["state"], ref.state) < tol
+    assert np.array_equal(r["conv_state"].cpu().double().numpy(), ref.prep.conv_state)
+
+
+def _verify_setup(B=5, W=4, H=2, d=128, seed=7):
+    w = I.generate("ver", lengths=[W] * B, H=H, dk=d, dv=d, dtype=torch.bfloat16, gate_mode=I.GATE_SAFE,
+                   state_std=0.02, conv_state_std=1.0, seed=seed)
+    rows = {n: getattr(w, n).view(B, W, *getattr(w, n).shape[1:]).cuda() for n in ("q", "k", "v", "g", "beta")}
+    return w, rows
+
+
+def _decode_rows(w, rows, d, state, cs, row_ids, active):
+    """Serial decode of rows row_ids; a sequence takes part at step s only if active(b, s)."""
+    B = w.N
+    outs = []
+    for s in row_ids:
+        slots = torch.tensor([b if active(b, s) else -1 for b in range(B)], dtype=torch.int32, device="cuda")
+        o = torch.full((B, w.H, w.dv), float("nan"), device="cuda")
+        K.kda_decode(d, state, cs, w.conv_w.cuda(), rows["q"][:, s].contiguous(), rows["k"][:, s].contiguous(),
+                     rows["v"][:, s].contiguous(), rows["g"][:, s].contiguous(), rows["beta"][:, s].contiguous(),
+                     w.gate_mode, w.lower_bound, o, slots=slots)
+        outs.append(o)
+    return torch.stack(outs, 1)  # [B, steps, H, dv]
+
+
+def test_verify_window_replay_is_bitwise_serial_decode():
+    B, W = 5, 4
+    w, rows = _verify_setup(B, W)
+    d = dims_for(w)
+    accept = torch.tensor([0, 3, 1, 2, 3], dtype=torch.int32)  # rows 0..j kept
+    n_commit = (accept + 1).cuda()
+    # verify path: window, then commit-only
+    st_v, cs_v = w.state0.cuda().clone(), w.conv_state0.cuda().clone()
+    log = K.VerifyLog.empty(d, B, W)
+    o_v = torch.empty(B, W, w.H, w.dv, device="cuda")
+    K.kda_verify_window(d, st_v, cs_v, w.conv_w.cuda(), None, None, log, rows["q"], rows["k"], rows["v"], rows["g"],
+                        rows["beta"], w.gate_mode, w.lower_bound, o_v)
+    st_after_window = st_v.clone()
+    assert torch.equal(st_after_window, w.state0.cuda())  # uncommitted rows leave the state alone
+    K.kda_verify_window(d, st_v, cs_v, w.conv_w.cuda(), n_commit, log, None, None, None, None, None, None,
+                        w.gate_mode, w.lower_bound, None, batch=B)
+    # serial decode of the kept rows only (negative slots skip the others)
+    st_d, cs_d = w.state0.cuda().clone(), w.conv_state0.cuda().clone()
+    o_d = _decode_rows(w, rows, d, st_d, cs_d, range(W), lambda b, s: s <= int(accept[b]))
+    torch.cuda.synchronize()
+    assert torch.equal(st_v, st_d)
+    assert torch.equal(cs_v, cs_d)
+    for b in range(B):
+        j = int(accept[b])
+        assert torch.equal(o_v[b, :j + 1], o_d[b, :j + 1])
+    # every window row equals decode of all W rows
+    st_a, cs_a = w.state0.cuda().clone(), w.conv_state0.cuda().clone()
+    o_all = _decode_rows(w, rows, d, st_a, cs_a, range(W), lambda b, s: True)
+    assert torch.equal(o_v, o_all)
+    # log contents equal the oracle's per-row decay, key and update within tolerance
+    ref = oracle_layer(w, with_log=True)
+    assert rel(log.a.reshape(-1, w.H, w.dk), ref.log_a) < 1e-6
+    assert rel(log.k_hat.reshape(-1, w.H, w.dk), ref.log_k) < 1e-5
+    assert rel(log.u.reshape(-1, w.H, w.dv), ref.log_u) < TOL_BF16
+    assert rel(o_v.reshape(-1, w.H, w.dv), ref.o) < TOL_BF16
+
+
+def test_verify_commit_and_next_window_in_one_call():
+    """Commit the previous window and run the next one in the same call; equals serial decode bitwise."""
+    B, W = 4, 3
+    w, rows = _verify_setup(B, 2 * W, seed=11)
+    d = dims_for(w)
+    first = {k: v[:, :W].contiguous() for k, v in rows.items()}
+    second = {k: v[:, W:].contiguous() for k, v in rows.items()}
+    acc1 = torch.tensor([3, 1, 2, 3], dtype=torch.int32)  # rows committed from window 1 (count)
+    st, cs = w.state0.cuda().clone(), w.conv_state0.cuda().clone()
+    log1, log2 = K.VerifyLog.empty(d, B, W), K.VerifyLog.empty(d, B, W)
+    o1 = torch.empty(B, W, w.H, w.dv, device="cuda")
+    o2 = torch.empty_like(o1)
+    K.kda_verify_window(d, st, cs, w.conv_w.cuda(), None, None, log1, first["q"], first["k"], first["v"],
+                        first["g"], first["beta"], w.gate_mode, w.lower_bound, o1)
+    K.kda_verify_window(d, st, cs, w.conv_w.cuda(), acc1.cuda(), log1, log2, second["q"], second["k"], second["v"],
+                        second["g"], second["beta"], w.gate_mode, w.lower_bound, o2)
+    # serial: rows 0..acc1-1 of window 1, then all rows of window 2 on top
+    for b in range(B):
+        n1 = int(acc1[b])
+        seq_rows = {k: torch.cat([first[k][b:b + 1, :n1], second[k][b:b + 1]], 1) for k in first}
+        sd = K.Dims(w.H, w.dk, w.dv, w.dtype)
+        stb = w.state0[b:b + 1].cuda().clone()
+        csb = w.conv_state0[b:b + 1].cuda().clone()
+        outs = []
+        committed = stb.clone()
+        for s in range(n1 + W):
+            if s == n1:
+                committed = stb.clone()
+            o = torch.empty(1, w.H, w.dv, device="cuda")
+            K.kda_decode(sd, stb, csb, w.conv_w.cuda(), *(seq_rows[k][:, s].contiguous() for k in
+                                                        ("q", "k", "v", "g", "beta")), w.gate_mode, w.lower_bound, o)
+            outs.append(o)
+        torch.cuda.synchronize()
+        assert torch.equal(torch.cat(outs[n1:], 0), o2[b])
+        assert torch.equal(committed[0], st[b])  # state committed through window 1 only
+        del csb
+
+
+# ---------------------------------------------------------------------------
+# chunked prefill
+# ---------------------------------------------------------------------------
+
+def test_prefill_tiny_fp32_config():
+    """The tiny all-fp32 workload (1 x 1 head, T=256, d=64, softplus gate): <= 1e-5."""
+    w = I.tiny()
+    r = gpu_layer_prefill(w)
+    ref = oracle_layer(w)
+    assert rel(r["o"], ref.o) < TOL_FP32
+    assert rel(r["y"], ref.y) < TOL_FP32
+    assert rel(r["state"], ref.state) < TOL_FP32
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("gate", [I.GATE_SAFE, I.GATE_SOFTPLUS])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64), (64, 128)])
+def test_prefill_varlen_parity(dtype, gate, dk, dv):
+    w = small(dtype, lens=(200, 1, 0, 64, 127, 65), H=2, d=dk, dv=dv, gate=gate, seed=dk + dv)
+    r = gpu_layer_prefill(w)
+    ref = oracle_layer(w)
+    tol = tol_for(w)
+    assert rel(r["o"], ref.o) < tol
+    assert rel(r["y"], ref.y) < tol
+    assert rel(r["state"], ref.state) < tol
+
+
+@pytest.mark.parametrize("precision", [K.PREC_FP32, K.PREC_BF16X3])
+def test_prefill_precision_policies_on_bf16_rows(precision):
+    w = small(torch.bfloat16, lens=(300, 77), H=2, d=128, gate=I.GATE_SAFE, seed=21)
+    r = gpu_layer_prefill(w, precision=precision)
+    ref = oracle_layer(w)
+    assert rel(r["y"], ref.y) < TOL_BF16
+    assert rel(r["state"], ref.state) < TOL_BF16
+
+
+def test_prefill_steep_decay_takes_exact_path():
+    """Softplus gate fed with very large raw gates: decay spans far beyond e^40 within half a block."""
+    w = small(torch.float32, lens=(150, 40), H=2, d=64, gate=I.GATE_SOFTPLUS, seed=31)
+    w.g.mul_(30.0)
+    r = gpu_layer_prefill(w)
+    ref = oracle_layer(w)
+    assert np.all(np.isfinite(r["o"].cpu().numpy()))
+    assert rel(r["o"], ref.o) < 1e-4
+    assert rel(r["state"], ref.state) < 1e-4
+
+
+def test_prefill_packed_equals_alone_bitwise():
+    w = small(torch.bfloat16, lens=(100, 64, 3, 129), H=2, d=128, seed=41)
+    full = gpu_layer_prefill(w)
+    cu = w.cu_seqlens.tolist()
+    for n in range(w.N):
+        sl = slice(cu[n], cu[n + 1])
+        one = I.Workload("one", w.H, w.dk, w.dv, torch.tensor([0, cu[n + 1] - cu[n]], dtype=torch.int32),
+                         w.q[sl], w.k[sl], w.v[sl], w.g[sl], w.beta[sl], w.z[sl], w.conv_w, w.norm_w,
+                         w.state0[n:n + 1], w.conv_state0[n:n + 1], w.gate_mode, w.lower_bound)
+        alone = gpu_layer_prefill(one)
+        assert torch.equal(alone["o"], full["o"][sl])
+        assert torch.equal(alone["state"][0], full["state"][n])
+
+
+@pytest.mark.parametrize("cut", [64, 128])
+def test_prefill_cut_at_chunk_multiple_is_bitwise(cut):
+    w = small(torch.bfloat16, lens=(300,), H=2, d=128, seed=51)
+    full = gpu_layer_prefill(w)
+    a = I.Workload("a", w.H, w.dk, w.dv, torch.tensor([0, cut], dtype=torch.int32), w.q[:cut], w.k[:cut], w.v[:cut],
+                   w.g[:cut], w.beta[:cut], w.z[:cut], w.conv_w, w.norm_w, w.state0, w.conv_state0, w.gate_mode,
+                   w.lower_bound)
+    ra = gpu_layer_prefill(a)
+    b = I.Workload("b", w.H, w.dk, w.dv, torch.tensor([0, 300 - cut], dtype=torch.int32), w.q[cut:], w.k[cut:],
+                   w.v[cut:], w.g[cut:], w.beta[cut:], w.z[cut:], w.conv_w, w.norm_w, ra["state"].cpu(),
+                   ra["prep"]["conv_state"].cpu(), w.gate_mode, w.lower_bound)
+    rb = gpu_layer_prefill(b)
+    assert torch.equal(torch.cat([ra["o"], rb["o"]]), full["o"])
+    assert torch.equal(rb["state"], full["state"])
+
+
+def test_prefill_slots_and_negative_slot():
+    w = small(torch.bfloat16, lens=(90, 70, 40), H=2, d=64, seed=61)
+    d = dims_for(w)
+    wd, p = gpu_prep(w, d)
+    pool = torch.randn(5, w.H, w.dk, w.dv, device="cuda") * 0.02
+    slots = torch.tensor([3, -1, 0], dtype=torch.int32, device="cuda")
+    pool_before = pool.clone()
+    # the state pool is indexed by slot: put each sequence's initial state there
+    pool[3] = wd.state0[0]
+    pool[0] = wd.state0[2]
+    expect_untouched = pool.clone()
+    o = torch.full((w.T, w.H, w.dv), 7.0, device="cuda")
+    ws = torch.empty(K.kda_prefill_workspace_bytes(d, w.N, w.T), dtype=torch.uint8, device="cuda")
+    K.kda_prefill_varlen(d, wd.cu_seqlens, p["q_hat"], p["k_hat"], p["v"], p["g"], p["beta"], pool, o, ws,
+                         slots=slots)
+    torch.cuda.synchronize()
+    ref = oracle_layer(w)
+    cu = w.cu_seqlens.tolist()
+    assert rel(pool[3], ref.state[0]) < TOL_BF16
+    assert rel(pool[0], ref.state[2]) < TOL_BF16
+    for s in (1, 2, 4):
+        assert torch.equal(pool[s], expect_untouched[s])
+    assert torch.all(o[cu[1]:cu[2]] == 7.0)  # skipped sequence: outputs untouched
+    assert rel(o[:cu[1]], ref.o[:cu[1]]) < TOL_BF16
+    del pool_before
+
+
+def test_errors_write_nothing():
+    w = small(torch.bfloat16, lens=(10,), H=2, d=128)
+    d = dims_for(w)
+    wd = w.to("cuda")
+    o = torch.full((1, w.H, w.dv), 3.0, device="cuda")
+    st = wd.state0.clone()
+    with pytest.raises(K.KdaError) as e:
+        K.kda_decode(d, st, wd.conv_state0, wd.conv_w, wd.q[:1], wd.k[:1], wd.v[:1], wd.g[:1], wd.beta[:1],
+                     I.GATE_SAFE, 0.5, o)  # bad lower bound
+    assert e.value.code == K.KDA_E_GATE
+    torch.cuda.synchronize()
+    assert torch.all(o == 3.0) and torch.equal(st, wd.state0)
