@@ -75,6 +75,20 @@ class Workload:
               for f in self.__dataclass_fields__}
         return Workload(**kw)
 
+    def select_heads(self, heads) -> "Workload":
+        """The same workload restricted to a subset of heads (conv channels picked per stream)."""
+        heads = list(heads)
+        H, dk, dv = self.H, self.dk, self.dv
+        ch = torch.tensor([h * dk + i for h in heads for i in range(dk)] +
+                          [H * dk + h * dk + i for h in heads for i in range(dk)] +
+                          [2 * H * dk + h * dv + i for h in heads for i in range(dv)])
+        hs = torch.tensor(heads)
+        pick = (lambda t: t[:, hs].contiguous())
+        return Workload(self.name, len(heads), dk, dv, self.cu_seqlens, pick(self.q), pick(self.k), pick(self.v),
+                        pick(self.g), pick(self.beta), pick(self.z), self.conv_w[ch].contiguous(), self.norm_w,
+                        pick(self.state0), self.conv_state0[:, :, ch].contiguous(), self.gate_mode, self.lower_bound,
+                        dict(self.meta))
+
     def f64(self, name: str) -> np.ndarray:
         """The tensor widened exactly to float64 (what the oracle consumes)."""
         return getattr(self, name).detach().cpu().to(torch.float64).numpy()

@@ -30,18 +30,7 @@ def dims_for(w: Workload, precision=None) -> K.Dims:
 
 
 def select_heads(w: Workload, heads) -> Workload:
-    """The same workload restricted to a subset of heads (heads are independent,
-    so the restriction is exact); conv channels are picked per stream."""
-    heads = list(heads)
-    H, dk, dv = w.H, w.dk, w.dv
-    ch = ([h * dk + i for h in heads for i in range(dk)] + [H * dk + h * dk + i for h in heads for i in range(dk)] +
-          [2 * H * dk + h * dv + i for h in heads for i in range(dv)])
-    ch = torch.tensor(ch)
-    hs = torch.tensor(heads)
-    return Workload(w.name, len(heads), dk, dv, w.cu_seqlens, w.q[:, hs].contiguous(), w.k[:, hs].contiguous(),
-                    w.v[:, hs].contiguous(), w.g[:, hs].contiguous(), w.beta[:, hs].contiguous(),
-                    w.z[:, hs].contiguous(), w.conv_w[ch].contiguous(), w.norm_w, w.state0[:, hs].contiguous(),
-                    w.conv_state0[:, :, ch].contiguous(), w.gate_mode, w.lower_bound, dict(w.meta))
+    return w.select_heads(heads)
 
 
 def oracle_layer(w: Workload, with_log=False):
