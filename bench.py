@@ -79,6 +79,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--unfused", action="store_true", help="run kda_prep separately instead of inside the prompt pass")
+    ap.add_argument("--precision", choices=("fp16", "bf16x3", "fp32"), default="bf16x3",
+                    help="arithmetic of the prompt path's matrix products (see kda_precision)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -97,7 +100,8 @@ def main():
     # ---------------- prompt workload ----------------
     w = I.prefill()
     T, H, dk, dv = w.T, w.H, w.dk, w.dv
-    d = K.Dims(H, dk, dv, w.dtype)
+    prec = {"fp16": K.PREC_FP16, "bf16x3": K.PREC_BF16X3, "fp32": K.PREC_FP32}[args.precision]
+    d = K.Dims(H, dk, dv, w.dtype, precision=prec)
     wd = w.to(dev)
     f = lambda *s: torch.empty(*s, device=dev, dtype=torch.float32)
     qh, kh, vv, gg, bb = f(T, H, dk), f(T, H, dk), f(T, H, dv), f(T, H, dk), f(T, H)
@@ -106,26 +110,38 @@ def main():
     o = f(T, H, dv)
     y = torch.empty(T, H, dv, device=dev, dtype=torch.bfloat16)
     ws = torch.empty(K.kda_prefill_workspace_bytes(d, w.N, T), dtype=torch.uint8, device=dev)
-    names = ("kda_prep", "kda_prefill_varlen", "gated_rmsnorm_out")
+    raw = dict(q_raw=wd.q, k_raw=wd.k, v_raw=wd.v, g_raw=wd.g, beta_logit=wd.beta, conv_weight=wd.conv_w,
+               conv_state_in=cs, conv_state_out=cs, gate_mode=w.gate_mode, lower_bound=w.lower_bound)
+    if args.unfused:
+        names = ("kda_prep", "kda_prefill_varlen", "gated_rmsnorm_out")
+    else:
+        names = ("kda_prefill_varlen", "gated_rmsnorm_out")
 
     def step(ev=None):
+        i = 0
         if ev is not None:
-            ev[0].record(stream)
-        K.kda_prep(d, wd.cu_seqlens, wd.q, wd.k, wd.v, wd.conv_w, cs, cs, wd.g, wd.beta, w.gate_mode, w.lower_bound,
-                   qh, kh, vv, gg, bb)
+            ev[i].record(stream)
+        if args.unfused:
+            K.kda_prep(d, wd.cu_seqlens, wd.q, wd.k, wd.v, wd.conv_w, cs, cs, wd.g, wd.beta, w.gate_mode,
+                       w.lower_bound, qh, kh, vv, gg, bb)
+            i += 1
+            if ev is not None:
+                ev[i].record(stream)
+            K.kda_prefill_varlen(d, wd.cu_seqlens, qh, kh, vv, gg, bb, state, o, ws)
+        else:
+            K.kda_prefill_varlen(d, wd.cu_seqlens, None, None, None, None, None, state, o, ws, raw=raw)
+        i += 1
         if ev is not None:
-            ev[1].record(stream)
-        K.kda_prefill_varlen(d, wd.cu_seqlens, qh, kh, vv, gg, bb, state, o, ws)
-        if ev is not None:
-            ev[2].record(stream)
+            ev[i].record(stream)
         K.gated_rmsnorm_out(o, wd.z, wd.norm_w, 1e-6, y)
+        i += 1
         if ev is not None:
-            ev[3].record(stream)
+            ev[i].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
@@ -156,6 +172,7 @@ def main():
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "prefill T=4096 H=16 d_k=d_v=128 bf16 rows, fp32 state, safe gate lb=-5, chunk 64",
+                   "matrix_products": args.precision, "preamble": "separate" if args.unfused else "fused",
                    "global_batch": 1, "seq_len": T, "parallelism": "none"},
         "roofline": roof,
         "entry_points_ms": per_entry,

@@ -38,8 +38,8 @@
  *     the sequence: nothing of it is read or written.
  *   - Alignment: buffers the kernels move with 128-bit accesses must be 16-byte
  *     aligned: the state, the fp32 rows q_hat/k_hat/v/g of the prompt path, the
- *     outputs o of decode and verify, a log's u, and every buffer of
- *     gated_rmsnorm_out.  Every other pointer needs its element alignment.
+ *     raw q/k/v rows handed to kda_prefill_varlen in `raw`, the outputs o of
+ *     decode and verify, a log's u, and every buffer of gated_rmsnorm_out.  Every other pointer needs its element alignment.
  *   - Errors: each call returns KDA_OK or one KDA_E_* code.  All validation
  *     happens before the first launch; on error nothing is enqueued and no
  *     output is written.  kda_last_error() gives a message (thread-local).
@@ -76,8 +76,12 @@ enum kda_act { KDA_ACT_NONE = 0, KDA_ACT_SILU = 1 };
 /* Arithmetic of the chunked prompt path's matrix products (all accumulate in fp32):
  *   FP32   fp32 matrix-core products;
  *   BF16X3 each fp32 operand split into bf16 hi + lo and the product formed as
- *          hi*hi + hi*lo + lo*hi (relative error about 2^-16 per product). */
-enum kda_precision { KDA_PREC_FP32 = 0, KDA_PREC_BF16X3 = 1 };
+ *          hi*hi + hi*lo + lo*hi (relative error about 2^-16 per product);
+ *   FP16   in the inter-chunk pass, the per-chunk operands (each entry bounded
+ *          by 1) rounded once to fp16 and the state / update operands split
+ *          into fp16 hi + lo (relative error about 2^-12 per product); the
+ *          intra-chunk products as in BF16X3. */
+enum kda_precision { KDA_PREC_FP32 = 0, KDA_PREC_BF16X3 = 1, KDA_PREC_FP16 = 2 };
 
 typedef struct kda_dims {
   int32_t num_heads;  /* H >= 1 */
@@ -121,10 +125,30 @@ int kda_prep(const kda_dims* d, int32_t num_seqs, int64_t t_tot, const int32_t* 
  * bound that depends only on num_seqs and t_tot). */
 size_t kda_prefill_workspace_bytes(const kda_dims* d, int32_t num_seqs, int64_t t_tot);
 
+/* Raw projected rows and preamble parameters, for running the preamble inside
+ * the prompt kernels (kda_prefill_varlen with a non-NULL `raw`).  Device
+ * pointers; shapes and meaning as in kda_prep. */
+typedef struct kda_raw_rows {
+  const void* q_raw;          /* [t_tot, H, d_k] in_dtype */
+  const void* k_raw;          /* [t_tot, H, d_k] */
+  const void* v_raw;          /* [t_tot, H, d_v] */
+  const void* g_raw;          /* [t_tot, H, d_k] */
+  const void* beta_logit;     /* [t_tot, H] */
+  const float* conv_weight;   /* [C, 4] fp32 */
+  const void* conv_state_in;  /* [slots, 3, C] in_dtype, read */
+  void* conv_state_out;       /* same shape, written after all reads (may equal conv_state_in) */
+  int32_t gate_mode;          /* kda_gate */
+  float lower_bound;          /* safe mode only: finite, < 0 */
+} kda_raw_rows;
+
 /* kda_prefill_varlen -- the delta rule (part 4) over packed prompt rows, in
  * 64-row chunks anchored at each sequence's first row (WY/UT form with an
  * intra-chunk lower-triangular solve, then a sequential pass over chunks).
- *   q_hat, k_hat, v, g, beta   fp32 outputs of kda_prep (g is the log decay)
+ *   q_hat, k_hat, v, g, beta   fp32 outputs of kda_prep (g is the log decay);
+ *                              ignored (may be NULL) when `raw` is given
+ *   raw     NULL, or raw rows + preamble parameters: the preamble (parts 1-3)
+ *           then runs inside the prompt kernels, with the same bits as kda_prep,
+ *           and the conv state is carried as kda_prep would carry it
  *   state   fp32 [slots, H, d_k, d_v], read as the initial state and
  *           overwritten with the final state of each sequence
  *   o       fp32 [t_tot, H, d_v], pre-norm output
@@ -133,8 +157,8 @@ size_t kda_prefill_workspace_bytes(const kda_dims* d, int32_t num_seqs, int64_t 
  * bits as the uncut prompt. */
 int kda_prefill_varlen(const kda_dims* d, int32_t num_seqs, int64_t t_tot, const int32_t* cu_seqlens,
                        const int32_t* slots, const float* q_hat, const float* k_hat, const float* v,
-                       const float* g, const float* beta, float* state, float* o, void* workspace,
-                       size_t workspace_bytes, hipStream_t stream);
+                       const float* g, const float* beta, const kda_raw_rows* raw, float* state, float* o,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* kda_decode -- one row per sequence (parts 1-4 fused): conv step on the conv
  * state, gates, norms, state step, readout.

@@ -27,7 +27,7 @@ KDA_OK, KDA_E_ARG, KDA_E_GEOMETRY, KDA_E_ALIGN, KDA_E_GATE, KDA_E_DTYPE, KDA_E_W
 DTYPE_F32, DTYPE_BF16 = 0, 1
 GATE_SOFTPLUS, GATE_SAFE = 0, 1
 ACT_NONE, ACT_SILU = 0, 1
-PREC_FP32, PREC_BF16X3 = 0, 1
+PREC_FP32, PREC_BF16X3, PREC_FP16 = 0, 1, 2
 EXPORTS = ("kda_prep", "kda_prefill_workspace_bytes", "kda_prefill_varlen", "kda_decode", "kda_verify_window",
            "gated_rmsnorm_out", "kda_last_error")
 
@@ -42,6 +42,13 @@ class KdaDims(ctypes.Structure):
     _fields_ = [("num_heads", ctypes.c_int32), ("head_dim_k", ctypes.c_int32), ("head_dim_v", ctypes.c_int32),
                 ("conv_width", ctypes.c_int32), ("in_dtype", ctypes.c_int32), ("conv_act", ctypes.c_int32),
                 ("precision", ctypes.c_int32)]
+
+
+class KdaRawRows(ctypes.Structure):
+    _fields_ = [("q_raw", ctypes.c_void_p), ("k_raw", ctypes.c_void_p), ("v_raw", ctypes.c_void_p),
+                ("g_raw", ctypes.c_void_p), ("beta_logit", ctypes.c_void_p), ("conv_weight", ctypes.c_void_p),
+                ("conv_state_in", ctypes.c_void_p), ("conv_state_out", ctypes.c_void_p),
+                ("gate_mode", ctypes.c_int32), ("lower_bound", ctypes.c_float)]
 
 
 class KdaLog(ctypes.Structure):
@@ -65,7 +72,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.kda_prep.argtypes = [D, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp, vp, vp, vp, vp]
         lib.kda_prefill_workspace_bytes.argtypes = [D, i32, i64]
         lib.kda_prefill_workspace_bytes.restype = ctypes.c_size_t
-        lib.kda_prefill_varlen.argtypes = [D, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        lib.kda_prefill_varlen.argtypes = [D, i32, i64, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(KdaRawRows), vp, vp,
+                                           vp, ctypes.c_size_t, vp]
         lib.kda_decode.argtypes = [D, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp]
         lib.kda_verify_window.argtypes = [D, i32, i32, vp, vp, vp, vp, vp, Lg, Lg, vp, vp, vp, vp, vp, i32, f32, vp, vp]
         lib.gated_rmsnorm_out.argtypes = [i64, i32, vp, vp, i32, vp, f32, vp, i32, vp]
@@ -160,15 +168,32 @@ def kda_prefill_workspace_bytes(d: Dims, num_seqs: int, t_tot: int) -> int:
     return int(load_library().kda_prefill_workspace_bytes(ctypes.byref(dims), int(num_seqs), int(t_tot)))
 
 
-def kda_prefill_varlen(d: Dims, cu_seqlens, q_hat, k_hat, v, g, beta, state, o, workspace, slots=None):
+def kda_prefill_varlen(d: Dims, cu_seqlens, q_hat, k_hat, v, g, beta, state, o, workspace, slots=None, raw=None):
+    """Chunked prompt pass.  With raw=dict(q_raw, k_raw, v_raw, g_raw, beta_logit, conv_weight, conv_state_in,
+    conv_state_out, gate_mode, lower_bound) the preamble runs inside the prompt kernels and q_hat..beta may be None."""
     lib = load_library()
-    T = q_hat.shape[0]
     N = cu_seqlens.numel() - 1
     H, dk, dv = d.num_heads, d.head_dim_k, d.head_dim_v
     _need(cu_seqlens, "cu_seqlens", torch.int32)
-    for name, t, shp in (("q_hat", q_hat, (T, H, dk)), ("k_hat", k_hat, (T, H, dk)), ("v", v, (T, H, dv)),
-                         ("g", g, (T, H, dk)), ("beta", beta, (T, H)), ("o", o, (T, H, dv))):
-        _need(t, name, torch.float32, shp)
+    rr = None
+    if raw is None:
+        T = q_hat.shape[0]
+        for name, t, shp in (("q_hat", q_hat, (T, H, dk)), ("k_hat", k_hat, (T, H, dk)), ("v", v, (T, H, dv)),
+                             ("g", g, (T, H, dk)), ("beta", beta, (T, H))):
+            _need(t, name, torch.float32, shp)
+    else:
+        T = raw["q_raw"].shape[0]
+        dt = d.in_dtype
+        for name, shp in (("q_raw", (T, H, dk)), ("k_raw", (T, H, dk)), ("v_raw", (T, H, dv)), ("g_raw", (T, H, dk)),
+                          ("beta_logit", (T, H))):
+            _need(raw[name], name, dt, shp)
+        _need(raw["conv_weight"], "conv_weight", torch.float32, (d.conv_channels, 4))
+        _need(raw["conv_state_in"], "conv_state_in", dt)
+        _need(raw["conv_state_out"], "conv_state_out", dt, raw["conv_state_in"].shape)
+        rr = KdaRawRows(*(raw[n].data_ptr() for n in ("q_raw", "k_raw", "v_raw", "g_raw", "beta_logit", "conv_weight",
+                                                      "conv_state_in", "conv_state_out")),
+                        int(raw["gate_mode"]), float(raw["lower_bound"]))
+    _need(o, "o", torch.float32, (T, H, dv))
     _need(state, "state", torch.float32)
     if state.dim() != 4 or tuple(state.shape[1:]) != (H, dk, dv):
         raise ValueError(f"state must be [slots, {H}, {dk}, {dv}]")
@@ -177,8 +202,9 @@ def kda_prefill_varlen(d: Dims, cu_seqlens, q_hat, k_hat, v, g, beta, state, o, 
         _need(slots, "slots", torch.int32, (N,))
     dims = d.c()
     _check(lib.kda_prefill_varlen(ctypes.byref(dims), N, T, _ptr(cu_seqlens), _ptr(slots), _ptr(q_hat), _ptr(k_hat),
-                                  _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o), _ptr(workspace),
-                                  workspace.numel() * workspace.element_size(), _stream()))
+                                  _ptr(v), _ptr(g), _ptr(beta), ctypes.byref(rr) if rr is not None else None,
+                                  _ptr(state), _ptr(o), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _stream()))
 
 
 def kda_decode(d: Dims, state, conv_state, conv_weight, q_raw, k_raw, v_raw, g_raw, beta_logit, gate_mode,

@@ -43,7 +43,7 @@ int check_dims(const kda_dims* d) {
     return fail(KDA_E_DTYPE, "unknown in_dtype %d", d->in_dtype);
   if (d->conv_act != KDA_ACT_NONE && d->conv_act != KDA_ACT_SILU)
     return fail(KDA_E_DTYPE, "unknown conv_act %d", d->conv_act);
-  if (d->precision != KDA_PREC_FP32 && d->precision != KDA_PREC_BF16X3)
+  if (d->precision != KDA_PREC_FP32 && d->precision != KDA_PREC_BF16X3 && d->precision != KDA_PREC_FP16)
     return fail(KDA_E_DTYPE, "unknown precision %d", d->precision);
   return KDA_OK;
 }
@@ -117,26 +117,39 @@ int kda_prep(const kda_dims* d, int32_t num_seqs, int64_t t_tot, const int32_t* 
 
 size_t kda_prefill_workspace_bytes(const kda_dims* d, int32_t num_seqs, int64_t t_tot) {
   if (check_dims(d) != KDA_OK || num_seqs < 0 || t_tot < 0) return 0;
-  return kda::prefill_workspace_bytes(d->num_heads, d->head_dim_k, d->head_dim_v, num_seqs, t_tot);
+  return kda::prefill_workspace_bytes(d->num_heads, d->head_dim_k, d->head_dim_v, d->precision, num_seqs, t_tot);
 }
 
 int kda_prefill_varlen(const kda_dims* d, int32_t num_seqs, int64_t t_tot, const int32_t* cu_seqlens,
                        const int32_t* slots, const float* q_hat, const float* k_hat, const float* v,
-                       const float* g, const float* beta, float* state, float* o, void* workspace,
-                       size_t workspace_bytes, hipStream_t stream) {
+                       const float* g, const float* beta, const kda_raw_rows* raw, float* state, float* o,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
   KDA_TRY(check_dims(d));
   if (num_seqs < 0 || t_tot < 0) return fail(KDA_E_ARG, "kda_prefill_varlen: negative size");
   if (num_seqs == 0 && t_tot > 0) return fail(KDA_E_ARG, "kda_prefill_varlen: rows without sequences");
   KDA_TRY(check_opt_ptr("kda_prefill_varlen: slots", slots));
+  if (raw) KDA_TRY(check_gate(raw->gate_mode, raw->lower_bound));
+  const unsigned eb = elem_bytes(d->in_dtype);
   if (num_seqs > 0) {
     KDA_TRY(check_ptrs("kda_prefill_varlen: cu_seqlens", {cu_seqlens}, 4));
     KDA_TRY(check_ptrs("kda_prefill_varlen: state", {state}));
+    if (raw) {
+      KDA_TRY(check_ptrs("kda_prefill_varlen: raw conv weight", {raw->conv_weight}, 4));
+      KDA_TRY(check_ptrs("kda_prefill_varlen: raw conv state", {raw->conv_state_in, raw->conv_state_out}, eb));
+    }
   }
   if (t_tot > 0) {
-    KDA_TRY(check_ptrs("kda_prefill_varlen", {q_hat, k_hat, v, g}));
-    KDA_TRY(check_ptrs("kda_prefill_varlen", {beta, o}, 4));
+    if (raw) {
+      KDA_TRY(check_ptrs("kda_prefill_varlen: raw q/k/v rows", {raw->q_raw, raw->k_raw, raw->v_raw}));
+      KDA_TRY(check_ptrs("kda_prefill_varlen: raw g/beta rows", {raw->g_raw, raw->beta_logit}, eb));
+    } else {
+      KDA_TRY(check_ptrs("kda_prefill_varlen", {q_hat, k_hat, v, g}));
+      KDA_TRY(check_ptrs("kda_prefill_varlen", {beta}, 4));
+    }
+    KDA_TRY(check_ptrs("kda_prefill_varlen: o", {o}, 4));
   }
-  const size_t need = kda::prefill_workspace_bytes(d->num_heads, d->head_dim_k, d->head_dim_v, num_seqs, t_tot);
+  const size_t need =
+      kda::prefill_workspace_bytes(d->num_heads, d->head_dim_k, d->head_dim_v, d->precision, num_seqs, t_tot);
   if (num_seqs > 0) {
     if (!workspace || workspace_bytes < need)
       return fail(KDA_E_WORKSPACE, "kda_prefill_varlen: workspace of %zu bytes needed, %zu given", need,
@@ -145,8 +158,18 @@ int kda_prefill_varlen(const kda_dims* d, int32_t num_seqs, int64_t t_tot, const
       return fail(KDA_E_ALIGN, "kda_prefill_varlen: workspace must be 256-byte aligned");
   }
   if (num_seqs == 0) return ok();
-  kda::PrefillLaunch L{d->num_heads, d->head_dim_k, d->head_dim_v, d->precision, num_seqs, t_tot, cu_seqlens, slots,
-                       q_hat, k_hat, v, g, beta, state, o, workspace, workspace_bytes};
+  kda::PrefillLaunch L{};
+  L.H = d->num_heads; L.dk = d->head_dim_k; L.dv = d->head_dim_v; L.precision = d->precision;
+  L.num_seqs = num_seqs; L.t_tot = t_tot; L.cu_seqlens = cu_seqlens; L.slots = slots;
+  L.q_hat = q_hat; L.k_hat = k_hat; L.v = v; L.g = g; L.beta = beta; L.state = state; L.o = o;
+  L.workspace = workspace; L.workspace_bytes = workspace_bytes;
+  L.in_dtype = d->in_dtype; L.act = d->conv_act;
+  if (raw) {
+    L.fused = 1; L.gate_mode = raw->gate_mode; L.lb = raw->lower_bound;
+    L.raw_q = raw->q_raw; L.raw_k = raw->k_raw; L.raw_v = raw->v_raw; L.raw_g = raw->g_raw;
+    L.raw_beta = raw->beta_logit; L.conv_w = raw->conv_weight; L.cs_in = raw->conv_state_in;
+    L.cs_out = raw->conv_state_out;
+  }
   return hip_status(kda::launch_prefill(L, stream), "kda_prefill_varlen");
 }
 

@@ -43,12 +43,39 @@ __device__ __forceinline__ float conv4_act(float w0, float w1, float w2, float w
   return act ? c * sigmoid(c) : c;
 }
 
-// sum over the 64 lanes of a wavefront; every lane receives lane 0's result so
-// all lanes hold identical bits
+// sum over the 64 lanes of a wavefront (xor butterfly: at every step both
+// partners add the same two values, so all lanes end with identical bits)
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-  return __shfl(x, 0, 64);
+  return x;
+}
+
+// One (row, head, stream) of the prompt preamble, computed by a whole
+// wavefront: lane l owns channels E*l .. E*l+E-1 (E = D/64).  tap(j, d) returns
+// conv input tap j (0 = oldest, 3 = current row) of channel d of this head; w
+// points at the head's first conv weight row of the stream.  Returns the conv
+// output after the activation, L2-normalised over the D channels when NORM.
+// The standalone preamble kernel (taps from HBM) and the fused prompt kernel
+// (taps from LDS) both call this, so they produce the same bits.
+template <int D, bool NORM, class TAP>
+__device__ __forceinline__ void conv_row(TAP tap, const float* __restrict__ w, int act, float (&out)[D / 64]) {
+  constexpr int E = D / 64;
+  const int lane = threadIdx.x & 63;
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int d = E * lane + e;
+    const float* wd = w + (int64_t)d * 4;
+    out[e] = conv4_act(wd[0], wd[1], wd[2], wd[3], tap(0, d), tap(1, d), tap(2, d), tap(3, d), act);
+    ss = fmaf(out[e], out[e], ss);
+  }
+  if constexpr (NORM) {
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss + kL2Eps);
+#pragma unroll
+    for (int e = 0; e < E; ++e) out[e] *= r;
+  }
 }
 
 // one state element's step: S' = a * S, then S = S' + k * u (explicit fma).

@@ -59,8 +59,15 @@ struct PrefillLaunch {
   float* o;
   void* workspace;
   size_t workspace_bytes;
+  // fused preamble (fused != 0): raw rows and conv / gate parameters
+  int fused, in_dtype, act, gate_mode;
+  float lb;
+  const void *raw_q, *raw_k, *raw_v, *raw_g, *raw_beta;
+  const float* conv_w;
+  const void* cs_in;
+  void* cs_out;
 };
-size_t prefill_workspace_bytes(int H, int dk, int dv, int num_seqs, int64_t t_tot);
+size_t prefill_workspace_bytes(int H, int dk, int dv, int precision, int num_seqs, int64_t t_tot);
 hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t s);
 
 }  // namespace kda

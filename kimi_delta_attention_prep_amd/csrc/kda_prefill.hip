@@ -15,33 +15,49 @@
 //   chunk_table  -- first chunk of every sequence (exclusive scan of ceil(len/64))
 //   chunk_intra  -- one workgroup per (chunk, head), all chunks in parallel:
 //                   G, A, P on the matrix cores, the 64x64 triangular solve,
-//                   W and U~; writes W, U~, Q^gamma, K_<, P, gamma_L.
+//                   W and U~.  It writes W, Q^gamma, P and K_<^T as matrix-core
+//                   operand fragments (each lane's 32-wide K slice, already
+//                   converted to the policy's operand type), U~ in the result
+//                   layout of 16-column slices, and gamma_L.
 //   chunk_scan   -- one workgroup per (sequence, head, 16 state columns), a
-//                   sequential pass over the sequence's chunks; the state slice
-//                   lives in LDS and all three products run on the matrix cores.
+//                   sequential pass over the sequence's chunks.  Each wavefront
+//                   loads its own operand fragments straight into registers
+//                   with 128-bit loads, one chunk ahead of use; only the small
+//                   B operands (the state slice and U slice) go through LDS.
 // The pairwise factors e^{G_r - G_i} are formed as e^{G_r - G_p} * e^{G_p - G_i}
-// around a pivot row p (the middle row of the 16-row block holding r), so each
-// 16x16 block of A and P is a plain matrix product.  Exponents are taken from
-// block-local prefix sums, which keeps them accurate to a few ulp of the
-// exponent itself; a diagonal block whose half-span of decay exceeds e^80 in
-// some key dim is recomputed exactly, pair by pair.
+// around pivot rows (below), so each 16x16 block of A and P is a plain matrix
+// product; exponents come from block-local prefix sums, which keeps them
+// accurate to a few ulp of the exponent itself.
+//
+// Precision policies of the matrix products (all accumulate in fp32; the
+// intra-chunk products always use fp32 or split bf16):
+//   FP32    fp32 operands, v_mfma_f32_16x16x4f32
+//   BF16X3  operands split into bf16 hi + lo, hi*hi + hi*lo + lo*hi
+//   FP16    A operands (W, Q^gamma, P, K_<^T: every entry bounded by 1) rounded
+//           once to fp16; B operands (state, U) split into fp16 hi + lo
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
 namespace kda {
 
-enum { POL_FP32 = 0, POL_BF16X3 = 1 };
+enum { POL_FP32 = 0, POL_BF16X3 = 1, POL_FP16 = 2 };
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 // ---------------------------------------------------------------------------
-// 16x16 matrix-core tile product:  acc (16x16 fp32) += A (16xK) * B (Kx16)
-// Fragment map of v_mfma_f32_16x16x4f32 and v_mfma_f32_16x16x32_bf16: lane l
-// holds row (l % 16) of A and column (l % 16) of B, with its K slice picked by
-// l / 16 (one element for fp32, eight consecutive for bf16); the result lane l
-// holds column l % 16, rows 4*(l/16) .. 4*(l/16)+3.  K is a multiple of 32.
+// 16x16 matrix-core tile product on the fly:  acc (16x16) += A (16xK) * B (Kx16)
+// Fragment map of v_mfma_f32_16x16x4f32 / v_mfma_f32_16x16x32_{bf16,f16}: lane
+// l holds row (l % 16) of A and column (l % 16) of B, with its K slice picked
+// by l / 16; the result lane l holds column l % 16, rows 4*(l/16)..4*(l/16)+3.
+// K is a multiple of 32.  Used by the intra-chunk kernel (FP32 or BF16X3).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
   hi = static_cast<__bf16>(x);
   lo = static_cast<__bf16>(x - static_cast<float>(hi));
+}
+__device__ __forceinline__ void split_f16(float x, _Float16& hi, _Float16& lo) {
+  hi = static_cast<_Float16>(x);
+  lo = static_cast<_Float16>(x - static_cast<float>(hi));
 }
 
 template <int POL, class FA, class FB>
@@ -67,47 +83,243 @@ __device__ __forceinline__ void mma16(floatx4& acc, int K, FA fa, FB fb) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Stored operand fragments.  A fragment is one lane's share of a 16-row x
+// 32-wide K block; element e of lane l sits at K index kof(l/16, e).
+// ---------------------------------------------------------------------------
+template <int POL>
+struct Frag;
+
+template <>
+struct Frag<POL_FP32> {
+  static constexpr int BYTES = 32;
+  __device__ static constexpr int kof(int g, int e) { return 4 * e + g; }
+  struct A { float v[8]; };
+  using B = A;
+  __device__ static A load_a(const uint8_t* p) {
+    A a;
+    const float4 x = *reinterpret_cast<const float4*>(p), y = *reinterpret_cast<const float4*>(p + 16);
+    a.v[0] = x.x; a.v[1] = x.y; a.v[2] = x.z; a.v[3] = x.w; a.v[4] = y.x; a.v[5] = y.y; a.v[6] = y.z; a.v[7] = y.w;
+    return a;
+  }
+  __device__ static void store_a(uint8_t* p, const float (&x)[8]) {
+    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<float4*>(p + 16) = make_float4(x[4], x[5], x[6], x[7]);
+  }
+  __device__ static B make_b(const float (&x)[8]) {
+    B b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) b.v[e] = x[e];
+    return b;
+  }
+  __device__ static floatx4 mma(floatx4 acc, const A& a, const B& b) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], acc, 0, 0, 0);
+    return acc;
+  }
+  // B operand kept in LDS as one fp32 plane [16 columns][K]: 4 consecutive K values per write
+  using P = float;
+  static constexpr int PLANES = 1;
+  __device__ static void store_b4(P* hi, P*, const floatx4& x) { *reinterpret_cast<floatx4*>(hi) = x; }
+  __device__ static B load_b(const P* hi, const P*, int g) {
+    B b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) b.v[e] = hi[kof(g, e)];
+    return b;
+  }
+};
+
+template <>
+struct Frag<POL_BF16X3> {
+  static constexpr int BYTES = 32;
+  __device__ static constexpr int kof(int g, int e) { return 8 * g + e; }
+  struct A { bf16x8 hi, lo; };
+  using B = A;
+  __device__ static A load_a(const uint8_t* p) {
+    A a;
+    a.hi = *reinterpret_cast<const bf16x8*>(p);
+    a.lo = *reinterpret_cast<const bf16x8*>(p + 16);
+    return a;
+  }
+  __device__ static B make_b(const float (&x)[8]) {
+    B b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      __bf16 h, l;
+      split_bf16(x[e], h, l);
+      b.hi[e] = h; b.lo[e] = l;
+    }
+    return b;
+  }
+  __device__ static void store_a(uint8_t* p, const float (&x)[8]) {
+    const B b = make_b(x);
+    *reinterpret_cast<bf16x8*>(p) = b.hi;
+    *reinterpret_cast<bf16x8*>(p + 16) = b.lo;
+  }
+  __device__ static floatx4 mma(floatx4 acc, const A& a, const B& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, acc, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
+  }
+  // B operand kept in LDS already split: hi and lo planes [16 columns][K] of bf16
+  using P = __bf16;
+  static constexpr int PLANES = 2;
+  __device__ static void store_b4(P* hi, P* lo, const floatx4& x) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    bf16x4 h, l;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      __bf16 a, b;
+      split_bf16(x[e], a, b);
+      h[e] = a; l[e] = b;
+    }
+    *reinterpret_cast<bf16x4*>(hi) = h;
+    *reinterpret_cast<bf16x4*>(lo) = l;
+  }
+  __device__ static B load_b(const P* hi, const P* lo, int g) {
+    B b;
+    b.hi = *reinterpret_cast<const bf16x8*>(hi + 8 * g);
+    b.lo = *reinterpret_cast<const bf16x8*>(lo + 8 * g);
+    return b;
+  }
+};
+
+template <>
+struct Frag<POL_FP16> {
+  static constexpr int BYTES = 16;
+  __device__ static constexpr int kof(int g, int e) { return 8 * g + e; }
+  struct A { f16x8 v; };
+  struct B { f16x8 hi, lo; };
+  __device__ static A load_a(const uint8_t* p) {
+    A a;
+    a.v = *reinterpret_cast<const f16x8*>(p);
+    return a;
+  }
+  __device__ static void store_a(uint8_t* p, const float (&x)[8]) {
+    f16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = static_cast<_Float16>(x[e]);
+    *reinterpret_cast<f16x8*>(p) = v;
+  }
+  __device__ static B make_b(const float (&x)[8]) {
+    B b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      _Float16 h, l;
+      split_f16(x[e], h, l);
+      b.hi[e] = h; b.lo[e] = l;
+    }
+    return b;
+  }
+  __device__ static floatx4 mma(floatx4 acc, const A& a, const B& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.v, b.lo, acc, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a.v, b.hi, acc, 0, 0, 0);
+  }
+  // B operand kept in LDS already split: hi and lo planes [16 columns][K] of fp16
+  using P = _Float16;
+  static constexpr int PLANES = 2;
+  __device__ static void store_b4(P* hi, P* lo, const floatx4& x) {
+    typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+    f16x4 h, l;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      _Float16 a, b;
+      split_f16(x[e], a, b);
+      h[e] = a; l[e] = b;
+    }
+    *reinterpret_cast<f16x4*>(hi) = h;
+    *reinterpret_cast<f16x4*>(lo) = l;
+  }
+  __device__ static B load_b(const P* hi, const P* lo, int g) {
+    B b;
+    b.hi = *reinterpret_cast<const f16x8*>(hi + 8 * g);
+    b.lo = *reinterpret_cast<const f16x8*>(lo + 8 * g);
+    return b;
+  }
+};
+
+// the intra-chunk kernel's own products: fp32 for the FP32 policy, split bf16 otherwise
+template <int POL>
+struct IntraPol { static constexpr int value = POL == POL_FP32 ? POL_FP32 : POL_BF16X3; };
+
 // e^x: the accurate library exponential for the fp32 policy, the hardware
-// exp2 for the split-bf16 policy (whose products carry ~2^-17 error anyway)
+// exp2 for the others (whose products carry a larger rounding anyway)
 template <int POL>
 __device__ __forceinline__ float pexp(float x) {
   if constexpr (POL == POL_FP32) return expf(x);
   else return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
 }
 
+// Write the A-operand fragments of a (16*MT) x (32*KB) matrix given by acc(row, k)
+// to dst[(mt * KB + kb) * 64 + lane], spread over the workgroup's threads.
+template <int POL, int NT, class ACC>
+__device__ __forceinline__ void write_afrags(uint8_t* dst, int MT, int KB, ACC acc) {
+  using F = Frag<POL>;
+  for (int item = threadIdx.x; item < MT * KB * 64; item += NT) {
+    const int lane = item & 63, blk = item >> 6, mt = blk / KB, kb = blk % KB;
+    const int row = 16 * mt + (lane & 15), g = lane >> 4;
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = acc(row, 32 * kb + F::kof(g, e));
+    F::store_a(dst + (size_t)item * F::BYTES, x);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // workspace layout
 // ---------------------------------------------------------------------------
+// Record of one (chunk, head), byte offsets; FB = fragment bytes per lane.
+//   Wf  [4 mt][dk/32 kb][64 lanes]    W        (rows 16mt.., K = key dim)
+//   Qf  [4 mt][dk/32 kb][64 lanes]    Q^gamma
+//   Pf  [4 mt][2 kb][64 lanes]        P        (K = chunk row)
+//   Kf  [dk/16 mt][2 kb][64 lanes]    K_<^T    (rows = key dim, K = chunk row)
+//   Ut  [dv/16 slice][4 mt][64 lanes][4] fp32  U~ in the matrix-core result layout
+//   gL  [dk] fp32                     gamma_L = e^{G_last}
 struct RecLayout {
-  int64_t W, Qg, Kl, Ut, P, gL, floats;  // offsets (floats) inside one (chunk, head) record
+  int64_t Wf, Qf, Pf, Kf, Ut, gL, bytes;
 };
-__host__ __device__ inline RecLayout rec_layout(int dk, int dv) {
+__host__ __device__ inline RecLayout rec_layout(int dk, int dv, int fb) {
   RecLayout r;
-  r.W = 0;
-  r.Qg = r.W + 64 * dk;
-  r.Kl = r.Qg + 64 * dk;
-  r.Ut = r.Kl + 64 * dk;
-  r.P = r.Ut + 64 * dv;
-  r.gL = r.P + 64 * 64;
-  r.floats = (r.gL + dk + 63) / 64 * 64;  // 256-byte aligned records
+  const int64_t fs = 64 * (int64_t)fb;
+  r.Wf = 0;
+  r.Qf = r.Wf + 4 * (dk / 32) * fs;
+  r.Pf = r.Qf + 4 * (dk / 32) * fs;
+  r.Kf = r.Pf + 4 * 2 * fs;
+  r.Ut = r.Kf + (dk / 16) * 2 * fs;
+  r.gL = r.Ut + (int64_t)64 * dv * 4;
+  r.bytes = (r.gL + (int64_t)dk * 4 + 255) / 256 * 256;
   return r;
 }
+static inline int frag_bytes(int precision) { return precision == POL_FP16 ? 16 : 32; }
 static inline int64_t max_chunks(int num_seqs, int64_t t_tot) { return t_tot / kChunk + num_seqs; }
-static inline size_t table_bytes(int num_seqs) { return ((size_t)(num_seqs + 1) * 4 + 255) / 256 * 256; }
+// chunk table, then a 1 KiB sink that absorbs stores of rows past a sequence's end
+static inline size_t table_bytes(int num_seqs) { return ((size_t)(num_seqs + 1) * 4 + 255) / 256 * 256 + 1024; }
 
-size_t prefill_workspace_bytes(int H, int dk, int dv, int num_seqs, int64_t t_tot) {
-  const RecLayout rl = rec_layout(dk, dv);
-  return table_bytes(num_seqs) + (size_t)max_chunks(num_seqs, t_tot) * H * rl.floats * sizeof(float);
+size_t prefill_workspace_bytes(int H, int dk, int dv, int precision, int num_seqs, int64_t t_tot) {
+  const RecLayout rl = rec_layout(dk, dv, frag_bytes(precision));
+  return table_bytes(num_seqs) + (size_t)max_chunks(num_seqs, t_tot) * H * (size_t)rl.bytes;
 }
+
+// raw rows and preamble parameters when the preamble runs inside the prompt kernels
+struct RawRowsArgs {
+  const void *q, *k, *v, *g, *beta;
+  const float* conv_w;
+  const void* cs_in;
+  void* cs_out;
+  int act, gate_mode;
+  float lb;
+};
 
 struct PrefillArgs {
   int H, num_seqs;
+  RawRowsArgs raw;
   const int32_t *cu, *slots;
   const float *q, *k, *v, *g, *beta;
   float *state, *o;
   int32_t* chunk_off;  // [num_seqs + 1]
-  float* recs;         // [max_chunks][H][rec floats]
-  int64_t rec_floats;
+  float* sink;         // [256] target of stores that must not land in o
+  uint8_t* recs;       // [max_chunks][H][rec bytes]
+  int64_t rec_bytes;
 };
 
 // ---------------------------------------------------------------------------
@@ -149,18 +361,25 @@ __device__ __forceinline__ int chunk_seq(const int32_t* chunk_off, int num_seqs,
 // ---------------------------------------------------------------------------
 // intra-chunk kernel
 //
-// Pivots.  Inside diagonal block R (rows 16R..16R+15) the pivot is its middle
-// row m_R = 16R+8 and gloc_r = G_r - G_{m_R} (a block-local prefix difference):
-//   A/P block (R,R): left k_r e^{gloc_r} (or q_r e^{gloc_r}), right k_i e^{-gloc_i}.
-// For an off-diagonal block (R,I), I < R, the pivot is the first row 16R of R:
-//   left  = k_r e^{gloc_r} * e^{-gloc_{16R}}            = k_r e^{G_r - G_{16R}}  <= |k_r|
-//   right = k_i e^{-gloc_i} * e^{G_{16R} - G_{m_I}}      = k_i e^{G_{16R} - G_i}  <= |k_i|
-// While every |gloc| <= 40 no factor overflows and a factor that underflows
-// can only drop terms below e^-47, so the products are as exact as fp32
-// allows.  A chunk with a wider half-block decay span (a key dim decaying by
-// more than e^40 over 8 rows) is recomputed exactly from its raw rows.
+// One workgroup (8 wavefronts) per (chunk, head).  Pivots: every 16-row block R
+// is anchored at its first row, gl_r = G_r - G_{16R} (a block-local prefix sum,
+// so exponents carry only the rounding of the decay they describe):
+//   diagonal block (R,R):  left  x_r e^{gl_r}            (<= |x_r|, x = k or q)
+//                          right k_i e^{-gl_i}           (<= |k_i| e^{span_R})
+//   block (R,I), I < R:    left  x_r e^{gl_r}
+//                          right k_i e^{D_RI - gl_i}     (<= |k_i|, D_RI = G_{16R} - G_{16I})
+// Each operand is one exponential of a small exponent times a unit-norm row.
+// While every block's decay span G_{16R} - G_{16R+15} stays within e^80, no
+// factor overflows, and a right factor that underflows only drops terms below
+// e^-87.  A chunk with a steeper block is recomputed pair by pair.  Q^gamma,
+// K_< and K^gamma are single exponentials of block-local sums: e^{G_{16R}+gl_r},
+// e^{G_last - G_{16I} - gl_i}, so they are exact to fp32 rounding whatever the decay.
+//
+// With a raw-row descriptor the kernel also runs the preamble (conv + SiLU, L2
+// norms, gates, beta) itself, through the same per-row device function as the
+// standalone preamble kernel, so the fused and unfused paths agree bit for bit.
 // ---------------------------------------------------------------------------
-constexpr float kSpanGuard = 40.0f;
+constexpr float kSpanGuard = 80.0f;
 
 template <int DK, int DV>
 struct IntraSmem {
@@ -168,41 +387,40 @@ struct IntraSmem {
   static constexpr int DM = DK > DV ? DK : DV;
   static constexpr int PK = DM + 4;  // row stride of the 64 x d tiles
   static constexpr int PL = L + 4;   // row stride of the 64 x 64 tiles
-  static constexpr int T0 = 0;                 // k e^{gloc}; later b e^{G} k        [L][PK]
-  static constexpr int T1 = T0 + L * PK;       // q e^{gloc}; later b v              [L][PK]
-  static constexpr int T2 = T1 + L * PK;       // block prefix of g; then k e^{-gloc} [L][PK]
-  static constexpr int TA = T2 + L * PK;       // A                                  [L][PL]
-  static constexpr int TP = TA + L * PL;       // P, then X                          [L][PL]
-  static constexpr int TB = TP + L * PL;       // beta                               [L]
-  static constexpr int TPV = TB + L;           // block prefix at the pivot row      [4][DK]
-  static constexpr int TEG = TPV + 4 * DK;     // e^{G_{m_R}}                        [4][DK]
-  static constexpr int TEL = TEG + 4 * DK;     // e^{G_last - G_{m_R}}               [4][DK]
-  static constexpr int TEF = TEL + 4 * DK;     // e^{-gloc_{16R}}                    [4][DK]
-  static constexpr int TEE = TEF + 4 * DK;     // e^{G_{16R} - G_{m_I}}, I < R       [6][DK]
-  static constexpr int TY = TEE + 6 * DK;      // 16x16 scratch of the solve         [16][17]
-  static constexpr int TFLAG = TY + 16 * 17;   // 1 int: chunk takes the exact path
+  static constexpr int T0 = 0;                // k_hat; later W                      [L][PK]
+  static constexpr int T1 = T0 + L * PK;      // q_hat; later b v                    [L][PK]
+  static constexpr int T2 = T1 + L * PK;      // g, then gl; later b e^{G} k          [L][PK]
+  static constexpr int TA = T2 + L * PK;      // A                                   [L][PL]
+  static constexpr int TP = TA + L * PL;      // P, then X                           [L][PL]
+  static constexpr int TB = TP + L * PL;      // beta                                [L]
+  static constexpr int TGF = TB + L;          // G_{16R} from the chunk start        [4][DK]
+  static constexpr int TX = TGF + 4 * DK;     // G_last - G_{16I}                    [4][DK]
+  static constexpr int TD = TX + 4 * DK;      // D_RI = G_{16R} - G_{16I}, I < R      [6][DK]
+  static constexpr int TG0 = TD + 6 * DK;     // g at each block's first row         [4][DK]
+  static constexpr int TY = TG0 + 4 * DK;     // solve scratch                       [2][16][17]
+  static constexpr int TFLAG = TY + 2 * 16 * 17;
   static constexpr int FLOATS = TFLAG + 4;
   static constexpr size_t BYTES = FLOATS * sizeof(float);
 };
 
 __device__ __forceinline__ int pair_index(int R, int I) { return R * (R - 1) / 2 + I; }  // I < R
 
-template <int DK, int DV, int POL>
-__global__ __launch_bounds__(256) void chunk_intra_kernel(PrefillArgs p) {
+template <int DK, int DV, int POL, typename RawT, bool FUSED>
+__global__ __launch_bounds__(512) void chunk_intra_kernel(PrefillArgs p) {
   using SM = IntraSmem<DK, DV>;
-  constexpr int L = SM::L, PK = SM::PK, PL = SM::PL;
+  constexpr int IP = IntraPol<POL>::value;
+  constexpr int L = SM::L, PK = SM::PK, PL = SM::PL, NT = 512;
   extern __shared__ __align__(16) float smem[];
-  float* sKl = smem + SM::T0;
-  float* sQl = smem + SM::T1;
-  float* sKr = smem + SM::T2;
+  float* sK = smem + SM::T0;
+  float* sQ = smem + SM::T1;
+  float* sG = smem + SM::T2;
   float* sA = smem + SM::TA;
   float* sP = smem + SM::TP;
   float* sBeta = smem + SM::TB;
-  float* sPv = smem + SM::TPV;
-  float* sEG = smem + SM::TEG;
-  float* sEL = smem + SM::TEL;
-  float* sEF = smem + SM::TEF;
-  float* sEE = smem + SM::TEE;
+  float* sGF = smem + SM::TGF;
+  float* sX = smem + SM::TX;
+  float* sD = smem + SM::TD;
+  float* sG0 = smem + SM::TG0;
   float* sY = smem + SM::TY;
   int* sFlag = reinterpret_cast<int*>(smem + SM::TFLAG);
 
@@ -211,406 +429,584 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(PrefillArgs p) {
   const int total = p.chunk_off[p.num_seqs];
   if (c >= total) return;
   const int n = chunk_seq(p.chunk_off, p.num_seqs, c);
-  const int64_t start = (int64_t)p.cu[n] + (int64_t)(c - p.chunk_off[n]) * L;
+  const int slot = p.slots ? p.slots[n] : n;
+  if (slot < 0) return;  // the sequence is skipped: nothing of it is read or written
+  const int64_t t0 = p.cu[n];
+  const int64_t start = t0 + (int64_t)(c - p.chunk_off[n]) * L;
   const int len = (int)min((int64_t)L, (int64_t)p.cu[n + 1] - start);
-  float* rec = p.recs + ((int64_t)c * H + h) * p.rec_floats;
-  const RecLayout rl = rec_layout(DK, DV);
-  auto row_off = [&](int r, int d) -> int64_t { return ((start + r) * H + h) * DK + d; };
+  uint8_t* rec = p.recs + ((int64_t)c * H + h) * p.rec_bytes;
+  const RecLayout rl = rec_layout(DK, DV, Frag<POL>::BYTES);
+  const int64_t Cch = (int64_t)H * (2 * DK + DV);
+  const RawT* raw_cs = FUSED ? static_cast<const RawT*>(p.raw.cs_in) + (int64_t)slot * 3 * Cch : nullptr;
 
-  // 1. rows of k, q, g (zero beyond the chunk's last row) and beta
-  for (int idx = t; idx < L * (DK / 4); idx += 256) {
-    const int r = idx / (DK / 4), c4 = 4 * (idx % (DK / 4));
-    float4 kk = {0.f, 0.f, 0.f, 0.f}, qq = kk, gg = kk;
-    if (r < len) {
-      kk = *reinterpret_cast<const float4*>(p.k + row_off(r, c4));
-      qq = *reinterpret_cast<const float4*>(p.q + row_off(r, c4));
-      gg = *reinterpret_cast<const float4*>(p.g + row_off(r, c4));
+  // 1. rows: k_hat, q_hat, g (zero past the chunk's last row) and beta
+  // Fused: each raw stream's 67 rows (3 halo rows, then the chunk) are staged
+  // in LDS with 16-byte loads -- halo rows come from the sequence's previous
+  // rows, or from its carried conv state at the sequence start -- and the
+  // per-row preamble then reads its conv taps from there.
+  RawT* stage = reinterpret_cast<RawT*>(sA);  // [67][D] raw rows, over the A / P tiles
+  auto stage_rows = [&](const RawT* src, int D, int64_t ch0) {
+    constexpr int VE = 16 / sizeof(RawT);  // elements per 16-byte load
+    const int per_row = D / VE;
+    const int64_t width = (int64_t)H * D;
+    for (int idx = t; idx < (L + 3) * per_row; idx += NT) {
+      const int sr = idx / per_row, c0 = (idx % per_row) * VE;
+      const int64_t pos = start - 3 + sr;  // packed row of this staged row
+      uint4 x = {0u, 0u, 0u, 0u};
+      if (sr < len + 3) {
+        if (pos >= t0) x = *reinterpret_cast<const uint4*>(src + pos * width + (int64_t)h * D + c0);
+        else {
+          // carried conv state row 3 + (pos - t0); its channels are not 16-byte aligned in general
+          const RawT* cr = raw_cs + (3 + (pos - t0)) * Cch + ch0 + c0;
+          RawT tmp[VE];
+#pragma unroll
+          for (int e = 0; e < VE; ++e) tmp[e] = cr[e];
+          x = *reinterpret_cast<const uint4*>(tmp);
+        }
+      }
+      *reinterpret_cast<uint4*>(stage + sr * D + c0) = x;
     }
-    *reinterpret_cast<float4*>(&sKl[r * PK + c4]) = kk;
-    *reinterpret_cast<float4*>(&sQl[r * PK + c4]) = qq;
-    *reinterpret_cast<float4*>(&sKr[r * PK + c4]) = gg;
+  };
+  if constexpr (FUSED) {
+    constexpr int E = DK / 64;
+    const int64_t wk = (int64_t)H * DK;
+    for (int s = 0; s < 2; ++s) {  // q, then k
+      const RawT* src = static_cast<const RawT*>(s == 0 ? p.raw.q : p.raw.k);
+      const int64_t ch0 = (s == 0 ? 0 : wk) + (int64_t)h * DK;
+      float* dst = s == 0 ? sQ : sK;
+      stage_rows(src, DK, ch0);
+      __syncthreads();
+      for (int r = wave; r < L; r += NT / 64) {
+        float x[E];
+        conv_row<DK, true>([&](int j, int d) { return to_f32(stage[(r + j) * DK + d]); }, p.raw.conv_w + ch0 * 4,
+                           p.raw.act, x);
+#pragma unroll
+        for (int e = 0; e < E; ++e) dst[r * PK + E * lane + e] = r < len ? x[e] : 0.f;
+      }
+      __syncthreads();
+    }
+    const RawT* rg = static_cast<const RawT*>(p.raw.g);
+    for (int idx = t; idx < L * DK; idx += NT) {
+      const int r = idx / DK, d = idx % DK;
+      sG[r * PK + d] = r < len ? log_decay(to_f32(rg[((start + r) * H + h) * DK + d]), p.raw.gate_mode, p.raw.lb) : 0.f;
+    }
+    if (t < L) sBeta[t] = t < len ? sigmoid(to_f32(static_cast<const RawT*>(p.raw.beta)[(start + t) * H + h])) : 0.f;
+  } else {
+    for (int idx = t; idx < L * (DK / 4); idx += NT) {
+      const int r = idx / (DK / 4), c4 = 4 * (idx % (DK / 4));
+      float4 kk = {0.f, 0.f, 0.f, 0.f}, qq = kk, gg = kk;
+      if (r < len) {
+        const int64_t off = ((start + r) * H + h) * DK + c4;
+        kk = *reinterpret_cast<const float4*>(p.k + off);
+        qq = *reinterpret_cast<const float4*>(p.q + off);
+        gg = *reinterpret_cast<const float4*>(p.g + off);
+      }
+      *reinterpret_cast<float4*>(&sK[r * PK + c4]) = kk;
+      *reinterpret_cast<float4*>(&sQ[r * PK + c4]) = qq;
+      *reinterpret_cast<float4*>(&sG[r * PK + c4]) = gg;
+    }
+    if (t < L) sBeta[t] = t < len ? p.beta[(start + t) * H + h] : 0.f;
   }
-  if (t < L) sBeta[t] = t < len ? p.beta[(start + t) * H + h] : 0.f;
   if (t == 0) sFlag[0] = 0;
   __syncthreads();
 
-  // 2. block-local inclusive prefix sums of g over each 16-row block (in place)
-  for (int item = t; item < 4 * DK; item += 256) {
-    const int R = item / DK, d = item % DK;
+  // 2. per (block R, key dim d): gl_r = sum of g over rows 16R+1..r (block-local prefix)
+  if (t < 4 * DK) {
+    const int R = t / DK, d = t % DK;
+    sG0[R * DK + d] = sG[(16 * R) * PK + d];
+    sG[(16 * R) * PK + d] = 0.f;
     float run = 0.f;
-    for (int r = 16 * R; r < 16 * R + 16; ++r) {
-      run += sKr[r * PK + d];
-      sKr[r * PK + d] = run;
+    for (int r = 16 * R + 1; r < 16 * R + 16; ++r) {
+      run += sG[r * PK + d];
+      sG[r * PK + d] = run;
     }
+    if (-run > kSpanGuard) atomicOr(sFlag, 1);  // the block's decay span G_{16R} - G_{16R+15}
   }
   __syncthreads();
 
-  // 3. per key dim, from block prefixes only (no differences of large sums):
-  //    pv[R] = prefix at m_R, tot[R] = block total, G at pivots and the last row
+  // 3. per key dim, from block-local sums: T_R = G_{16R+16} - G_{16R}, G_{16R}, G_last - G_{16I}, D_RI
   if (t < DK) {
     const int d = t;
-    float pv[4], tot[4], first[4];
+    float T[3];
 #pragma unroll
-    for (int R = 0; R < 4; ++R) {
-      pv[R] = sKr[(16 * R + 8) * PK + d];
-      tot[R] = sKr[(16 * R + 15) * PK + d];
-      first[R] = sKr[(16 * R) * PK + d];
-    }
+    for (int R = 0; R < 3; ++R) T[R] = sG[(16 * R + 15) * PK + d] + sG0[(R + 1) * DK + d];
     const int Rl = (len - 1) / 16;
-    const float pl = sKr[(len - 1) * PK + d];
-    float off = 0.f;  // G at the row before block R
-    float gl = 0.f;   // G at the last row
+    const float glL = sG[(len - 1) * PK + d];
+    float gf = sG0[d];
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
-      if (R == Rl) gl = off + pl;
-      sPv[R * DK + d] = pv[R];
-      sEG[R * DK + d] = pexp<POL>(off + pv[R]);
-      // G_last - G_{m_R}: rows m_R+1 .. len-1 (zero when the pivot lies past the last row)
-      float gLp = 0.f;
-      if (R < Rl) {
-        gLp = tot[R] - pv[R];
-        for (int Rm = R + 1; Rm < Rl; ++Rm) gLp += tot[Rm];
-        gLp += pl;
-      } else if (R == Rl && 16 * R + 8 < len) {
-        gLp = pl - pv[R];
+      sGF[R * DK + d] = gf;
+      float x = 0.f;  // G_last - G_{16R}: blocks past the last row hold only zero rows
+      if (R <= Rl) {
+        x = glL;
+        for (int J = R; J < Rl; ++J) x += T[J];
       }
-      sEL[R * DK + d] = pexp<POL>(gLp);
-      sEF[R * DK + d] = pexp<POL>(-(first[R] - pv[R]));
-      // G_{16R} - G_{m_I} for I < R: rows m_I+1 .. 16R
+      sX[R * DK + d] = x;
       for (int I = 0; I < R; ++I) {
-        float e = tot[I] - pv[I];
-        for (int Rm = I + 1; Rm < R; ++Rm) e += tot[Rm];
-        e += first[R];
-        sEE[pair_index(R, I) * DK + d] = pexp<POL>(e);
+        float dd = 0.f;
+        for (int J = I; J < R; ++J) dd += T[J];
+        sD[pair_index(R, I) * DK + d] = dd;
       }
-      // the exponents inside block R span [gloc(last row), gloc(first row)]
-      if (fmaxf(first[R] - pv[R], pv[R] - tot[R]) > kSpanGuard) atomicOr(sFlag, 1);
-      off += tot[R];
+      if (R < 3) gf += T[R];
     }
-    rec[rl.gL + d] = pexp<POL>(gl);
+    float glast = sG0[d];
+    for (int J = 0; J < Rl; ++J) glast += T[J];
+    reinterpret_cast<float*>(rec + rl.gL)[d] = pexp<POL>(glast + glL);
   }
   __syncthreads();
   const bool exact = sFlag[0] != 0;
 
-  // 4. elementwise: pivot operands, Q^gamma = e^{G_r} q_r and K_< = e^{G_last - G_r} k_r
-  for (int idx = t; idx < L * DK; idx += 256) {
-    const int r = idx / DK, d = idx % DK, R = r / 16;
-    const float gloc = fminf(fmaxf(sKr[r * PK + d] - sPv[R * DK + d], -kSpanGuard), kSpanGuard);
-    const float ep = pexp<POL>(gloc), em = pexp<POL>(-gloc);
-    const float kk = sKl[r * PK + d], qq = sQl[r * PK + d];
-    const float kl = kk * ep, ql = qq * ep, kr = kk * em;
-    sKl[r * PK + d] = kl;
-    sQl[r * PK + d] = ql;
-    sKr[r * PK + d] = kr;
-    rec[rl.Qg + r * DK + d] = sEG[R * DK + d] * ql;
-    rec[rl.Kl + r * DK + d] = sEL[R * DK + d] * kr;
-  }
-  __syncthreads();
-
+  // 4. A and P: 10 blocks x {A, P} = 20 tile products over the 8 wavefronts
   if (!exact) {
-    // 5. A and P, one 16x16 block pair (R >= I) at a time on the matrix cores
-    for (int blk = wave; blk < 10; blk += 4) {
+    for (int item = wave; item < 20; item += NT / 64) {
+      const int blk = item >> 1;
+      const bool isP = item & 1;
       int R = 0, I = blk;  // blocks in order (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) ...
       while (I > R) { I -= R + 1; ++R; }
-      floatx4 accA = {0.f, 0.f, 0.f, 0.f}, accP = accA;
-      if (I == R) {
-        auto fr = [&](int kk, int j) { return sKr[(16 * I + j) * PK + kk]; };
-        mma16<POL>(accA, DK, [&](int i, int kk) { return sKl[(16 * R + i) * PK + kk]; }, fr);
-        mma16<POL>(accP, DK, [&](int i, int kk) { return sQl[(16 * R + i) * PK + kk]; }, fr);
-      } else {
-        const float* ee = &sEE[pair_index(R, I) * DK];
-        const float* ef = &sEF[R * DK];
-        auto fr = [&](int kk, int j) { return sKr[(16 * I + j) * PK + kk] * ee[kk]; };
-        mma16<POL>(accA, DK, [&](int i, int kk) { return sKl[(16 * R + i) * PK + kk] * ef[kk]; }, fr);
-        mma16<POL>(accP, DK, [&](int i, int kk) { return sQl[(16 * R + i) * PK + kk] * ef[kk]; }, fr);
-      }
+      const float* x = isP ? sQ : sK;
+      const float* dd = I < R ? &sD[pair_index(R, I) * DK] : nullptr;
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      mma16<IP>(acc, DK,
+                [&](int i, int kk) {
+                  const int r = 16 * R + i;
+                  return x[r * PK + kk] * pexp<POL>(sG[r * PK + kk]);
+                },
+                [&](int kk, int j) {
+                  const int r = 16 * I + j;
+                  const float e = fmaxf(sG[r * PK + kk], -kSpanGuard);
+                  return sK[r * PK + kk] * pexp<POL>((dd ? dd[kk] : 0.f) - e);
+                });
       const int col = lane & 15, g4 = lane >> 4;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int rr = 16 * R + 4 * g4 + v, ii = 16 * I + col;
-        sA[rr * PL + ii] = (ii < rr) ? sBeta[rr] * accA[v] : 0.f;
-        sP[rr * PL + ii] = (ii <= rr) ? accP[v] : 0.f;
+        if (isP) sP[rr * PL + ii] = (ii <= rr) ? acc[v] : 0.f;
+        else sA[rr * PL + ii] = (ii < rr) ? sBeta[rr] * acc[v] : 0.f;
       }
     }
-    for (int idx = t; idx < L * L; idx += 256) {  // strictly-upper blocks are zero
+    for (int idx = t; idx < L * L; idx += NT) {  // strictly-upper blocks are zero
       const int rr = idx / L, ii = idx % L;
       if ((ii >> 4) > (rr >> 4)) { sA[rr * PL + ii] = 0.f; sP[rr * PL + ii] = 0.f; }
     }
   } else {
-    // 5'. exact path: G as a full-chunk prefix, every factor as one exponential
-    float* sG = sKl;   // G_r            [L][PK]
-    float* sK0 = sQl;  // k rows         [L][PK]
-    float* sQ0 = sKr;  // q rows         [L][PK]
-    for (int idx = t; idx < L * DK; idx += 256) {
-      const int r = idx / DK, d = idx % DK;
-      sK0[r * PK + d] = r < len ? p.k[row_off(r, d)] : 0.f;
-      sQ0[r * PK + d] = r < len ? p.q[row_off(r, d)] : 0.f;
-    }
-    if (t < DK) {
-      float run = 0.f;
-      for (int r = 0; r < L; ++r) {
-        run += r < len ? p.g[row_off(r, t)] : 0.f;
-        sG[r * PK + t] = run;
-      }
-    }
-    __syncthreads();
-    for (int pr = t; pr < L * L; pr += 256) {
+    // exact path: every pair (r, i <= r) with one exponential of G_r - G_i per key dim
+    for (int pr = t; pr < L * L; pr += NT) {
       const int r = pr / L, i = pr % L;
       float sa = 0.f, sp = 0.f;
       if (i <= r) {
+        const int R = r / 16, I = i / 16;
         for (int d = 0; d < DK; ++d) {
-          const float e = expf(sG[r * PK + d] - sG[i * PK + d]);
-          sa = fmaf(sK0[r * PK + d] * sK0[i * PK + d], e, sa);
-          sp = fmaf(sQ0[r * PK + d] * sK0[i * PK + d], e, sp);
+          const float dg = (sGF[R * DK + d] - sGF[I * DK + d]) + (sG[r * PK + d] - sG[i * PK + d]);
+          const float e = expf(dg);
+          sa = fmaf(sK[r * PK + d] * sK[i * PK + d], e, sa);
+          sp = fmaf(sQ[r * PK + d] * sK[i * PK + d], e, sp);
         }
       }
       sA[r * PL + i] = (i < r) ? sBeta[r] * sa : 0.f;
       sP[r * PL + i] = (i <= r) ? sp : 0.f;
     }
-    for (int idx = t; idx < L * DK; idx += 256) {
-      const int r = idx / DK, d = idx % DK;
-      const float G = sG[r * PK + d], GL = sG[(len - 1) * PK + d];
-      rec[rl.Qg + r * DK + d] = expf(G) * sQ0[r * PK + d];
-      rec[rl.Kl + r * DK + d] = expf(GL - G) * sK0[r * PK + d];
-    }
   }
   __syncthreads();
 
-  // 6. P to the record; then X = (I + A)^{-1} into the P tile
-  for (int idx = t; idx < L * L; idx += 256) {
-    const int rr = idx / L, ii = idx % L;
-    rec[rl.P + rr * L + ii] = sP[rr * PL + ii];
-  }
+  // 5. operand fragments of Q^gamma = e^{G_r} q_r, K_<^T (e^{G_last - G_i} k_i) and P
+  write_afrags<POL, NT>(rec + rl.Qf, 4, DK / 32, [&](int r, int d) {
+    return sQ[r * PK + d] * pexp<POL>(sGF[(r / 16) * DK + d] + sG[r * PK + d]);
+  });
+  write_afrags<POL, NT>(rec + rl.Kf, DK / 16, 2, [&](int d, int r) {
+    return sK[r * PK + d] * pexp<POL>(sX[(r / 16) * DK + d] - sG[r * PK + d]);
+  });
+  write_afrags<POL, NT>(rec + rl.Pf, 4, 2, [&](int r, int i) { return sP[r * PL + i]; });
   __syncthreads();
-  float* sX = sP;
-  for (int idx = t; idx < L * L; idx += 256) sX[(idx / L) * PL + idx % L] = 0.f;
+
+  // 6. X = (I + A)^{-1} into the P tile
+  float* sXi = sP;
+  for (int idx = t; idx < L * L; idx += NT) sXi[(idx / L) * PL + idx % L] = 0.f;
   __syncthreads();
   if (t < L) {  // diagonal blocks by forward substitution, one column per thread
     const int R = t / 16, cc = t % 16, b0 = 16 * R;
-    float x[16];
+    float xv[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float s = (r == cc) ? 1.f : 0.f;
+      float sacc = (r == cc) ? 1.f : 0.f;
 #pragma unroll
-      for (int i = 0; i < r; ++i) s = fmaf(-sA[(b0 + r) * PL + b0 + i], x[i], s);
-      x[r] = (r >= cc) ? s : 0.f;
+      for (int i = 0; i < r; ++i) sacc = fmaf(-sA[(b0 + r) * PL + b0 + i], xv[i], sacc);
+      xv[r] = (r >= cc) ? sacc : 0.f;
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sX[(b0 + r) * PL + b0 + cc] = x[r];
+    for (int r = 0; r < 16; ++r) sXi[(b0 + r) * PL + b0 + cc] = xv[r];
   }
   __syncthreads();
-  // off-diagonal blocks, nearest diagonals first: X_RI = -X_RR sum_{J=I}^{R-1} A_RJ X_JI
+  // off-diagonal blocks, nearest diagonals first (two blocks at a time):
+  // X_RI = -X_RR sum_{J=I}^{R-1} A_RJ X_JI
   for (int dist = 1; dist < 4; ++dist) {
-    for (int I = 0; I + dist < 4; ++I) {
-      const int R = I + dist;
-      const int r = t / 16, cc = t % 16;
-      float y = 0.f;
-      for (int J = I; J < R; ++J)
-        for (int kk = 0; kk < 16; ++kk)
-          y = fmaf(sA[(16 * R + r) * PL + 16 * J + kk], sX[(16 * J + kk) * PL + 16 * I + cc], y);
-      sY[r * 17 + cc] = y;
+    for (int I0 = 0; I0 + dist < 4; I0 += 2) {
+      const int I = I0 + (t >> 8), R = I + dist;
+      const bool act = (t >> 8) < 2 && R < 4;
+      const int r = (t >> 4) & 15, cc = t & 15;
+      float* y = sY + (t >> 8) * 16 * 17;
+      if (act) {
+        float acc = 0.f;
+        for (int J = I; J < R; ++J)
+          for (int kk = 0; kk < 16; ++kk)
+            acc = fmaf(sA[(16 * R + r) * PL + 16 * J + kk], sXi[(16 * J + kk) * PL + 16 * I + cc], acc);
+        y[r * 17 + cc] = acc;
+      }
       __syncthreads();
-      float x = 0.f;
-      for (int kk = 0; kk <= r; ++kk) x = fmaf(sX[(16 * R + r) * PL + 16 * R + kk], sY[kk * 17 + cc], x);
-      sX[(16 * R + r) * PL + 16 * I + cc] = -x;
+      if (act) {
+        float acc = 0.f;
+        for (int kk = 0; kk <= r; ++kk) acc = fmaf(sXi[(16 * R + r) * PL + 16 * R + kk], y[kk * 17 + cc], acc);
+        sXi[(16 * R + r) * PL + 16 * I + cc] = -acc;
+      }
       __syncthreads();
     }
   }
 
-  // 7. right-hand sides: b_r e^{G_r} k_r into T0, b_r v_r into T1
-  for (int idx = t; idx < L * DK; idx += 256) {
+  // 7. right-hand sides: b_r e^{G_r} k_r into T2 (over gl), b_r v_r into T1
+  for (int idx = t; idx < L * DK; idx += NT) {
     const int r = idx / DK, d = idx % DK;
-    const float kg = exact ? expf(sKl[r * PK + d]) * sQl[r * PK + d]   // exact path: T0 = G, T1 = k
-                           : sEG[(r / 16) * DK + d] * sKl[r * PK + d];
-    sKl[r * PK + d] = sBeta[r] * kg;
+    sG[r * PK + d] = sBeta[r] * (sK[r * PK + d] * pexp<POL>(sGF[(r / 16) * DK + d] + sG[r * PK + d]));
   }
-  __syncthreads();
-  for (int idx = t; idx < L * (DV / 4); idx += 256) {
-    const int r = idx / (DV / 4), c4 = 4 * (idx % (DV / 4));
-    float4 vv = {0.f, 0.f, 0.f, 0.f};
-    if (r < len) vv = *reinterpret_cast<const float4*>(p.v + ((start + r) * H + h) * DV + c4);
-    const float b = sBeta[r];
-    vv.x *= b; vv.y *= b; vv.z *= b; vv.w *= b;
-    *reinterpret_cast<float4*>(&sQl[r * PK + c4]) = vv;
+  if constexpr (FUSED) {
+    // v rows: conv (no norm) from staged taps, over the A tile (A is no longer needed);
+    // rows past the A tile's capacity fall back to taps from HBM
+    const int64_t ch0 = 2 * (int64_t)H * DK + (int64_t)h * DV;
+    constexpr bool fits = (L + 3) * DV * sizeof(RawT) <= (size_t)L * PL * sizeof(float);
+    if constexpr (fits) {
+      __syncthreads();  // every wavefront is past the solve's last read of A
+      stage_rows(static_cast<const RawT*>(p.raw.v), DV, ch0);
+      __syncthreads();
+    }
+    constexpr int EV = DV / 64;
+    const RawT* rv = static_cast<const RawT*>(p.raw.v);
+    const int64_t wv = (int64_t)H * DV;
+    for (int r = wave; r < L; r += NT / 64) {
+      float x[EV];
+      if constexpr (fits) {
+        conv_row<DV, false>([&](int j, int d) { return to_f32(stage[(r + j) * DV + d]); }, p.raw.conv_w + ch0 * 4,
+                            p.raw.act, x);
+      } else {
+        const int64_t rel = start - t0 + r;
+        conv_row<DV, false>([&](int j, int d) {
+          const int64_t pos = rel - 3 + j;
+          if (r >= len) return 0.f;
+          return pos >= 0 ? to_f32(rv[(t0 + pos) * wv + (int64_t)h * DV + d]) : to_f32(raw_cs[(3 + pos) * Cch + ch0 + d]);
+        }, p.raw.conv_w + ch0 * 4, p.raw.act, x);
+      }
+#pragma unroll
+      for (int e = 0; e < EV; ++e) sQ[r * PK + EV * lane + e] = r < len ? sBeta[r] * x[e] : 0.f;
+    }
+  } else {
+    for (int idx = t; idx < L * (DV / 4); idx += NT) {
+      const int r = idx / (DV / 4), c4 = 4 * (idx % (DV / 4));
+      float4 vv = {0.f, 0.f, 0.f, 0.f};
+      if (r < len) vv = *reinterpret_cast<const float4*>(p.v + ((start + r) * H + h) * DV + c4);
+      const float b = sBeta[r];
+      vv.x *= b; vv.y *= b; vv.z *= b; vv.w *= b;
+      *reinterpret_cast<float4*>(&sQ[r * PK + c4]) = vv;
+    }
   }
   __syncthreads();
 
-  // 8. W = X (b K^gamma), U~ = X (b V); X is lower triangular, so row block R needs K = 16(R+1)
+  // 8. W = X (b K^gamma), U~ = X (b V); X is lower triangular, so row block R needs K = 16(R+1).
+  //    U~ goes to the record in result layout; W through LDS (T0) into fragments.
   constexpr int NTW = 4 * (DK / 16), NTU = 4 * (DV / 16);
-  for (int tile = wave; tile < NTW + NTU; tile += 4) {
+  float* sW = sK;
+  for (int tile = wave; tile < NTW + NTU; tile += NT / 64) {
     const bool isW = tile < NTW;
     const int tt = isW ? tile : tile - NTW;
     const int R = tt % 4, cb = tt / 4;
     const int K = (16 * (R + 1) + 31) / 32 * 32;
-    const float* B = isW ? sKl : sQl;
+    const float* B = isW ? sG : sQ;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    mma16<POL>(acc, K, [&](int i, int kk) { return sX[(16 * R + i) * PL + kk]; },
-               [&](int kk, int j) { return B[kk * PK + 16 * cb + j]; });
-    const int col = lane & 15, g4 = lane >> 4;
-    float* dst = rec + (isW ? rl.W : rl.Ut);
-    const int ld = isW ? DK : DV;
+    mma16<IP>(acc, K, [&](int i, int kk) { return sXi[(16 * R + i) * PL + kk]; },
+              [&](int kk, int j) { return B[kk * PK + 16 * cb + j]; });
+    if (!isW) *reinterpret_cast<floatx4*>(rec + rl.Ut + ((int64_t)(cb * 4 + R) * 64 + lane) * 16) = acc;
+    else {
+      // W tiles overwrite k_hat in T0 only after every wavefront has passed step 7
+      const int col = lane & 15, g4 = lane >> 4;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) dst[(16 * R + 4 * g4 + v) * ld + 16 * cb + col] = acc[v];
+      for (int v = 0; v < 4; ++v) sW[(16 * R + 4 * g4 + v) * PK + 16 * cb + col] = acc[v];
+    }
   }
+  __syncthreads();
+  write_afrags<POL, NT>(rec + rl.Wf, 4, DK / 32, [&](int r, int d) { return sW[r * PK + d]; });
 }
 
 // ---------------------------------------------------------------------------
 // inter-chunk scan
+//
+// Workgroup = (sequence, head, 16 state columns j0..j0+15), 8 wavefronts in
+// two roles.  The four state wavefronts carry the sequential chain; state
+// wavefront w owns chunk rows 16w..16w+15 of U and state rows
+// 16*(w*DK/64 + s) + 0..15 (s < DK/64) as fp32 matrix-core accumulators:
+//   U_c = U~_c - W_c S_c          (B operand: S_c^T slice from LDS)
+//   S_{c+1} = gamma_L . S_c + K_<^T U_c
+// The four output wavefronts trail by one chunk, off the critical path:
+//   O_{c-1} = Q^gamma S_{c-1} + P U_{c-1}
+// S^T and U^T slices double-buffer in LDS; every chunk takes two workgroup
+// barriers.  Each role keeps NS register sets of operand fragments (two to
+// four, as registers allow) and loads chunk c+NS-1 while chunk c computes.
 // ---------------------------------------------------------------------------
-template <int DK, int DV>
+// LDS of the scan: S^T and U^T slices, double-buffered, stored as the B-operand
+// planes of the policy (element (column j, K index k) at plane[j * stride + k]).
+template <int DK, int POL>
 struct ScanSmem {
-  static constexpr int L = 64;
-  static constexpr int PK = DK + 4, PL = L + 4, PS = 16 + 4;
-  static constexpr int TW = 0;               // W        [L][PK]
-  static constexpr int TQ = TW + L * PK;     // Q^gamma  [L][PK]
-  static constexpr int TK = TQ + L * PK;     // K_<      [L][PK]
-  static constexpr int TP = TK + L * PK;     // P        [L][PL]
-  static constexpr int TS = TP + L * PL;     // state slice [DK][PS]
-  static constexpr int TU = TS + DK * PS;    // U slice  [L][PS]
-  static constexpr int TUT = TU + L * PS;    // U~ slice [L][PS]
-  static constexpr int TG = TUT + L * PS;    // gamma_L  [DK]
-  static constexpr int FLOATS = TG + DK;
-  static constexpr size_t BYTES = FLOATS * sizeof(float);
+  using P = typename Frag<POL>::P;
+  static constexpr int NP = Frag<POL>::PLANES;
+  static constexpr int PS = DK + 16 / sizeof(P);  // S^T row stride (16 rows = the slice's columns)
+  static constexpr int PU = 64 + 16 / sizeof(P);  // U^T row stride
+  static constexpr int S_PLANE = 16 * PS, U_PLANE = 16 * PU;
+  static constexpr int S_BUF = NP * S_PLANE, U_BUF = NP * U_PLANE;
+  static constexpr size_t BYTES = (size_t)(2 * S_BUF + 2 * U_BUF) * sizeof(P);
+};
+
+template <int DK, int POL>
+struct StateFrags {
+  using F = Frag<POL>;
+  static constexpr int KB = DK / 32, MS = DK / 64;
+  typename F::A w[KB], k[MS][2];
+  floatx4 ut;
+  float4 gl[MS];
+  __device__ void load(const uint8_t* rec, const RecLayout& rl, int w4, int lane, int split) {
+    constexpr int FB = F::BYTES;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) w[kb] = F::load_a(rec + rl.Wf + ((int64_t)(w4 * KB + kb) * 64 + lane) * FB);
+#pragma unroll
+    for (int s = 0; s < MS; ++s)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        k[s][kb] = F::load_a(rec + rl.Kf + ((int64_t)((w4 * MS + s) * 2 + kb) * 64 + lane) * FB);
+    ut = *reinterpret_cast<const floatx4*>(rec + rl.Ut + ((int64_t)(split * 4 + w4) * 64 + lane) * 16);
+#pragma unroll
+    for (int s = 0; s < MS; ++s)
+      gl[s] = *reinterpret_cast<const float4*>(rec + rl.gL + (int64_t)(16 * (w4 * MS + s) + 4 * (lane >> 4)) * 4);
+  }
+};
+
+template <int DK, int POL>
+struct OutFrags {
+  using F = Frag<POL>;
+  static constexpr int KB = DK / 32;
+  typename F::A q[KB], pp[2];
+  __device__ void load(const uint8_t* rec, const RecLayout& rl, int w4, int lane) {
+    constexpr int FB = F::BYTES;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) q[kb] = F::load_a(rec + rl.Qf + ((int64_t)(w4 * KB + kb) * 64 + lane) * FB);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) pp[kb] = F::load_a(rec + rl.Pf + ((int64_t)(w4 * 2 + kb) * 64 + lane) * FB);
+  }
 };
 
 template <int DK, int DV, int POL>
-__global__ __launch_bounds__(256) void chunk_scan_kernel(PrefillArgs p, int groups) {
-  using SM = ScanSmem<DK, DV>;
-  constexpr int L = SM::L, PK = SM::PK, PL = SM::PL, PS = SM::PS;
-  constexpr int NSPLIT = DV / 16;
-  extern __shared__ __align__(16) float smem[];
-  float* sW = smem + SM::TW;
-  float* sQ = smem + SM::TQ;
-  float* sK = smem + SM::TK;
-  float* sP = smem + SM::TP;
-  float* sS = smem + SM::TS;
-  float* sU = smem + SM::TU;
-  float* sUt = smem + SM::TUT;
-  float* sG = smem + SM::TG;
+__global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillArgs p, int groups) {
+  using SM = ScanSmem<DK, POL>;
+  using F = Frag<POL>;
+  using P = typename F::P;
+  constexpr int L = kChunk, PS = SM::PS, PU = SM::PU;
+  constexpr int NSPLIT = DV / 16, KB = DK / 32, MS = DK / 64;
+  // register sets of operand fragments per role: chunk c+NS-1 loads while chunk c computes
+  constexpr int NS = F::BYTES == 16 ? 4 : (DK == 64 ? 3 : 2);
+  extern __shared__ __align__(16) float smem_f[];
+  P* smem = reinterpret_cast<P*>(smem_f);
 
   // workgroups of one (sequence, head) share its chunk records: keep them on one XCD
   // (workgroups are dealt round-robin over the 8 XCDs by linear id)
-  const int id = blockIdx.x, xcd = id % 8, k = id / 8;
-  const int grp = (k / NSPLIT) * 8 + xcd, split = k % NSPLIT;
+  const int id = blockIdx.x, xcd = id % 8, kq = id / 8;
+  const int grp = (kq / NSPLIT) * 8 + xcd, split = kq % NSPLIT;
   if (grp >= groups) return;
-  const int H = p.H, n = grp / H, h = grp % H;
-  const int slot = p.slots ? p.slots[n] : n;
+  const int H = p.H, n_seq = grp / H, h = grp % H;
+  const int slot = p.slots ? p.slots[n_seq] : n_seq;
   if (slot < 0) return;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int col = lane & 15, g4 = lane >> 4;
+  const bool is_state = wave < 4;
+  const int w4 = wave & 3, col = lane & 15, g4 = lane >> 4;
   const int j0 = 16 * split;
-  const RecLayout rl = rec_layout(DK, DV);
+  const RecLayout rl = rec_layout(DK, DV, F::BYTES);
   float* Sg = p.state + ((int64_t)slot * H + h) * DK * DV;
+  // plane pointers of buffer b; "store" helpers take the rows 4*g4.. of column col
+  auto sS = [&](int b, int plane) { return smem + b * SM::S_BUF + plane * SM::S_PLANE; };
+  auto sU = [&](int b, int plane) { return smem + 2 * SM::S_BUF + b * SM::U_BUF + plane * SM::U_PLANE; };
+  auto put_s = [&](int b, int row0, const floatx4& x) {
+    F::store_b4(sS(b, 0) + col * PS + row0, sS(b, SM::NP - 1) + col * PS + row0, x);
+  };
+  auto put_u = [&](int b, int row0, const floatx4& x) {
+    F::store_b4(sU(b, 0) + col * PU + row0, sU(b, SM::NP - 1) + col * PU + row0, x);
+  };
+  auto get_s = [&](int b, int kb) { return F::load_b(sS(b, 0) + col * PS + 32 * kb, sS(b, SM::NP - 1) + col * PS + 32 * kb, g4); };
+  auto get_u = [&](int b, int kb) { return F::load_b(sU(b, 0) + col * PU + 32 * kb, sU(b, SM::NP - 1) + col * PU + 32 * kb, g4); };
 
-  for (int idx = t; idx < DK * 4; idx += 256) {
-    const int r = idx / 4, c4 = 4 * (idx % 4);
-    *reinterpret_cast<float4*>(&sS[r * PS + c4]) = *reinterpret_cast<const float4*>(Sg + (int64_t)r * DV + j0 + c4);
-  }
-  const int c_begin = p.chunk_off[n], c_end = p.chunk_off[n + 1];
-  for (int c = c_begin; c < c_end; ++c) {
-    const float* rec = p.recs + ((int64_t)c * H + h) * p.rec_floats;
-    const int64_t start = (int64_t)p.cu[n] + (int64_t)(c - c_begin) * L;
-    const int len = (int)min((int64_t)L, (int64_t)p.cu[n + 1] - start);
-    __syncthreads();  // previous chunk done with the tiles
-    for (int idx = t; idx < L * (DK / 4); idx += 256) {
-      const int r = idx / (DK / 4), c4 = 4 * (idx % (DK / 4));
-      *reinterpret_cast<float4*>(&sW[r * PK + c4]) = *reinterpret_cast<const float4*>(rec + rl.W + r * DK + c4);
-      *reinterpret_cast<float4*>(&sQ[r * PK + c4]) = *reinterpret_cast<const float4*>(rec + rl.Qg + r * DK + c4);
-      *reinterpret_cast<float4*>(&sK[r * PK + c4]) = *reinterpret_cast<const float4*>(rec + rl.Kl + r * DK + c4);
-    }
-    for (int idx = t; idx < L * (L / 4); idx += 256) {
-      const int r = idx / (L / 4), c4 = 4 * (idx % (L / 4));
-      *reinterpret_cast<float4*>(&sP[r * PL + c4]) = *reinterpret_cast<const float4*>(rec + rl.P + r * L + c4);
-    }
-    {
-      const int r = t / 4, c4 = 4 * (t % 4);  // 64 rows x 16 columns of U~
-      *reinterpret_cast<float4*>(&sUt[r * PS + c4]) = *reinterpret_cast<const float4*>(rec + rl.Ut + r * DV + j0 + c4);
-    }
-    for (int d = t; d < DK; d += 256) sG[d] = rec[rl.gL + d];
-    __syncthreads();
-
-    // U = U~ - W S  (wave w: rows 16w .. 16w+15)
-    {
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-      mma16<POL>(acc, DK, [&](int i, int kk) { return sW[(16 * wave + i) * PK + kk]; },
-                 [&](int kk, int j) { return sS[kk * PS + j]; });
+  floatx4 Sacc[MS];
+  if (is_state) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int rr = 16 * wave + 4 * g4 + v;
-        sU[rr * PS + col] = sUt[rr * PS + col] - acc[v];
-      }
-    }
-    __syncthreads();
-    // O = Q^gamma S + P U  (P is lower triangular: row block w needs K = 16(w+1))
-    {
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-      mma16<POL>(acc, DK, [&](int i, int kk) { return sQ[(16 * wave + i) * PK + kk]; },
-                 [&](int kk, int j) { return sS[kk * PS + j]; });
-      mma16<POL>(acc, (16 * (wave + 1) + 31) / 32 * 32, [&](int i, int kk) { return sP[(16 * wave + i) * PL + kk]; },
-                 [&](int kk, int j) { return sU[kk * PS + j]; });
+    for (int s = 0; s < MS; ++s) {
+      const int r0 = 16 * (w4 * MS + s) + 4 * g4;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int rr = 16 * wave + 4 * g4 + v;
-        if (rr < len) p.o[((start + rr) * H + h) * DV + j0 + col] = acc[v];
-      }
-    }
-    // S_L = Diag(gamma_L) S + K_<^T U  (wave w: state rows 16*(2w+s) .. +15)
-    floatx4 accS[DK / 64];
-#pragma unroll
-    for (int s = 0; s < DK / 64; ++s) {
-      const int rb = 16 * (wave * (DK / 64) + s);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int rr = rb + 4 * g4 + v;
-        accS[s][v] = sG[rr] * sS[rr * PS + col];
-      }
-      mma16<POL>(accS[s], L, [&](int i, int kk) { return sK[kk * PK + rb + i]; },
-                 [&](int kk, int j) { return sU[kk * PS + j]; });
-    }
-    __syncthreads();  // every read of the old state is done
-#pragma unroll
-    for (int s = 0; s < DK / 64; ++s) {
-      const int rb = 16 * (wave * (DK / 64) + s);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) sS[(rb + 4 * g4 + v) * PS + col] = accS[s][v];
+      for (int v = 0; v < 4; ++v) Sacc[s][v] = Sg[(int64_t)(r0 + v) * DV + j0 + col];
+      put_s(0, r0, Sacc[s]);
     }
   }
-  __syncthreads();
-  for (int idx = t; idx < DK * 4; idx += 256) {
-    const int r = idx / 4, c4 = 4 * (idx % 4);
-    *reinterpret_cast<float4*>(Sg + (int64_t)r * DV + j0 + c4) = *reinterpret_cast<const float4*>(&sS[r * PS + c4]);
+
+  const int c_begin = p.chunk_off[n_seq], n = p.chunk_off[n_seq + 1] - c_begin;
+  const int64_t seq_start = p.cu[n_seq], seq_end = p.cu[n_seq + 1];
+  auto rec_of = [&](int i) { return p.recs + ((int64_t)(c_begin + i) * H + h) * p.rec_bytes; };
+
+  // Iteration i (0..n): the state role takes chunk i (register set i % 3), the
+  // output role chunk i-1.  Both roles run n+1 iterations of two barriers each.
+  if (is_state) {
+    StateFrags<DK, POL> sf[NS];
+    // Every load below is unconditional (indices clamped to the last chunk), so
+    // the compiler can count outstanding loads exactly and wait only for the
+    // set a chunk needs.
+    auto clampc = [&](int j) { return j < n ? j : n - 1; };
+    if (n > 0) {
+#pragma unroll
+      for (int j = 0; j < NS - 1; ++j) sf[j].load(rec_of(clampc(j)), rl, w4, lane, split);
+    }
+    auto iter = [&](int i, const StateFrags<DK, POL>& cur, StateFrags<DK, POL>& ahead) {
+      const int bi = i & 1, bp = (i + 1) & 1;
+      __syncthreads();  // S^T_i complete; every read of the buffers rewritten below is done
+      ahead.load(rec_of(clampc(i + NS - 1)), rl, w4, lane, split);
+      if (i < n) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) acc = F::mma(acc, cur.w[kb], get_s(bi, kb));
+        floatx4 u;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) u[v] = cur.ut[v] - acc[v];
+        put_u(bi, 16 * w4 + 4 * g4, u);
+      }
+      __syncthreads();  // U^T_i complete
+      if (i < n) {
+        const typename F::B u0 = get_u(bi, 0), u1 = get_u(bi, 1);
+#pragma unroll
+        for (int s = 0; s < MS; ++s) {
+          const float4 gl = cur.gl[s];
+          Sacc[s][0] *= gl.x; Sacc[s][1] *= gl.y; Sacc[s][2] *= gl.z; Sacc[s][3] *= gl.w;
+          Sacc[s] = F::mma(Sacc[s], cur.k[s][0], u0);
+          Sacc[s] = F::mma(Sacc[s], cur.k[s][1], u1);
+          put_s(bp, 16 * (w4 * MS + s) + 4 * g4, Sacc[s]);
+        }
+      }
+    };
+    // n+1 iterations rounded up to a multiple of NS (the output role trails by one chunk)
+    const int iters = n > 0 ? (n + NS) / NS * NS : 0;
+    for (int base = 0; base < iters; base += NS) {
+#pragma unroll
+      for (int u = 0; u < NS; ++u) iter(base + u, sf[u], sf[(u + NS - 1) % NS]);
+    }
+#pragma unroll
+    for (int s = 0; s < MS; ++s) {
+      const int r0 = 16 * (w4 * MS + s) + 4 * g4;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) Sg[(int64_t)(r0 + v) * DV + j0 + col] = Sacc[s][v];
+    }
+  } else {
+    OutFrags<DK, POL> of[NS];
+    auto clampc = [&](int j) { return j < n ? j : n - 1; };
+    if (n > 0) {
+#pragma unroll
+      for (int j = 0; j < NS - 2; ++j) of[j].load(rec_of(clampc(j)), rl, w4, lane);
+    }
+    auto iter = [&](int i, const OutFrags<DK, POL>& prev, OutFrags<DK, POL>& next) {
+      const int bp = (i + 1) & 1;  // LDS buffers of chunk i-1
+      floatx4 ao = {0.f, 0.f, 0.f, 0.f};
+      __syncthreads();
+      next.load(rec_of(clampc(i + NS - 2)), rl, w4, lane);
+      const bool live = i >= 1 && i <= n;
+      if (live) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) ao = F::mma(ao, prev.q[kb], get_s(bp, kb));
+      }
+      __syncthreads();
+      if (live) {
+        // P is lower triangular: row block w4 needs chunk rows < 16(w4+1)
+        ao = F::mma(ao, prev.pp[0], get_u(bp, 0));
+        if (w4 >= 2) ao = F::mma(ao, prev.pp[1], get_u(bp, 1));
+      }
+      // stores are unconditional: rows past the sequence (or iterations without a chunk) go to the sink
+      const int64_t start = seq_start + (int64_t)(i - 1) * L;
+      const int len = live ? (int)min((int64_t)L, seq_end - start) : 0;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int rr = 16 * w4 + 4 * g4 + v;
+        float* dst = rr < len ? &p.o[((start + rr) * H + h) * DV + j0 + col] : &p.sink[lane * 4 + v];
+        *dst = ao[v];
+      }
+    };
+    const int iters = n > 0 ? (n + NS) / NS * NS : 0;
+    for (int base = 0; base < iters; base += NS) {
+#pragma unroll
+      for (int u = 0; u < NS; ++u) iter(base + u, of[(u + NS - 1) % NS], of[(u + NS - 2) % NS]);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // host launch
 // ---------------------------------------------------------------------------
-template <int DK, int DV, int POL>
+template <typename RawT>
+__global__ __launch_bounds__(256) void prefill_conv_state_kernel(PrefillArgs p, int DK, int DV) {
+  // carried conv state after a fused prompt pass: the last 3 raw rows of each sequence
+  // (reaching back into the old conv state for short ones); same order rule as the preamble's
+  const int n = blockIdx.y;
+  const int64_t C = (int64_t)p.H * (2 * DK + DV);
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= C) return;
+  const int slot = p.slots ? p.slots[n] : n;
+  if (slot < 0) return;
+  const int64_t t0 = p.cu[n], len = (int64_t)p.cu[n + 1] - t0;
+  const int64_t qk = (int64_t)p.H * DK;
+  const RawT* in = static_cast<const RawT*>(p.raw.cs_in) + (int64_t)slot * 3 * C;
+  RawT* out = static_cast<RawT*>(p.raw.cs_out) + (int64_t)slot * 3 * C;
+  for (int r = 0; r < 3; ++r) {
+    const int64_t pos = len - 3 + r;
+    RawT x;
+    if (pos >= 0) {
+      const int64_t row = t0 + pos;
+      if (c < qk) x = static_cast<const RawT*>(p.raw.q)[row * qk + c];
+      else if (c < 2 * qk) x = static_cast<const RawT*>(p.raw.k)[row * qk + (c - qk)];
+      else x = static_cast<const RawT*>(p.raw.v)[row * (int64_t)p.H * DV + (c - 2 * qk)];
+    } else {
+      x = in[(3 + pos) * C + c];
+    }
+    out[r * C + c] = x;
+  }
+}
+
+template <int DK, int DV, int POL, typename RawT, bool FUSED>
 static hipError_t launch_prefill_t(const PrefillLaunch& Lc, hipStream_t s) {
   PrefillArgs p;
   p.H = Lc.H; p.num_seqs = Lc.num_seqs; p.cu = Lc.cu_seqlens; p.slots = Lc.slots;
   p.q = Lc.q_hat; p.k = Lc.k_hat; p.v = Lc.v; p.g = Lc.g; p.beta = Lc.beta; p.state = Lc.state; p.o = Lc.o;
+  p.raw = {Lc.raw_q, Lc.raw_k, Lc.raw_v, Lc.raw_g, Lc.raw_beta, Lc.conv_w, Lc.cs_in, Lc.cs_out,
+           Lc.act, Lc.gate_mode, Lc.lb};
   p.chunk_off = static_cast<int32_t*>(Lc.workspace);
-  p.recs = reinterpret_cast<float*>(static_cast<char*>(Lc.workspace) + table_bytes(Lc.num_seqs));
-  p.rec_floats = rec_layout(DK, DV).floats;
+  p.sink = reinterpret_cast<float*>(static_cast<uint8_t*>(Lc.workspace) + table_bytes(Lc.num_seqs) - 1024);
+  p.recs = static_cast<uint8_t*>(Lc.workspace) + table_bytes(Lc.num_seqs);
+  p.rec_bytes = rec_layout(DK, DV, Frag<POL>::BYTES).bytes;
   hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(256), 0, s, Lc.cu_seqlens, Lc.num_seqs, p.chunk_off);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t mc = max_chunks(Lc.num_seqs, Lc.t_tot);
+  constexpr size_t intra_bytes = IntraSmem<DK, DV>::BYTES;
+  constexpr size_t scan_bytes = ScanSmem<DK, POL>::BYTES;
+  static bool attr_set = false;
+  if (!attr_set) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_intra_kernel<DK, DV, POL, RawT, FUSED>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)intra_bytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
   if (mc > 0 && Lc.t_tot > 0) {
-    constexpr size_t intra_bytes = IntraSmem<DK, DV>::BYTES;
-    static bool attr_set = false;
-    if (!attr_set) {
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_intra_kernel<DK, DV, POL>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)intra_bytes);
-      if (e != hipSuccess) return e;
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_scan_kernel<DK, DV, POL>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)ScanSmem<DK, DV>::BYTES);
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
-    hipLaunchKernelGGL((chunk_intra_kernel<DK, DV, POL>), dim3((unsigned)mc, (unsigned)Lc.H), dim3(256), intra_bytes,
-                       s, p);
+    hipLaunchKernelGGL((chunk_intra_kernel<DK, DV, POL, RawT, FUSED>), dim3((unsigned)mc, (unsigned)Lc.H), dim3(512),
+                       intra_bytes, s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if constexpr (FUSED) {  // conv state written after every read of the old one (the two may alias)
+    const int64_t C = (int64_t)Lc.H * (2 * DK + DV);
+    hipLaunchKernelGGL((prefill_conv_state_kernel<RawT>), dim3((unsigned)((C + 255) / 256), (unsigned)Lc.num_seqs),
+                       dim3(256), 0, s, p, DK, DV);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -618,17 +1014,25 @@ static hipError_t launch_prefill_t(const PrefillLaunch& Lc, hipStream_t s) {
   if (groups > 0) {
     const int nsplit = DV / 16;
     const int wgs = (groups + 7) / 8 * 8 * nsplit;
-    constexpr size_t scan_bytes = ScanSmem<DK, DV>::BYTES;
-    hipLaunchKernelGGL((chunk_scan_kernel<DK, DV, POL>), dim3((unsigned)wgs), dim3(256), scan_bytes, s, p, groups);
+    hipLaunchKernelGGL((chunk_scan_kernel<DK, DV, POL>), dim3((unsigned)wgs), dim3(512), scan_bytes, s, p, groups);
   }
   return hipGetLastError();
 }
 
+template <int DK, int DV, int POL>
+static hipError_t launch_prefill_pol(const PrefillLaunch& L, hipStream_t s) {
+  if (!L.fused) return launch_prefill_t<DK, DV, POL, float, false>(L, s);
+  if (L.in_dtype == 1) return launch_prefill_t<DK, DV, POL, uint16_t, true>(L, s);
+  return launch_prefill_t<DK, DV, POL, float, true>(L, s);
+}
+
 hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t s) {
-#define KDA_PF_CASE(DK_, DV_)                                                                        \
-  if (L.dk == DK_ && L.dv == DV_)                                                                    \
-    return L.precision == POL_FP32 ? launch_prefill_t<DK_, DV_, POL_FP32>(L, s)                      \
-                                   : launch_prefill_t<DK_, DV_, POL_BF16X3>(L, s);
+#define KDA_PF_CASE(DK_, DV_)                                                       \
+  if (L.dk == DK_ && L.dv == DV_) {                                                 \
+    if (L.precision == POL_FP32) return launch_prefill_pol<DK_, DV_, POL_FP32>(L, s); \
+    if (L.precision == POL_FP16) return launch_prefill_pol<DK_, DV_, POL_FP16>(L, s); \
+    return launch_prefill_pol<DK_, DV_, POL_BF16X3>(L, s);                          \
+  }
   KDA_PF_CASE(64, 64)
   KDA_PF_CASE(64, 128)
   KDA_PF_CASE(128, 64)

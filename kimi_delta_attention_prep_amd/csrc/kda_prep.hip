@@ -56,57 +56,29 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<RawT> p) {
   const int64_t rel = row - t0;
   const int64_t C = (int64_t)H * (2 * DK + DV);
   const RawT* cs = p.cs_in + (int64_t)slot * 3 * C;
-
-  // value of channel `ch` (a column of the packed source `src` with `width` channels per row)
-  // at sequence-relative position `pos` in [-3, rel]
-  auto src_val = [&](const RawT* src, int64_t width, int64_t col, int64_t ch, int64_t pos) -> float {
-    if (pos >= 0) return to_f32(src[(t0 + pos) * width + col]);
-    return to_f32(cs[(3 + pos) * C + ch]);
+  const int64_t wk = (int64_t)H * DK, wv = (int64_t)H * DV;
+  // tap j of a channel: packed row t0+rel-3+j, or the carried conv state before the sequence start
+  auto tap_of = [&](const RawT* src, int64_t width, int64_t col0, int64_t ch0) {
+    return [=](int j, int d) {
+      const int64_t pos = rel - 3 + j;
+      return pos >= 0 ? to_f32(src[(t0 + pos) * width + col0 + d]) : to_f32(cs[(3 + pos) * C + ch0 + d]);
+    };
   };
-
-  float cq[EK], ck[EK], cv[EV];
-  float sq = 0.f, sk = 0.f;
-#pragma unroll
-  for (int e = 0; e < EK; ++e) {
-    const int d = EK * lane + e;
-    const int64_t colq = (int64_t)h * DK + d;
-    const int64_t chq = colq, chk = (int64_t)H * DK + colq;
-    float xq[4], xk[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      xq[j] = src_val(p.q, (int64_t)H * DK, colq, chq, rel - 3 + j);
-      xk[j] = src_val(p.k, (int64_t)H * DK, colq, chk, rel - 3 + j);
-    }
-    const float* wq = p.conv_w + chq * 4;
-    const float* wk = p.conv_w + chk * 4;
-    cq[e] = conv4_act(wq[0], wq[1], wq[2], wq[3], xq[0], xq[1], xq[2], xq[3], p.act);
-    ck[e] = conv4_act(wk[0], wk[1], wk[2], wk[3], xk[0], xk[1], xk[2], xk[3], p.act);
-    sq = fmaf(cq[e], cq[e], sq);
-    sk = fmaf(ck[e], ck[e], sk);
-  }
-#pragma unroll
-  for (int e = 0; e < EV; ++e) {
-    const int d = EV * lane + e;
-    const int64_t colv = (int64_t)h * DV + d;
-    const int64_t chv = 2 * (int64_t)H * DK + colv;
-    float xv[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) xv[j] = src_val(p.v, (int64_t)H * DV, colv, chv, rel - 3 + j);
-    const float* wv = p.conv_w + chv * 4;
-    cv[e] = conv4_act(wv[0], wv[1], wv[2], wv[3], xv[0], xv[1], xv[2], xv[3], p.act);
-  }
-  sq = wave_sum(sq);
-  sk = wave_sum(sk);
-  const float rq = 1.0f / sqrtf(sq + kL2Eps), rk = 1.0f / sqrtf(sk + kL2Eps);
+  float q[EK], k[EK], v[EV];
+  conv_row<DK, true>(tap_of(p.q, wk, (int64_t)h * DK, (int64_t)h * DK), p.conv_w + (int64_t)h * DK * 4, p.act, q);
+  conv_row<DK, true>(tap_of(p.k, wk, (int64_t)h * DK, wk + (int64_t)h * DK), p.conv_w + (wk + (int64_t)h * DK) * 4,
+                     p.act, k);
+  conv_row<DV, false>(tap_of(p.v, wv, (int64_t)h * DV, 2 * wk + (int64_t)h * DV),
+                      p.conv_w + (2 * wk + (int64_t)h * DV) * 4, p.act, v);
   const int64_t ok = pair * DK + EK * lane, ov = pair * DV + EV * lane;
 #pragma unroll
   for (int e = 0; e < EK; ++e) {
-    p.q_hat[ok + e] = cq[e] * rq;
-    p.k_hat[ok + e] = ck[e] * rk;
+    p.q_hat[ok + e] = q[e];
+    p.k_hat[ok + e] = k[e];
     p.g_out[ok + e] = log_decay(to_f32(p.g[ok + e]), p.gate_mode, p.lb);
   }
 #pragma unroll
-  for (int e = 0; e < EV; ++e) p.v_out[ov + e] = cv[e];
+  for (int e = 0; e < EV; ++e) p.v_out[ov + e] = v[e];
   if (lane == 0) p.beta_out[pair] = sigmoid(to_f32(p.beta[pair]));
 }
 

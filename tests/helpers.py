@@ -50,15 +50,30 @@ def gpu_prep(w: Workload, d: K.Dims, dev="cuda"):
     return wd, out
 
 
-def gpu_layer_prefill(w: Workload, precision=None, y_dtype=torch.float32, dev="cuda"):
-    """prep -> chunked prefill -> gated RMSNorm, all through the C ABI."""
+def raw_rows(wd: Workload, conv_state_out):
+    return dict(q_raw=wd.q, k_raw=wd.k, v_raw=wd.v, g_raw=wd.g, beta_logit=wd.beta, conv_weight=wd.conv_w,
+                conv_state_in=wd.conv_state0, conv_state_out=conv_state_out, gate_mode=wd.gate_mode,
+                lower_bound=wd.lower_bound)
+
+
+def gpu_layer_prefill(w: Workload, precision=None, y_dtype=torch.float32, dev="cuda", fused=False):
+    """prep -> chunked prefill -> gated RMSNorm, all through the C ABI (fused: the preamble runs inside
+    kda_prefill_varlen from the raw rows)."""
     d = dims_for(w, precision)
-    wd, p = gpu_prep(w, d, dev)
     T, H, dv = w.T, w.H, w.dv
+    if fused:
+        wd = w.to(dev)
+        p = {"conv_state": torch.empty_like(wd.conv_state0)}
+    else:
+        wd, p = gpu_prep(w, d, dev)
     state = wd.state0.clone()
     o = torch.empty(T, H, dv, device=dev, dtype=torch.float32)
     ws = torch.empty(max(K.kda_prefill_workspace_bytes(d, w.N, T), 1), dtype=torch.uint8, device=dev)
-    K.kda_prefill_varlen(d, wd.cu_seqlens, p["q_hat"], p["k_hat"], p["v"], p["g"], p["beta"], state, o, ws)
+    if fused:
+        K.kda_prefill_varlen(d, wd.cu_seqlens, None, None, None, None, None, state, o, ws,
+                             raw=raw_rows(wd, p["conv_state"]))
+    else:
+        K.kda_prefill_varlen(d, wd.cu_seqlens, p["q_hat"], p["k_hat"], p["v"], p["g"], p["beta"], state, o, ws)
     y = torch.empty(T, H, dv, device=dev, dtype=y_dtype)
     K.gated_rmsnorm_out(o, wd.z, wd.norm_w, EPS, y)
     torch.cuda.synchronize()

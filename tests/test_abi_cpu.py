@@ -110,7 +110,8 @@ def test_prep_and_prefill_checks(lib):
     assert prep(2, 10, MIS) == K.KDA_E_ALIGN
     need = lib.kda_prefill_workspace_bytes(ctypes.byref(d), 2, 1000)
     assert need > 0
-    pf = lambda ws, nb: lib.kda_prefill_varlen(ctypes.byref(d), 2, 1000, A, None, A, A, A, A, A, A, A, ws, nb, None)
+    pf = lambda ws, nb: lib.kda_prefill_varlen(ctypes.byref(d), 2, 1000, A, None, A, A, A, A, A, None, A, A, ws, nb,
+                                               None)
     assert pf(A, need - 1) == K.KDA_E_WORKSPACE
     assert pf(None, need) == K.KDA_E_WORKSPACE
     assert pf(ctypes.c_void_p(0x10010), need) == K.KDA_E_ALIGN

@@ -190,12 +190,13 @@ def test_prefill_tiny_fp32_config():
     assert rel(r["state"], ref.state) < TOL_FP32
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("dtype,precision", [(torch.bfloat16, None), (torch.bfloat16, K.PREC_FP16),
+                                             (torch.float32, None)])
 @pytest.mark.parametrize("gate", [I.GATE_SAFE, I.GATE_SOFTPLUS])
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64), (64, 128)])
-def test_prefill_varlen_parity(dtype, gate, dk, dv):
+def test_prefill_varlen_parity(dtype, precision, gate, dk, dv):
     w = small(dtype, lens=(200, 1, 0, 64, 127, 65), H=2, d=dk, dv=dv, gate=gate, seed=dk + dv)
-    r = gpu_layer_prefill(w)
+    r = gpu_layer_prefill(w, precision=precision)
     ref = oracle_layer(w)
     tol = tol_for(w)
     assert rel(r["o"], ref.o) < tol
@@ -203,13 +204,52 @@ def test_prefill_varlen_parity(dtype, gate, dk, dv):
     assert rel(r["state"], ref.state) < tol
 
 
-@pytest.mark.parametrize("precision", [K.PREC_FP32, K.PREC_BF16X3])
+@pytest.mark.parametrize("precision", [K.PREC_FP32, K.PREC_BF16X3, K.PREC_FP16])
 def test_prefill_precision_policies_on_bf16_rows(precision):
     w = small(torch.bfloat16, lens=(300, 77), H=2, d=128, gate=I.GATE_SAFE, seed=21)
     r = gpu_layer_prefill(w, precision=precision)
     ref = oracle_layer(w)
     assert rel(r["y"], ref.y) < TOL_BF16
     assert rel(r["state"], ref.state) < TOL_BF16
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("precision", [None, K.PREC_FP16])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128), (128, 64)])
+def test_fused_preamble_is_bitwise_the_unfused_path(dtype, precision, dk, dv):
+    """kda_prefill_varlen with raw rows == kda_prep then kda_prefill_varlen, bit for bit (o, state, conv state)."""
+    w = small(dtype, lens=(150, 3, 0, 64, 70), H=2, d=dk, dv=dv, gate=I.GATE_SOFTPLUS, seed=71)
+    a = gpu_layer_prefill(w, precision=precision)
+    b = gpu_layer_prefill(w, precision=precision, fused=True)
+    assert torch.equal(a["o"], b["o"])
+    assert torch.equal(a["state"], b["state"])
+    assert torch.equal(a["prep"]["conv_state"], b["prep"]["conv_state"])
+
+
+def test_fused_preamble_with_slots_and_in_place_conv_state():
+    w = small(torch.bfloat16, lens=(90, 2, 70), H=2, d=128, seed=81)
+    d = dims_for(w, K.PREC_FP16)
+    wd = w.to("cuda")
+    slots = torch.tensor([2, -1, 0], dtype=torch.int32, device="cuda")
+    pool = torch.zeros(3, w.H, w.dk, w.dv, device="cuda")
+    pool[2], pool[0] = wd.state0[0], wd.state0[2]
+    cpool = torch.zeros(3, 3, w.C, device="cuda", dtype=w.dtype)
+    cpool[2], cpool[0] = wd.conv_state0[0], wd.conv_state0[2]
+    cpool_before = cpool.clone()
+    o = torch.full((w.T, w.H, w.dv), 5.0, device="cuda")
+    ws = torch.empty(K.kda_prefill_workspace_bytes(d, w.N, w.T), dtype=torch.uint8, device="cuda")
+    raw = dict(q_raw=wd.q, k_raw=wd.k, v_raw=wd.v, g_raw=wd.g, beta_logit=wd.beta, conv_weight=wd.conv_w,
+               conv_state_in=cpool, conv_state_out=cpool, gate_mode=w.gate_mode, lower_bound=w.lower_bound)
+    K.kda_prefill_varlen(d, wd.cu_seqlens, None, None, None, None, None, pool, o, ws, slots=slots, raw=raw)
+    torch.cuda.synchronize()
+    ref = oracle_layer(w)
+    cu = w.cu_seqlens.tolist()
+    assert rel(pool[2], ref.state[0]) < TOL_BF16 and rel(pool[0], ref.state[2]) < TOL_BF16
+    assert torch.all(o[cu[1]:cu[2]] == 5.0)
+    assert torch.equal(cpool[1], cpool_before[1])
+    assert np.array_equal(cpool[2].cpu().double().numpy(), ref.prep.conv_state[0])
+    assert np.array_equal(cpool[0].cpu().double().numpy(), ref.prep.conv_state[2])
+    assert rel(o[:cu[1]], ref.o[:cu[1]]) < TOL_BF16
 
 
 def test_prefill_steep_decay_takes_exact_path():
@@ -223,32 +263,33 @@ def test_prefill_steep_decay_takes_exact_path():
     assert rel(r["state"], ref.state) < 1e-4
 
 
-def test_prefill_packed_equals_alone_bitwise():
+@pytest.mark.parametrize("precision", [K.PREC_BF16X3, K.PREC_FP16])
+def test_prefill_packed_equals_alone_bitwise(precision):
     w = small(torch.bfloat16, lens=(100, 64, 3, 129), H=2, d=128, seed=41)
-    full = gpu_layer_prefill(w)
+    full = gpu_layer_prefill(w, precision=precision)
     cu = w.cu_seqlens.tolist()
     for n in range(w.N):
         sl = slice(cu[n], cu[n + 1])
         one = I.Workload("one", w.H, w.dk, w.dv, torch.tensor([0, cu[n + 1] - cu[n]], dtype=torch.int32),
                          w.q[sl], w.k[sl], w.v[sl], w.g[sl], w.beta[sl], w.z[sl], w.conv_w, w.norm_w,
                          w.state0[n:n + 1], w.conv_state0[n:n + 1], w.gate_mode, w.lower_bound)
-        alone = gpu_layer_prefill(one)
+        alone = gpu_layer_prefill(one, precision=precision)
         assert torch.equal(alone["o"], full["o"][sl])
         assert torch.equal(alone["state"][0], full["state"][n])
 
 
-@pytest.mark.parametrize("cut", [64, 128])
-def test_prefill_cut_at_chunk_multiple_is_bitwise(cut):
+@pytest.mark.parametrize("cut,precision", [(64, K.PREC_BF16X3), (128, K.PREC_BF16X3), (128, K.PREC_FP16)])
+def test_prefill_cut_at_chunk_multiple_is_bitwise(cut, precision):
     w = small(torch.bfloat16, lens=(300,), H=2, d=128, seed=51)
-    full = gpu_layer_prefill(w)
+    full = gpu_layer_prefill(w, precision=precision)
     a = I.Workload("a", w.H, w.dk, w.dv, torch.tensor([0, cut], dtype=torch.int32), w.q[:cut], w.k[:cut], w.v[:cut],
                    w.g[:cut], w.beta[:cut], w.z[:cut], w.conv_w, w.norm_w, w.state0, w.conv_state0, w.gate_mode,
                    w.lower_bound)
-    ra = gpu_layer_prefill(a)
+    ra = gpu_layer_prefill(a, precision=precision)
     b = I.Workload("b", w.H, w.dk, w.dv, torch.tensor([0, 300 - cut], dtype=torch.int32), w.q[cut:], w.k[cut:],
                    w.v[cut:], w.g[cut:], w.beta[cut:], w.z[cut:], w.conv_w, w.norm_w, ra["state"].cpu(),
                    ra["prep"]["conv_state"].cpu(), w.gate_mode, w.lower_bound)
-    rb = gpu_layer_prefill(b)
+    rb = gpu_layer_prefill(b, precision=precision)
     assert torch.equal(torch.cat([ra["o"], rb["o"]]), full["o"])
     assert torch.equal(rb["state"], full["state"])
 
