@@ -140,8 +140,8 @@ int kda_prefill_varlen(const kda_dims* d, int32_t num_seqs, int64_t t_tot, const
   }
   if (t_tot > 0) {
     if (raw) {
-      KDA_TRY(check_ptrs("kda_prefill_varlen: raw q/k/v rows", {raw->q_raw, raw->k_raw, raw->v_raw}));
-      KDA_TRY(check_ptrs("kda_prefill_varlen: raw g/beta rows", {raw->g_raw, raw->beta_logit}, eb));
+      KDA_TRY(check_ptrs("kda_prefill_varlen: raw q/k/v/g rows", {raw->q_raw, raw->k_raw, raw->v_raw, raw->g_raw}));
+      KDA_TRY(check_ptrs("kda_prefill_varlen: raw beta logits", {raw->beta_logit}, eb));
     } else {
       KDA_TRY(check_ptrs("kda_prefill_varlen", {q_hat, k_hat, v, g}));
       KDA_TRY(check_ptrs("kda_prefill_varlen", {beta}, 4));

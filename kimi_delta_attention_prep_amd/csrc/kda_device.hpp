@@ -51,30 +51,47 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// One (row, head, stream) of the prompt preamble, computed by a whole
-// wavefront: lane l owns channels E*l .. E*l+E-1 (E = D/64).  tap(j, d) returns
-// conv input tap j (0 = oldest, 3 = current row) of channel d of this head; w
-// points at the head's first conv weight row of the stream.  Returns the conv
-// output after the activation, L2-normalised over the D channels when NORM.
-// The standalone preamble kernel (taps from HBM) and the fused prompt kernel
-// (taps from LDS) both call this, so they produce the same bits.
-template <int D, bool NORM, class TAP>
-__device__ __forceinline__ void conv_row(TAP tap, const float* __restrict__ w, int act, float (&out)[D / 64]) {
+// NR rows (of one head and stream) of the prompt preamble, computed by a whole
+// wavefront: lane l owns channels E*l .. E*l+E-1 (E = D/64) of every row.
+// tap(rr, j, d) returns conv input tap j (0 = oldest, 3 = current row) of
+// channel d for row rr; w points at the head's first conv weight row of the
+// stream.  out[rr] gets the conv output after the activation, L2-normalised
+// over the D channels when NORM.  The rows are independent and computed side
+// by side; each row's arithmetic does not depend on NR, so the standalone
+// preamble kernel (one row, taps from HBM) and the fused prompt kernel (eight
+// rows, taps from LDS) produce the same bits.
+template <int D, bool NORM, int NR, class TAP>
+__device__ __forceinline__ void conv_rows(TAP tap, const float* __restrict__ w, int act, float (&out)[NR][D / 64]) {
   constexpr int E = D / 64;
   const int lane = threadIdx.x & 63;
-  float ss = 0.f;
+  float wt[E][4];
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int d = E * lane + e;
-    const float* wd = w + (int64_t)d * 4;
-    out[e] = conv4_act(wd[0], wd[1], wd[2], wd[3], tap(0, d), tap(1, d), tap(2, d), tap(3, d), act);
-    ss = fmaf(out[e], out[e], ss);
+  for (int e = 0; e < E; ++e)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wt[e][j] = w[(int64_t)(E * lane + e) * 4 + j];
+  float ss[NR];
+#pragma unroll
+  for (int rr = 0; rr < NR; ++rr) {
+    ss[rr] = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int d = E * lane + e;
+      out[rr][e] = conv4_act(wt[e][0], wt[e][1], wt[e][2], wt[e][3], tap(rr, 0, d), tap(rr, 1, d), tap(rr, 2, d),
+                             tap(rr, 3, d), act);
+      ss[rr] = fmaf(out[rr][e], out[rr][e], ss[rr]);
+    }
   }
-  if constexpr (NORM) {
-    ss = wave_sum(ss);
-    const float r = 1.0f / sqrtf(ss + kL2Eps);
+  if constexpr (NORM) {  // wave_sum of every row, side by side
 #pragma unroll
-    for (int e = 0; e < E; ++e) out[e] *= r;
+    for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+      for (int rr = 0; rr < NR; ++rr) ss[rr] += __shfl_xor(ss[rr], off, 64);
+#pragma unroll
+    for (int rr = 0; rr < NR; ++rr) {
+      const float r = 1.0f / sqrtf(ss[rr] + kL2Eps);
+#pragma unroll
+      for (int e = 0; e < E; ++e) out[rr][e] *= r;
+    }
   }
 }
 

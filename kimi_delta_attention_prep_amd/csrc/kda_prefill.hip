@@ -403,6 +403,17 @@ struct IntraSmem {
   static constexpr size_t BYTES = FLOATS * sizeof(float);
 };
 
+// element e of a 16-byte piece of raw rows (bf16 bit patterns or fp32)
+template <typename RawT>
+__device__ __forceinline__ float piece_elem(const uint4& x, int e) {
+  if constexpr (sizeof(RawT) == 2) {
+    const uint32_t w = e < 2 ? x.x : e < 4 ? x.y : e < 6 ? x.z : x.w;
+    return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+  } else {
+    return __uint_as_float(e == 0 ? x.x : e == 1 ? x.y : e == 2 ? x.z : x.w);
+  }
+}
+
 __device__ __forceinline__ int pair_index(int R, int I) { return R * (R - 1) / 2 + I; }  // I < R
 
 template <int DK, int DV, int POL, typename RawT, bool FUSED>
@@ -440,57 +451,92 @@ __global__ __launch_bounds__(512) void chunk_intra_kernel(PrefillArgs p) {
   const RawT* raw_cs = FUSED ? static_cast<const RawT*>(p.raw.cs_in) + (int64_t)slot * 3 * Cch : nullptr;
 
   // 1. rows: k_hat, q_hat, g (zero past the chunk's last row) and beta
-  // Fused: each raw stream's 67 rows (3 halo rows, then the chunk) are staged
-  // in LDS with 16-byte loads -- halo rows come from the sequence's previous
-  // rows, or from its carried conv state at the sequence start -- and the
-  // per-row preamble then reads its conv taps from there.
-  RawT* stage = reinterpret_cast<RawT*>(sA);  // [67][D] raw rows, over the A / P tiles
-  auto stage_rows = [&](const RawT* src, int D, int64_t ch0) {
-    constexpr int VE = 16 / sizeof(RawT);  // elements per 16-byte load
+  // Fused: every raw row the chunk needs is loaded up front, 16 bytes per load.
+  // The q and k streams are staged in LDS as 67 rows each (3 halo rows, then
+  // the chunk's rows; halo rows come from the sequence's previous rows, or
+  // from its carried conv state at the sequence start) and each wavefront
+  // then runs the preamble of 8 rows side by side, reading its taps there.
+  constexpr int VE = 16 / sizeof(RawT);  // raw elements per 16-byte piece
+  // piece idx of a staged stream (row sr = idx / (D / VE) of the 67): zero past the chunk's last row
+  auto load_staged = [&](const RawT* src, int D, int64_t ch0, int idx) {
     const int per_row = D / VE;
-    const int64_t width = (int64_t)H * D;
-    for (int idx = t; idx < (L + 3) * per_row; idx += NT) {
-      const int sr = idx / per_row, c0 = (idx % per_row) * VE;
-      const int64_t pos = start - 3 + sr;  // packed row of this staged row
-      uint4 x = {0u, 0u, 0u, 0u};
-      if (sr < len + 3) {
-        if (pos >= t0) x = *reinterpret_cast<const uint4*>(src + pos * width + (int64_t)h * D + c0);
-        else {
-          // carried conv state row 3 + (pos - t0); its channels are not 16-byte aligned in general
-          const RawT* cr = raw_cs + (3 + (pos - t0)) * Cch + ch0 + c0;
-          RawT tmp[VE];
+    const int sr = idx / per_row, c0 = (idx % per_row) * VE;
+    const int64_t pos = start - 3 + sr;  // packed row of this staged row
+    uint4 x = {0u, 0u, 0u, 0u};
+    if (idx < (L + 3) * per_row && sr < len + 3) {
+      if (pos >= t0) x = *reinterpret_cast<const uint4*>(src + pos * ((int64_t)H * D) + (int64_t)h * D + c0);
+      else {
+        // carried conv state row 3 + (pos - t0); its channels are not 16-byte aligned in general
+        const RawT* cr = raw_cs + (3 + (pos - t0)) * Cch + ch0 + c0;
+        uint32_t wv[4];
 #pragma unroll
-          for (int e = 0; e < VE; ++e) tmp[e] = cr[e];
-          x = *reinterpret_cast<const uint4*>(tmp);
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (sizeof(RawT) == 2) wv[e] = (uint32_t)cr[2 * e] | ((uint32_t)cr[2 * e + 1] << 16);
+          else wv[e] = __float_as_uint(cr[e]);
         }
+        x = {wv[0], wv[1], wv[2], wv[3]};
       }
-      *reinterpret_cast<uint4*>(stage + sr * D + c0) = x;
     }
+    return x;
+  };
+  auto store_staged = [&](RawT* st, int D, int idx, uint4 x) {
+    if (idx < (L + 3) * (D / VE)) *reinterpret_cast<uint4*>(st + idx * VE) = x;
   };
   if constexpr (FUSED) {
     constexpr int E = DK / 64;
+    constexpr int NSK = ((L + 3) * (DK / VE) + NT - 1) / NT;  // pieces per thread of a staged q or k stream
+    constexpr int NGK = (L * (DK / VE) + NT - 1) / NT;        // pieces per thread of the g rows
+    static_assert(2 * (L + 3) * DK * sizeof(RawT) <= (size_t)(L * PK + 2 * L * PL) * sizeof(float),
+                  "staged q and k rows fit over T2, A and P");
+    RawT* stq = reinterpret_cast<RawT*>(sG);  // [67][DK] staged q rows, then k rows, over T2, A and P
+    RawT* stk = stq + (L + 3) * DK;
     const int64_t wk = (int64_t)H * DK;
-    for (int s = 0; s < 2; ++s) {  // q, then k
-      const RawT* src = static_cast<const RawT*>(s == 0 ? p.raw.q : p.raw.k);
-      const int64_t ch0 = (s == 0 ? 0 : wk) + (int64_t)h * DK;
-      float* dst = s == 0 ? sQ : sK;
-      stage_rows(src, DK, ch0);
-      __syncthreads();
-      for (int r = wave; r < L; r += NT / 64) {
-        float x[E];
-        conv_row<DK, true>([&](int j, int d) { return to_f32(stage[(r + j) * DK + d]); }, p.raw.conv_w + ch0 * 4,
-                           p.raw.act, x);
+    const int64_t chq = (int64_t)h * DK, chk = wk + (int64_t)h * DK;
+    uint4 xq[NSK], xk[NSK], xg[NGK];
 #pragma unroll
-        for (int e = 0; e < E; ++e) dst[r * PK + E * lane + e] = r < len ? x[e] : 0.f;
-      }
-      __syncthreads();
+    for (int i = 0; i < NSK; ++i) {
+      xq[i] = load_staged(static_cast<const RawT*>(p.raw.q), DK, chq, t + i * NT);
+      xk[i] = load_staged(static_cast<const RawT*>(p.raw.k), DK, chk, t + i * NT);
     }
     const RawT* rg = static_cast<const RawT*>(p.raw.g);
-    for (int idx = t; idx < L * DK; idx += NT) {
-      const int r = idx / DK, d = idx % DK;
-      sG[r * PK + d] = r < len ? log_decay(to_f32(rg[((start + r) * H + h) * DK + d]), p.raw.gate_mode, p.raw.lb) : 0.f;
+#pragma unroll
+    for (int i = 0; i < NGK; ++i) {
+      const int idx = t + i * NT, r = idx / (DK / VE), c0 = (idx % (DK / VE)) * VE;
+      xg[i] = {0u, 0u, 0u, 0u};
+      if (idx < L * (DK / VE) && r < len) xg[i] = *reinterpret_cast<const uint4*>(rg + ((start + r) * H + h) * DK + c0);
     }
-    if (t < L) sBeta[t] = t < len ? sigmoid(to_f32(static_cast<const RawT*>(p.raw.beta)[(start + t) * H + h])) : 0.f;
+    const float braw = (t < len) ? to_f32(static_cast<const RawT*>(p.raw.beta)[(start + t) * H + h]) : 0.f;
+#pragma unroll
+    for (int i = 0; i < NSK; ++i) {
+      store_staged(stq, DK, t + i * NT, xq[i]);
+      store_staged(stk, DK, t + i * NT, xk[i]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {  // q, then k: rows wave + 8 rr
+      const RawT* st = s == 0 ? stq : stk;
+      float* dst = s == 0 ? sQ : sK;
+      float x[L / 8][E];
+      conv_rows<DK, true, L / 8>([&](int rr, int j, int d) { return to_f32(st[(wave + 8 * rr + j) * DK + d]); },
+                                 p.raw.conv_w + (s == 0 ? chq : chk) * 4, p.raw.act, x);
+#pragma unroll
+      for (int rr = 0; rr < L / 8; ++rr) {
+        const int r = wave + 8 * rr;
+#pragma unroll
+        for (int e = 0; e < E; ++e) dst[r * PK + E * lane + e] = r < len ? x[rr][e] : 0.f;
+      }
+    }
+    __syncthreads();  // the staged rows over T2 are consumed
+#pragma unroll
+    for (int i = 0; i < NGK; ++i) {
+      const int idx = t + i * NT, r = idx / (DK / VE), c0 = (idx % (DK / VE)) * VE;
+      if (idx < L * (DK / VE)) {
+#pragma unroll
+        for (int e = 0; e < VE; ++e)
+          sG[r * PK + c0 + e] = r < len ? log_decay(piece_elem<RawT>(xg[i], e), p.raw.gate_mode, p.raw.lb) : 0.f;
+      }
+    }
+    if (t < L) sBeta[t] = t < len ? sigmoid(braw) : 0.f;
   } else {
     for (int idx = t; idx < L * (DK / 4); idx += NT) {
       const int r = idx / (DK / 4), c4 = 4 * (idx % (DK / 4));
@@ -619,6 +665,16 @@ __global__ __launch_bounds__(512) void chunk_intra_kernel(PrefillArgs p) {
   __syncthreads();
 
   // 6. X = (I + A)^{-1} into the P tile
+  // Fused: the v rows the chunk needs are loaded here and land during the solve
+  // (staged over A in step 7 where they fit; fp32 rows read their taps from HBM)
+  constexpr bool kVStaged = FUSED && (L + 3) * DV * sizeof(RawT) <= (size_t)L * PL * sizeof(float);
+  constexpr int NSV = kVStaged ? ((L + 3) * (DV / VE) + NT - 1) / NT : 1;
+  const int64_t chv = 2 * (int64_t)H * DK + (int64_t)h * DV;
+  uint4 xv[NSV];
+  if constexpr (kVStaged) {
+#pragma unroll
+    for (int i = 0; i < NSV; ++i) xv[i] = load_staged(static_cast<const RawT*>(p.raw.v), DV, chv, t + i * NT);
+  }
   float* sXi = sP;
   for (int idx = t; idx < L * L; idx += NT) sXi[(idx / L) * PL + idx % L] = 0.f;
   __syncthreads();
@@ -667,33 +723,31 @@ __global__ __launch_bounds__(512) void chunk_intra_kernel(PrefillArgs p) {
     sG[r * PK + d] = sBeta[r] * (sK[r * PK + d] * pexp<POL>(sGF[(r / 16) * DK + d] + sG[r * PK + d]));
   }
   if constexpr (FUSED) {
-    // v rows: conv (no norm) from staged taps, over the A tile (A is no longer needed);
-    // rows past the A tile's capacity fall back to taps from HBM
-    const int64_t ch0 = 2 * (int64_t)H * DK + (int64_t)h * DV;
-    constexpr bool fits = (L + 3) * DV * sizeof(RawT) <= (size_t)L * PL * sizeof(float);
-    if constexpr (fits) {
-      __syncthreads();  // every wavefront is past the solve's last read of A
-      stage_rows(static_cast<const RawT*>(p.raw.v), DV, ch0);
-      __syncthreads();
-    }
+    // v rows: conv (no norm), 8 rows per wavefront side by side, b_r v_r into T1
     constexpr int EV = DV / 64;
-    const RawT* rv = static_cast<const RawT*>(p.raw.v);
-    const int64_t wv = (int64_t)H * DV;
-    for (int r = wave; r < L; r += NT / 64) {
-      float x[EV];
-      if constexpr (fits) {
-        conv_row<DV, false>([&](int j, int d) { return to_f32(stage[(r + j) * DV + d]); }, p.raw.conv_w + ch0 * 4,
-                            p.raw.act, x);
-      } else {
-        const int64_t rel = start - t0 + r;
-        conv_row<DV, false>([&](int j, int d) {
-          const int64_t pos = rel - 3 + j;
-          if (r >= len) return 0.f;
-          return pos >= 0 ? to_f32(rv[(t0 + pos) * wv + (int64_t)h * DV + d]) : to_f32(raw_cs[(3 + pos) * Cch + ch0 + d]);
-        }, p.raw.conv_w + ch0 * 4, p.raw.act, x);
-      }
+    float x[L / 8][EV];
+    if constexpr (kVStaged) {
+      RawT* stv = reinterpret_cast<RawT*>(sA);  // [67][DV] staged v rows over A, which the solve no longer reads
+      __syncthreads();
 #pragma unroll
-      for (int e = 0; e < EV; ++e) sQ[r * PK + EV * lane + e] = r < len ? sBeta[r] * x[e] : 0.f;
+      for (int i = 0; i < NSV; ++i) store_staged(stv, DV, t + i * NT, xv[i]);
+      __syncthreads();
+      conv_rows<DV, false, L / 8>([&](int rr, int j, int d) { return to_f32(stv[(wave + 8 * rr + j) * DV + d]); },
+                                  p.raw.conv_w + chv * 4, p.raw.act, x);
+    } else {
+      const RawT* rv = static_cast<const RawT*>(p.raw.v);
+      const int64_t wv = (int64_t)H * DV, rel0 = start - t0 + wave;
+      conv_rows<DV, false, L / 8>([&](int rr, int j, int d) {
+        const int64_t pos = rel0 + 8 * rr - 3 + j;
+        if (wave + 8 * rr >= len) return 0.f;
+        return pos >= 0 ? to_f32(rv[(t0 + pos) * wv + (int64_t)h * DV + d]) : to_f32(raw_cs[(3 + pos) * Cch + chv + d]);
+      }, p.raw.conv_w + chv * 4, p.raw.act, x);
+    }
+#pragma unroll
+    for (int rr = 0; rr < L / 8; ++rr) {
+      const int r = wave + 8 * rr;
+#pragma unroll
+      for (int e = 0; e < EV; ++e) sQ[r * PK + EV * lane + e] = r < len ? sBeta[r] * x[rr][e] : 0.f;
     }
   } else {
     for (int idx = t; idx < L * (DV / 4); idx += NT) {

@@ -59,26 +59,26 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<RawT> p) {
   const int64_t wk = (int64_t)H * DK, wv = (int64_t)H * DV;
   // tap j of a channel: packed row t0+rel-3+j, or the carried conv state before the sequence start
   auto tap_of = [&](const RawT* src, int64_t width, int64_t col0, int64_t ch0) {
-    return [=](int j, int d) {
+    return [=](int, int j, int d) {
       const int64_t pos = rel - 3 + j;
       return pos >= 0 ? to_f32(src[(t0 + pos) * width + col0 + d]) : to_f32(cs[(3 + pos) * C + ch0 + d]);
     };
   };
-  float q[EK], k[EK], v[EV];
-  conv_row<DK, true>(tap_of(p.q, wk, (int64_t)h * DK, (int64_t)h * DK), p.conv_w + (int64_t)h * DK * 4, p.act, q);
-  conv_row<DK, true>(tap_of(p.k, wk, (int64_t)h * DK, wk + (int64_t)h * DK), p.conv_w + (wk + (int64_t)h * DK) * 4,
-                     p.act, k);
-  conv_row<DV, false>(tap_of(p.v, wv, (int64_t)h * DV, 2 * wk + (int64_t)h * DV),
-                      p.conv_w + (2 * wk + (int64_t)h * DV) * 4, p.act, v);
+  float q[1][EK], k[1][EK], v[1][EV];
+  conv_rows<DK, true, 1>(tap_of(p.q, wk, (int64_t)h * DK, (int64_t)h * DK), p.conv_w + (int64_t)h * DK * 4, p.act, q);
+  conv_rows<DK, true, 1>(tap_of(p.k, wk, (int64_t)h * DK, wk + (int64_t)h * DK),
+                         p.conv_w + (wk + (int64_t)h * DK) * 4, p.act, k);
+  conv_rows<DV, false, 1>(tap_of(p.v, wv, (int64_t)h * DV, 2 * wk + (int64_t)h * DV),
+                          p.conv_w + (2 * wk + (int64_t)h * DV) * 4, p.act, v);
   const int64_t ok = pair * DK + EK * lane, ov = pair * DV + EV * lane;
 #pragma unroll
   for (int e = 0; e < EK; ++e) {
-    p.q_hat[ok + e] = q[e];
-    p.k_hat[ok + e] = k[e];
+    p.q_hat[ok + e] = q[0][e];
+    p.k_hat[ok + e] = k[0][e];
     p.g_out[ok + e] = log_decay(to_f32(p.g[ok + e]), p.gate_mode, p.lb);
   }
 #pragma unroll
-  for (int e = 0; e < EV; ++e) p.v_out[ov + e] = v[e];
+  for (int e = 0; e < EV; ++e) p.v_out[ov + e] = v[0][e];
   if (lane == 0) p.beta_out[pair] = sigmoid(to_f32(p.beta[pair]));
 }
 
