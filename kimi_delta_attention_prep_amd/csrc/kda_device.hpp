@@ -24,7 +24,11 @@ constexpr int kChunk = 64;       // prompt rows per chunk
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(uint16_t x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }
 
-__device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + expf(-x)); }
+// sigma(x) = 1 / (1 + e^-x) from the hardware exp2 and reciprocal (each within
+// about one ulp); e^-x overflows to inf for x < -88, which gives exactly 0
+__device__ __forceinline__ float sigmoid(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.4426950408889634f));
+}
 
 // per-key-dim log decay g: softplus gate g = -softplus(x) = -(max(x,0) + log1p(e^-|x|));
 // safe gate g = lb * sigmoid(x), so a = e^g lies in (e^lb, 1)
@@ -33,14 +37,19 @@ __device__ __forceinline__ float log_decay(float x, int gate_mode, float lb) {
   return -(fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x))));
 }
 
-// depthwise causal conv over 4 taps (x0 oldest, x3 current row), then the activation
-__device__ __forceinline__ float conv4_act(float w0, float w1, float w2, float w3, float x0, float x1, float x2,
-                                           float x3, int act) {
+// depthwise causal conv over 4 taps (x0 oldest, x3 current row), then SiLU when ACT
+template <bool ACT>
+__device__ __forceinline__ float conv4(float w0, float w1, float w2, float w3, float x0, float x1, float x2, float x3) {
   float c = w0 * x0;
   c = fmaf(w1, x1, c);
   c = fmaf(w2, x2, c);
   c = fmaf(w3, x3, c);
-  return act ? c * sigmoid(c) : c;
+  if constexpr (ACT) return c * sigmoid(c);
+  return c;
+}
+__device__ __forceinline__ float conv4_act(float w0, float w1, float w2, float w3, float x0, float x1, float x2,
+                                           float x3, int act) {
+  return act ? conv4<true>(w0, w1, w2, w3, x0, x1, x2, x3) : conv4<false>(w0, w1, w2, w3, x0, x1, x2, x3);
 }
 
 // sum over the 64 lanes of a wavefront (xor butterfly: at every step both
@@ -60,8 +69,8 @@ __device__ __forceinline__ float wave_sum(float x) {
 // by side; each row's arithmetic does not depend on NR, so the standalone
 // preamble kernel (one row, taps from HBM) and the fused prompt kernel (eight
 // rows, taps from LDS) produce the same bits.
-template <int D, bool NORM, int NR, class TAP>
-__device__ __forceinline__ void conv_rows(TAP tap, const float* __restrict__ w, int act, float (&out)[NR][D / 64]) {
+template <int D, bool NORM, int NR, bool ACT, class TAP>
+__device__ __forceinline__ void conv_rows_t(TAP tap, const float* __restrict__ w, float (&out)[NR][D / 64]) {
   constexpr int E = D / 64;
   const int lane = threadIdx.x & 63;
   float wt[E][4];
@@ -76,8 +85,8 @@ __device__ __forceinline__ void conv_rows(TAP tap, const float* __restrict__ w, 
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int d = E * lane + e;
-      out[rr][e] = conv4_act(wt[e][0], wt[e][1], wt[e][2], wt[e][3], tap(rr, 0, d), tap(rr, 1, d), tap(rr, 2, d),
-                             tap(rr, 3, d), act);
+      out[rr][e] = conv4<ACT>(wt[e][0], wt[e][1], wt[e][2], wt[e][3], tap(rr, 0, d), tap(rr, 1, d), tap(rr, 2, d),
+                              tap(rr, 3, d));
       ss[rr] = fmaf(out[rr][e], out[rr][e], ss[rr]);
     }
   }
@@ -93,6 +102,13 @@ __device__ __forceinline__ void conv_rows(TAP tap, const float* __restrict__ w, 
       for (int e = 0; e < E; ++e) out[rr][e] *= r;
     }
   }
+}
+// the activation is chosen once for the whole batch of rows, so that the rows'
+// loads and arithmetic interleave freely
+template <int D, bool NORM, int NR, class TAP>
+__device__ __forceinline__ void conv_rows(TAP tap, const float* __restrict__ w, int act, float (&out)[NR][D / 64]) {
+  if (act) conv_rows_t<D, NORM, NR, true>(tap, w, out);
+  else conv_rows_t<D, NORM, NR, false>(tap, w, out);
 }
 
 // one state element's step: S' = a * S, then S = S' + k * u (explicit fma).

@@ -395,10 +395,11 @@ struct IntraSmem {
   static constexpr int TB = TP + L * PL;      // beta                                [L]
   static constexpr int TGF = TB + L;          // G_{16R} from the chunk start        [4][DK]
   static constexpr int TX = TGF + 4 * DK;     // G_last - G_{16I}                    [4][DK]
-  static constexpr int TD = TX + 4 * DK;      // D_RI = G_{16R} - G_{16I}, I < R      [6][DK]
-  static constexpr int TG0 = TD + 6 * DK;     // g at each block's first row         [4][DK]
-  static constexpr int TY = TG0 + 4 * DK;     // solve scratch                       [2][16][17]
-  static constexpr int TFLAG = TY + 2 * 16 * 17;
+  static constexpr int TD = TX + 4 * DK;      // e^{G_{16R} - G_{16I+16}}, I + 1 < R  [6][DK]
+  static constexpr int TG0 = TD + 6 * DK;     // g at each block's first row, then
+                                              // T_I = G_{16I+16} - G_{16I}            [4][DK]
+  static constexpr int TY = TG0 + 4 * DK;     // solve scratch, one per wavefront    [3][16][17]
+  static constexpr int TFLAG = TY + 3 * 16 * 17;
   static constexpr int FLOATS = TFLAG + 4;
   static constexpr size_t BYTES = FLOATS * sizeof(float);
 };
@@ -415,6 +416,55 @@ __device__ __forceinline__ float piece_elem(const uint4& x, int e) {
 }
 
 __device__ __forceinline__ int pair_index(int R, int I) { return R * (R - 1) / 2 + I; }  // I < R
+
+// One block pair of A and P: acc_a += (s . La) Rt^T and acc_p += (s . Lq) Rt^T over
+// K = DK, where La, Lq, Rt point at 16 rows of row stride PK and s is a per-K
+// scale (none when null).  The right operand is split once for both products.
+template <int IP, int DK, int PK>
+__device__ __forceinline__ void pair_mma(floatx4& acc_a, floatx4& acc_p, const float* La, const float* Lq,
+                                         const float* Rt, const float* s) {
+  const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+  if constexpr (IP == POL_FP32) {
+    auto fa = [&](int i, int kk) { return s ? La[i * PK + kk] * s[kk] : La[i * PK + kk]; };
+    auto fq = [&](int i, int kk) { return s ? Lq[i * PK + kk] * s[kk] : Lq[i * PK + kk]; };
+    auto fb = [&](int kk, int j) { return Rt[j * PK + kk]; };
+    mma16<IP>(acc_a, DK, fa, fb);
+    mma16<IP>(acc_p, DK, fq, fb);
+  } else {
+#pragma unroll
+    for (int k0 = 0; k0 < DK; k0 += 32) {
+      const int kk = k0 + 8 * g;
+      float a[8], q[8], b[8];
+      auto ld8 = [&](const float* p, float (&x)[8]) {
+        const float4 u = *reinterpret_cast<const float4*>(p), w = *reinterpret_cast<const float4*>(p + 4);
+        x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w; x[4] = w.x; x[5] = w.y; x[6] = w.z; x[7] = w.w;
+      };
+      ld8(La + r * PK + kk, a);
+      ld8(Lq + r * PK + kk, q);
+      ld8(Rt + r * PK + kk, b);
+      if (s) {
+        float sc[8];
+        ld8(s + kk, sc);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { a[e] *= sc[e]; q[e] *= sc[e]; }
+      }
+      bf16x8 ah, al, qh, ql, bh, bl;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        __bf16 h, l;
+        split_bf16(a[e], h, l); ah[e] = h; al[e] = l;
+        split_bf16(q[e], h, l); qh[e] = h; ql[e] = l;
+        split_bf16(b[e], h, l); bh[e] = h; bl[e] = l;
+      }
+      acc_a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc_a, 0, 0, 0);
+      acc_a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc_a, 0, 0, 0);
+      acc_a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc_a, 0, 0, 0);
+      acc_p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql, bh, acc_p, 0, 0, 0);
+      acc_p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, bl, acc_p, 0, 0, 0);
+      acc_p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, bh, acc_p, 0, 0, 0);
+    }
+  }
+}
 
 template <int DK, int DV, int POL, typename RawT, bool FUSED>
 __global__ __launch_bounds__(512) void chunk_intra_kernel(PrefillArgs p) {
@@ -570,7 +620,8 @@ __global__ __launch_bounds__(512) void chunk_intra_kernel(PrefillArgs p) {
   }
   __syncthreads();
 
-  // 3. per key dim, from block-local sums: T_R = G_{16R+16} - G_{16R}, G_{16R}, G_last - G_{16I}, D_RI
+  // 3. per key dim, from block-local sums: T_R = G_{16R+16} - G_{16R}, G_{16R}, G_last - G_{16I},
+  //    e^{G_{16R} - G_{16I+16}} for the off-diagonal block pairs, and gamma_L
   if (t < DK) {
     const int d = t;
     float T[3];
@@ -588,46 +639,91 @@ __global__ __launch_bounds__(512) void chunk_intra_kernel(PrefillArgs p) {
         for (int J = R; J < Rl; ++J) x += T[J];
       }
       sX[R * DK + d] = x;
-      for (int I = 0; I < R; ++I) {
+      for (int I = 0; I + 1 < R; ++I) {
         float dd = 0.f;
-        for (int J = I; J < R; ++J) dd += T[J];
-        sD[pair_index(R, I) * DK + d] = dd;
+        for (int J = I + 1; J < R; ++J) dd += T[J];
+        sD[pair_index(R, I) * DK + d] = pexp<POL>(dd);
       }
       if (R < 3) gf += T[R];
     }
     float glast = sG0[d];
     for (int J = 0; J < Rl; ++J) glast += T[J];
     reinterpret_cast<float*>(rec + rl.gL)[d] = pexp<POL>(glast + glL);
+#pragma unroll
+    for (int R = 0; R < 3; ++R) sG0[R * DK + d] = T[R];  // g at the first rows is no longer needed
   }
   __syncthreads();
   const bool exact = sFlag[0] != 0;
 
-  // 4. A and P: 10 blocks x {A, P} = 20 tile products over the 8 wavefronts
+  // 4. operand fragments of Q^gamma = e^{G_r} q_r and K_<^T (e^{G_last - G_i} k_i), from q, k and gl
+  write_afrags<POL, NT>(rec + rl.Qf, 4, DK / 32, [&](int r, int d) {
+    return sQ[r * PK + d] * pexp<POL>(sGF[(r / 16) * DK + d] + sG[r * PK + d]);
+  });
+  write_afrags<POL, NT>(rec + rl.Kf, DK / 16, 2, [&](int d, int r) {
+    return sK[r * PK + d] * pexp<POL>(sX[(r / 16) * DK + d] - sG[r * PK + d]);
+  });
+  __syncthreads();
+
+  // 5. A and P.  Per block pair (R, I <= R), with pivots at the blocks' first rows:
+  //      A_ri = b_r sum_d [k_r e^{gl_r}] E_RI [k_i e^{T_I - gl_i}]     (I < R)
+  //      A_ri = b_r sum_d [k_r e^{gl_r}]      [k_i e^{-gl_i}]          (I = R)
+  //    with E_RI = e^{G_{16R} - G_{16I+16}} (1 for R = I + 1), and the same with q_r for P.
+  //    Off the diagonal every factor is at most 1, so a factor that underflows
+  //    belongs to a term below e^-87; on the diagonal the span guard keeps both
+  //    factors within e^{+-80}.  The factors are formed once per chunk in place:
+  //    T0 = k e^{gl}, T1 = q e^{gl}, T2 = k e^{-gl}, and k e^{T_I - gl} for
+  //    blocks 0..2 over the A / P tiles; each wavefront then computes whole
+  //    block pairs, A and P together, sharing the right operand.
   if (!exact) {
-    for (int item = wave; item < 20; item += NT / 64) {
-      const int blk = item >> 1;
-      const bool isP = item & 1;
-      int R = 0, I = blk;  // blocks in order (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) ...
-      while (I > R) { I -= R + 1; ++R; }
-      const float* x = isP ? sQ : sK;
-      const float* dd = I < R ? &sD[pair_index(R, I) * DK] : nullptr;
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-      mma16<IP>(acc, DK,
-                [&](int i, int kk) {
-                  const int r = 16 * R + i;
-                  return x[r * PK + kk] * pexp<POL>(sG[r * PK + kk]);
-                },
-                [&](int kk, int j) {
-                  const int r = 16 * I + j;
-                  const float e = fmaxf(sG[r * PK + kk], -kSpanGuard);
-                  return sK[r * PK + kk] * pexp<POL>((dd ? dd[kk] : 0.f) - e);
-                });
-      const int col = lane & 15, g4 = lane >> 4;
+    float* sRk = sA;  // [48][PK] k e^{T_I - gl}, over the A and P tiles until the products are done
+    for (int idx = t; idx < L * (DK / 4); idx += NT) {
+      const int r = idx / (DK / 4), d4 = 4 * (idx % (DK / 4));
+      const float4 kk = *reinterpret_cast<const float4*>(&sK[r * PK + d4]);
+      const float4 qq = *reinterpret_cast<const float4*>(&sQ[r * PK + d4]);
+      const float4 gg = *reinterpret_cast<const float4*>(&sG[r * PK + d4]);
+      const float kv[4] = {kk.x, kk.y, kk.z, kk.w}, qv[4] = {qq.x, qq.y, qq.z, qq.w}, gv[4] = {gg.x, gg.y, gg.z, gg.w};
+      float lk[4], lq[4], rd[4], rk[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int rr = 16 * R + 4 * g4 + v, ii = 16 * I + col;
-        if (isP) sP[rr * PL + ii] = (ii <= rr) ? acc[v] : 0.f;
-        else sA[rr * PL + ii] = (ii < rr) ? sBeta[rr] * acc[v] : 0.f;
+      for (int e = 0; e < 4; ++e) {
+        const float ep = pexp<POL>(gv[e]);
+        lk[e] = kv[e] * ep;
+        lq[e] = qv[e] * ep;
+        rd[e] = kv[e] * pexp<POL>(-gv[e]);
+        if (r < 48) rk[e] = kv[e] * pexp<POL>(sG0[(r / 16) * DK + d4 + e] - gv[e]);
+      }
+      *reinterpret_cast<float4*>(&sK[r * PK + d4]) = make_float4(lk[0], lk[1], lk[2], lk[3]);
+      *reinterpret_cast<float4*>(&sQ[r * PK + d4]) = make_float4(lq[0], lq[1], lq[2], lq[3]);
+      *reinterpret_cast<float4*>(&sG[r * PK + d4]) = make_float4(rd[0], rd[1], rd[2], rd[3]);
+      if (r < 48) *reinterpret_cast<float4*>(&sRk[r * PK + d4]) = make_float4(rk[0], rk[1], rk[2], rk[3]);
+    }
+    __syncthreads();
+    floatx4 acc[2][2];  // [pair of this wavefront][A, P]
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int pr = wave + 8 * j;  // pairs in order (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) ...
+      acc[j][0] = acc[j][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (pr < 10) {
+        int R = 0, I = pr;
+        while (I > R) { I -= R + 1; ++R; }
+        const float* right = I == R ? &sG[16 * I * PK] : &sRk[16 * I * PK];
+        const float* scale = I + 1 < R ? &sD[pair_index(R, I) * DK] : nullptr;
+        pair_mma<IP, DK, PK>(acc[j][0], acc[j][1], &sK[16 * R * PK], &sQ[16 * R * PK], right, scale);
+      }
+    }
+    __syncthreads();  // every wavefront is done with the factors over A and P
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int pr = wave + 8 * j;
+      if (pr < 10) {
+        int R = 0, I = pr;
+        while (I > R) { I -= R + 1; ++R; }
+        const int col = lane & 15, g4 = lane >> 4;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int rr = 16 * R + 4 * g4 + v, ii = 16 * I + col;
+          sA[rr * PL + ii] = (ii < rr) ? sBeta[rr] * acc[j][0][v] : 0.f;
+          sP[rr * PL + ii] = (ii <= rr) ? acc[j][1][v] : 0.f;
+        }
       }
     }
     for (int idx = t; idx < L * L; idx += NT) {  // strictly-upper blocks are zero
@@ -653,14 +749,6 @@ __global__ __launch_bounds__(512) void chunk_intra_kernel(PrefillArgs p) {
     }
   }
   __syncthreads();
-
-  // 5. operand fragments of Q^gamma = e^{G_r} q_r, K_<^T (e^{G_last - G_i} k_i) and P
-  write_afrags<POL, NT>(rec + rl.Qf, 4, DK / 32, [&](int r, int d) {
-    return sQ[r * PK + d] * pexp<POL>(sGF[(r / 16) * DK + d] + sG[r * PK + d]);
-  });
-  write_afrags<POL, NT>(rec + rl.Kf, DK / 16, 2, [&](int d, int r) {
-    return sK[r * PK + d] * pexp<POL>(sX[(r / 16) * DK + d] - sG[r * PK + d]);
-  });
   write_afrags<POL, NT>(rec + rl.Pf, 4, 2, [&](int r, int i) { return sP[r * PL + i]; });
   __syncthreads();
 
@@ -692,35 +780,63 @@ __global__ __launch_bounds__(512) void chunk_intra_kernel(PrefillArgs p) {
     for (int r = 0; r < 16; ++r) sXi[(b0 + r) * PL + b0 + cc] = xv[r];
   }
   __syncthreads();
-  // off-diagonal blocks, nearest diagonals first (two blocks at a time):
-  // X_RI = -X_RR sum_{J=I}^{R-1} A_RJ X_JI
+  // off-diagonal blocks, nearest diagonals first, one wavefront per block on the matrix cores (fp32):
+  //   Y = sum_{J=I}^{R-1} A_RJ X_JI,  X_RI = -X_RR Y
   for (int dist = 1; dist < 4; ++dist) {
-    for (int I0 = 0; I0 + dist < 4; I0 += 2) {
-      const int I = I0 + (t >> 8), R = I + dist;
-      const bool act = (t >> 8) < 2 && R < 4;
-      const int r = (t >> 4) & 15, cc = t & 15;
-      float* y = sY + (t >> 8) * 16 * 17;
-      if (act) {
-        float acc = 0.f;
-        for (int J = I; J < R; ++J)
-          for (int kk = 0; kk < 16; ++kk)
-            acc = fmaf(sA[(16 * R + r) * PL + 16 * J + kk], sXi[(16 * J + kk) * PL + 16 * I + cc], acc);
-        y[r * 17 + cc] = acc;
-      }
-      __syncthreads();
-      if (act) {
-        float acc = 0.f;
-        for (int kk = 0; kk <= r; ++kk) acc = fmaf(sXi[(16 * R + r) * PL + 16 * R + kk], y[kk * 17 + cc], acc);
-        sXi[(16 * R + r) * PL + 16 * I + cc] = -acc;
-      }
-      __syncthreads();
+    if (wave < 4 - dist) {
+      const int I = wave, R = I + dist, col = lane & 15, g4 = lane >> 4;
+      floatx4 y = {0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 16 * I; k0 < 16 * R; k0 += 4)
+        y = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[(16 * R + col) * PL + k0 + g4], sXi[(k0 + g4) * PL + 16 * I + col],
+                                                 y, 0, 0, 0);
+      float* yb = sY + wave * 16 * 17;  // this wavefront's own scratch: written, then read back in order
+#pragma unroll
+      for (int v = 0; v < 4; ++v) yb[(4 * g4 + v) * 17 + col] = y[v];
+      floatx4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k0 = 0; k0 < 16; k0 += 4)
+        x = __builtin_amdgcn_mfma_f32_16x16x4f32(sXi[(16 * R + col) * PL + 16 * R + k0 + g4], yb[(k0 + g4) * 17 + col],
+                                                 x, 0, 0, 0);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sXi[(16 * R + 4 * g4 + v) * PL + 16 * I + col] = -x[v];
     }
+    __syncthreads();
   }
 
-  // 7. right-hand sides: b_r e^{G_r} k_r into T2 (over gl), b_r v_r into T1
-  for (int idx = t; idx < L * DK; idx += NT) {
-    const int r = idx / DK, d = idx % DK;
-    sG[r * PK + d] = sBeta[r] * (sK[r * PK + d] * pexp<POL>(sGF[(r / 16) * DK + d] + sG[r * PK + d]));
+  // 7. right-hand sides as B-operand fragments of the intra products:
+  //    b_r e^{G_r} k_r into T2, b_r v_r into T0 (through T1).  A fragment item is
+  //    (column tile c, 32-row block kb, lane): 8 rows of one column.  e^{G_r} k_r
+  //    is e^{G_{16R}} (k_r e^{gl_r}) from the factors of step 5, or formed
+  //    directly from gl on the exact path.
+  using FI = Frag<IP>;
+  using FB = typename FI::B;
+  constexpr bool kContig = FI::kof(0, 1) == 1;  // a lane's 8 rows lie in one 16-row block
+  constexpr int NFK = (DK / 16) * 2 * 64, PFK = (NFK + NT - 1) / NT;
+  constexpr int NFV = (DV / 16) * 2 * 64, PFV = (NFV + NT - 1) / NT;
+  {
+    FB fk[PFK];
+#pragma unroll
+    for (int i = 0; i < PFK; ++i) {
+      const int item = t + i * NT;
+      if (item < NFK) {
+        const int ln = item & 63, kb = (item >> 6) & 1, c = item >> 7;
+        const int d = 16 * c + (ln & 15), g = ln >> 4;
+        float x[8];
+        const float eg0 = pexp<POL>(sGF[((32 * kb + FI::kof(g, 0)) / 16) * DK + d]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 32 * kb + FI::kof(g, e);
+          const float gf = sGF[(r / 16) * DK + d];
+          if (exact) x[e] = sBeta[r] * (sK[r * PK + d] * pexp<POL>(gf + sG[r * PK + d]));
+          else x[e] = sBeta[r] * (sK[r * PK + d] * (kContig ? eg0 : pexp<POL>(gf)));
+        }
+        fk[i] = FI::make_b(x);
+      }
+    }
+    __syncthreads();  // every read of T2 is done
+#pragma unroll
+    for (int i = 0; i < PFK; ++i)
+      if (t + i * NT < NFK) reinterpret_cast<FB*>(sG)[t + i * NT] = fk[i];
   }
   if constexpr (FUSED) {
     // v rows: conv (no norm), 8 rows per wavefront side by side, b_r v_r into T1
@@ -761,29 +877,63 @@ __global__ __launch_bounds__(512) void chunk_intra_kernel(PrefillArgs p) {
   }
   __syncthreads();
 
-  // 8. W = X (b K^gamma), U~ = X (b V); X is lower triangular, so row block R needs K = 16(R+1).
-  //    U~ goes to the record in result layout; W through LDS (T0) into fragments.
-  constexpr int NTW = 4 * (DK / 16), NTU = 4 * (DV / 16);
-  float* sW = sK;
-  for (int tile = wave; tile < NTW + NTU; tile += NT / 64) {
-    const bool isW = tile < NTW;
-    const int tt = isW ? tile : tile - NTW;
-    const int R = tt % 4, cb = tt / 4;
-    const int K = (16 * (R + 1) + 31) / 32 * 32;
-    const float* B = isW ? sG : sQ;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    mma16<IP>(acc, K, [&](int i, int kk) { return sXi[(16 * R + i) * PL + kk]; },
-              [&](int kk, int j) { return B[kk * PK + 16 * cb + j]; });
-    if (!isW) *reinterpret_cast<floatx4*>(rec + rl.Ut + ((int64_t)(cb * 4 + R) * 64 + lane) * 16) = acc;
-    else {
-      // W tiles overwrite k_hat in T0 only after every wavefront has passed step 7
-      const int col = lane & 15, g4 = lane >> 4;
+  {
+    FB fv[PFV];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) sW[(16 * R + 4 * g4 + v) * PK + 16 * cb + col] = acc[v];
+    for (int i = 0; i < PFV; ++i) {
+      const int item = t + i * NT;
+      if (item < NFV) {
+        const int ln = item & 63, kb = (item >> 6) & 1, c = item >> 7;
+        const int d = 16 * c + (ln & 15), g = ln >> 4;
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = sQ[(32 * kb + FI::kof(g, e)) * PK + d];
+        fv[i] = FI::make_b(x);
+      }
     }
+    // T0 (k e^{gl}, or k) was last read before the barrier above
+#pragma unroll
+    for (int i = 0; i < PFV; ++i)
+      if (t + i * NT < NFV) reinterpret_cast<FB*>(sK)[t + i * NT] = fv[i];
   }
   __syncthreads();
-  write_afrags<POL, NT>(rec + rl.Wf, 4, DK / 32, [&](int r, int d) { return sW[r * PK + d]; });
+
+  // 8. W = X (b K^gamma), U~ = X (b V).  X is lower triangular, so row block R
+  //    needs K = 16(R+1) rounded up to 32.  Two wavefronts per row block R, each
+  //    holding its split rows of X and taking half of the W and U~ column tiles.
+  //    U~ goes to the record in result layout; W through LDS (T1) into fragments.
+  {
+    constexpr int NTW = DK / 16, NTU = DV / 16, NTT = NTW + NTU;
+    const FB* fRk = reinterpret_cast<const FB*>(sG);
+    const FB* fV = reinterpret_cast<const FB*>(sK);
+    float* sW = sQ;  // b v rows in T1 are consumed
+    const int R = 3 - (wave >> 1), half = wave & 1, KBR = (16 * (R + 1) + 31) / 32;
+    const int col = lane & 15, g4 = lane >> 4;
+    typename FI::A xa[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = sXi[(16 * R + col) * PL + 32 * kb + FI::kof(g4, e)];
+      xa[kb] = FI::make_b(x);
+    }
+    for (int c = half * (NTT / 2); c < (half + 1) * (NTT / 2); ++c) {
+      const bool isW = c < NTW;
+      const int cb = isW ? c : c - NTW;
+      const FB* bsrc = isW ? fRk : fV;
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        if (kb < KBR) acc = FI::mma(acc, xa[kb], bsrc[(cb * 2 + kb) * 64 + lane]);
+      if (!isW) *reinterpret_cast<floatx4*>(rec + rl.Ut + ((int64_t)(cb * 4 + R) * 64 + lane) * 16) = acc;
+      else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sW[(16 * R + 4 * g4 + v) * PK + 16 * cb + col] = acc[v];
+      }
+    }
+    __syncthreads();
+    write_afrags<POL, NT>(rec + rl.Wf, 4, DK / 32, [&](int r, int d) { return sW[r * PK + d]; });
+  }
 }
 
 // ---------------------------------------------------------------------------
