@@ -1,18 +1,27 @@
 """Benchmark of the KDA layer's hot path on one MI355X.
 
 One step = one prompt pass of the whole layer over a T=4096, H=16, d=128 bf16
-sequence (kda_prep -> kda_prefill_varlen -> gated_rmsnorm_out), carrying the
-recurrent state and conv state from step to step.  Throughput `value` is
-prompt tokens per second.  Batched decode (B=256 sequences, H=32, d=128, one
-row per sequence per step, 512 MiB of fp32 state) is timed in the same run and
-reported under "decode".  Inputs are synthetic (seeded), resident in HBM
-before timing starts.  Prints one JSON line.
+sequence: kda_prefill_varlen with the preamble fused (raw rows in), then
+gated_rmsnorm_out to bf16, carrying the recurrent state and conv state from
+step to step.  `value` is prompt tokens per second.  Batched decode (B=256
+sequences, H=32, d=128, one row per sequence per step, 512 MiB of fp32 state)
+is timed in the same run and reported under "decode".  Inputs are synthetic
+(seeded) and resident in HBM before timing starts.  Prints one JSON line.
 
 Timing: HIP events on torch's current stream (every library call is enqueued
-on it), W warmup steps, then exactly K steps bracketed by synchronize().  Each
-entry point is bracketed by its own events inside the timed region; the
-roofline object uses those live durations and the algorithmic bytes / FLOPs
-per launch documented in the design doc.
+on it): W warmup steps, then exactly K steps bracketed by synchronize().  The
+library's timing hook (kda_set_timing_events) brackets every kernel of the
+prompt call with events on the same stream, so the roofline object uses the
+dominant kernel's live average duration.  Its `traffic` comes from the
+rocprofv3 counter summary committed under profiles/, and is null when the
+kernel sources have changed since those counters were taken.
+
+Modes besides the default run:
+  --copy-calibration   also time a plain 1 GiB device copy (for counter runs:
+                       the copy's FETCH_SIZE / WRITE_SIZE scale the kernels')
+  --pmc-summary F W    turn two rocprofv3 --pmc runs (FETCH_SIZE, then
+                       WRITE_SIZE; their counter_collection.csv files) into
+                       the committed traffic summary
 """
 from __future__ import annotations
 
@@ -43,6 +52,104 @@ def prefill_algorithmic(T, H, dk, dv, chunk=64, y_bytes=4, in_bytes=2):
     bytes_ = T * H * (in_bytes * (3 * dk + 2 * dv) + in_bytes + y_bytes * dv)
     bytes_ += 2 * (H * dk * dv * 4) + 2 * 3 * H * (2 * dk + dv) * in_bytes
     return flops, bytes_
+
+
+def kernel_algorithmic(name, T, H, dk, dv, N=1, chunk=64, in_bytes=2, y_bytes=2):
+    """Algorithmic work of one launch of a kernel of the prompt pass: the HBM bytes
+    the pass cannot avoid that this kernel moves, and the FLOPs it must do.
+      chunk_intra  raw q, k, g, v rows + beta logit in; A, P, W, U~ and the solve
+      chunk_scan   o out + the state read and written; the three state products
+      gated_rmsnorm  o and z in, y out"""
+    C = chunk
+    th = T * H
+    if name == "chunk_intra":
+        macs = (C - 1) / 2 * dk + (C + 1) / 2 * (2 * dk + dv) + C * C / 6
+        return 2 * macs * th, th * (in_bytes * (3 * dk + dv) + in_bytes)
+    if name == "chunk_scan":
+        return 2 * 3 * dk * dv * th, th * dv * 4 + 2 * N * H * dk * dv * 4
+    if name == "gated_rmsnorm":
+        return 4 * dv * th, th * dv * (4 + in_bytes + y_bytes)
+    return 0.0, 0.0
+
+
+def source_digest():
+    """Digest of the sources the prompt and decode kernels are built from."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "kimi_delta_attention_prep_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp", ".cpp")):
+            h.update(f.encode())
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_T4096_H16_decode_B256.json")
+
+
+def committed_traffic(kernel, precision):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None if there is none, it was taken at another precision policy, or the
+    kernel sources changed since it was taken."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != source_digest() or t.get("precision") != precision:
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k["hbm_bytes_per_launch"]
+
+
+def pmc_summary(fetch_csv, write_csv, command, precision):
+    """Per-kernel FETCH_SIZE / WRITE_SIZE (KiB per dispatch) from two rocprofv3
+    counter runs, scaled by what the same counters read for the 1 GiB copy."""
+    import csv
+    from collections import defaultdict
+
+    def per_kernel(path, counter):
+        # average per dispatch of each kernel; for the copy, only the dispatches
+        # of the largest grid (the 1 GiB calibration copy)
+        acc = defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                acc[r["Kernel_Name"]].append((int(r["Grid_Size"]), float(r["Counter_Value"])))
+        out = {}
+        for k, v in acc.items():
+            if "copyBuffer" in k:
+                g = max(x[0] for x in v)
+                v = [x for x in v if x[0] == g]
+            out[k] = sum(x[1] for x in v) / len(v)
+        return out
+
+    f, w = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+
+    def find(d, key):
+        m = [k for k in d if key in k]
+        return max(m, key=lambda k: d[k]) if m else None
+
+    copy = find(f, "copyBuffer")
+    copy_kib = COPY_BYTES / 1024
+    ff = copy_kib / f[copy] if copy else 1.0
+    fw = copy_kib / w[find(w, "copyBuffer")] if copy else 1.0
+    keys = {"chunk_intra": "chunk_intra_kernel", "chunk_scan": "chunk_scan_kernel",
+            "gated_rmsnorm": "gated_rmsnorm_kernel", "kda_rows (decode)": "kda_rows_kernel",
+            "prefill_conv_state": "prefill_conv_state_kernel", "chunk_table": "chunk_table_kernel"}
+    out = {"command": command, "source_sha256": source_digest(), "precision": precision,
+           "copy_calibration": {"kernel": copy, "bytes": COPY_BYTES, "fetch_kib": f.get(copy), "write_kib":
+                                w.get(find(w, "copyBuffer")), "fetch_scale": ff, "write_scale": fw},
+           "kernels": {}}
+    for name, key in keys.items():
+        kf, kw = find(f, key), find(w, key)
+        if kf is None or kw is None:
+            continue
+        rd, wr = f[kf] * ff * 1024, w[kw] * fw * 1024
+        out["kernels"][name] = {"kernel": kf, "fetch_kib_raw": f[kf], "write_kib_raw": w[kw],
+                                "read_bytes": rd, "write_bytes": wr, "hbm_bytes_per_launch": rd + wr}
+    return out
+
+
+COPY_BYTES = 1 << 30
 
 
 def decode_algorithmic(B, H, dk, dv, in_bytes=2):
@@ -80,9 +187,18 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--unfused", action="store_true", help="run kda_prep separately instead of inside the prompt pass")
-    ap.add_argument("--precision", choices=("fp16", "bf16x3", "fp32"), default="bf16x3",
+    ap.add_argument("--precision", choices=("fp16", "bf16x3", "fp32"), default="fp16",
                     help="arithmetic of the prompt path's matrix products (see kda_precision)")
+    ap.add_argument("--copy-calibration", action="store_true", help="also run a plain 1 GiB device copy")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--pmc-command", default="", help="the counter command, stored in the summary")
     args = ap.parse_args()
+    if args.pmc_summary:
+        out = pmc_summary(*args.pmc_summary, args.pmc_command, args.precision)
+        with open(TRAFFIC_FILE, "w") as fh:
+            json.dump(out, fh, indent=1)
+        print(json.dumps(out, indent=1))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -138,44 +254,69 @@ def main():
         if ev is not None:
             ev[i].record(stream)
 
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    evs = [[mk() for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    kev = [[mk() for _ in range(2 * len(K.PREFILL_KERNELS))] for _ in range(args.steps)]
+    for e in (x for row in kev for x in row):
+        e.record(stream)  # creates the HIP events the hook records into
+    t_start, t_end = mk(), mk()
     torch.cuda.synchronize()
     t_start.record(stream)
     for s in range(args.steps):
+        K.kda_set_timing_events(kev[s])
         step(evs[s])
     t_end.record(stream)
     torch.cuda.synchronize()
+    K.kda_set_timing_events(None)
     ms = t_start.elapsed_time(t_end) / args.steps
     per_entry = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i, n in enumerate(names)}
+    per_kernel = {}
+    for i, n in enumerate(K.PREFILL_KERNELS):
+        if args.unfused and n == "prefill_conv_state":
+            continue
+        per_kernel[n] = sum(e[2 * i].elapsed_time(e[2 * i + 1]) for e in kev) / args.steps
+    per_kernel["gated_rmsnorm"] = per_entry["gated_rmsnorm_out"]  # one kernel per call
     tokens_per_s = T / (ms * 1e-3)
 
     flops, bytes_ = prefill_algorithmic(T, H, dk, dv, y_bytes=2)
-    dom = max(per_entry, key=per_entry.get)
-    dom_ms = per_entry[dom]
-    # prefill entry point: matrix-core work dominates its kernels' arithmetic; the
-    # roofline object prices the whole pass's algorithmic FLOPs against it
-    if dom == "kda_prefill_varlen":
-        roof = {"kernel": "kda_prefill_varlen (chunk_intra + chunk_scan)", "bound": "hbm",
-                "achieved": bytes_ / (dom_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-    else:
-        roof = {"kernel": dom, "bound": "hbm", "achieved": bytes_ / (dom_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+    dom = max(per_kernel, key=per_kernel.get)
+    dom_ms = per_kernel[dom]
+    kf, kb = kernel_algorithmic(dom, T, H, dk, dv, N=w.N)
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if kb > 0 and kf / kb < ridge:
+        roof = {"kernel": dom, "bound": "hbm", "achieved": kb / (dom_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
+    else:
+        roof = {"kernel": dom, "bound": "mfma", "achieved": kf / (dom_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = committed_traffic(dom, args.precision)
+    roof["ms_per_launch"] = dom_ms
+    roof["algorithmic_bytes_per_launch"] = kb
+    roof["algorithmic_flops_per_launch"] = kf
     out = {
         "metric": "KDA tokens/s: prefill (T=4096,H=16) and decode (B=256); % MFMA/HBM peak",
         "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {"fp16": "fp16", "bf16x3": "bf16", "fp32": "f32"}[args.precision],
         "data": "synthetic",
         "config": {"workload": "prefill T=4096 H=16 d_k=d_v=128 bf16 rows, fp32 state, safe gate lb=-5, chunk 64",
                    "matrix_products": args.precision, "preamble": "separate" if args.unfused else "fused",
                    "global_batch": 1, "seq_len": T, "parallelism": "none"},
         "roofline": roof,
         "entry_points_ms": per_entry,
+        "kernels_ms": per_kernel,
         "whole_pass": {"algorithmic_GB": bytes_ / 1e9, "algorithmic_GFLOP": flops / 1e9,
                        "GB_per_s": bytes_ / (ms * 1e-3) / 1e9, "hbm_frac": bytes_ / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                        "TFLOP_per_s": flops / (ms * 1e-3) / 1e12,
@@ -211,9 +352,10 @@ def main():
         dflops, dbytes = decode_algorithmic(B, Hd, wdec.dk, wdec.dv)
         out["decode"] = {"workload": "decode B=256 H=32 d=128 bf16 rows, fp32 state (512 MiB), safe gate lb=-5",
                          "value": B / (dms * 1e-3), "unit": "tokens/s", "ms_per_step": dms,
-                         "roofline": {"kernel": "kda_rows_kernel (kda_decode)", "bound": "hbm",
+                         "roofline": {"kernel": "kda_rows (decode)", "bound": "hbm",
                                       "achieved": dbytes / (dms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                      "frac": dbytes / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None},
+                                      "frac": dbytes / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                      "traffic": committed_traffic("kda_rows (decode)", args.precision)},
                          "algorithmic_bytes_per_step": dbytes}
 
     if not args.no_cpu_baseline:

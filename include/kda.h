@@ -58,6 +58,7 @@ extern "C" {
 #endif
 
 typedef struct ihipStream_t* hipStream_t;
+typedef struct ihipEvent_t* hipEvent_t;
 
 enum kda_status {
   KDA_OK = 0,
@@ -195,6 +196,18 @@ int gated_rmsnorm_out(int64_t rows, int32_t d_v, const float* o, const void* z, 
 
 /* Message for the last error returned on this thread ("" if none). */
 const char* kda_last_error(void);
+
+/* kda_set_timing_events -- measurement hook for benchmarks.  Until the next
+ * call, every kda_prefill_varlen call made by this thread records events[2i]
+ * and events[2i+1] on its stream immediately before and after its kernel i,
+ * for 2i+1 < count:
+ *   i = 0 chunk table,  1 intra-chunk kernel,  2 conv-state carry (only with
+ *   `raw`; not recorded otherwise),  3 inter-chunk scan.
+ * The events are caller-owned hipEvent_t handles, already created; the library
+ * keeps only the pointer, which must stay valid while set.  count = 0 (events
+ * may be NULL) turns the hook off.  Errors: KDA_E_ARG for a negative or odd
+ * count, or NULL events with count > 0. */
+int kda_set_timing_events(hipEvent_t* events, int32_t count);
 
 #ifdef __cplusplus
 }

@@ -29,7 +29,7 @@ GATE_SOFTPLUS, GATE_SAFE = 0, 1
 ACT_NONE, ACT_SILU = 0, 1
 PREC_FP32, PREC_BF16X3, PREC_FP16 = 0, 1, 2
 EXPORTS = ("kda_prep", "kda_prefill_workspace_bytes", "kda_prefill_varlen", "kda_decode", "kda_verify_window",
-           "gated_rmsnorm_out", "kda_last_error")
+           "gated_rmsnorm_out", "kda_last_error", "kda_set_timing_events")
 
 
 class KdaError(RuntimeError):
@@ -78,7 +78,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.kda_verify_window.argtypes = [D, i32, i32, vp, vp, vp, vp, vp, Lg, Lg, vp, vp, vp, vp, vp, i32, f32, vp, vp]
         lib.gated_rmsnorm_out.argtypes = [i64, i32, vp, vp, i32, vp, f32, vp, i32, vp]
         lib.kda_last_error.restype = ctypes.c_char_p
-        for f in ("kda_prep", "kda_prefill_varlen", "kda_decode", "kda_verify_window", "gated_rmsnorm_out"):
+        lib.kda_set_timing_events.argtypes = [vp, i32]
+        for f in ("kda_prep", "kda_prefill_varlen", "kda_decode", "kda_verify_window", "gated_rmsnorm_out",
+                  "kda_set_timing_events"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -291,3 +293,30 @@ def gated_rmsnorm_out(o, z, w, eps, y):
     _need(y, "y", shape=o.shape)
     _check(lib.gated_rmsnorm_out(rows, dv, _ptr(o), _ptr(z), _dtype_code(z.dtype), _ptr(w), float(eps), _ptr(y),
                                  _dtype_code(y.dtype), _stream()))
+
+
+# kernels of one kda_prefill_varlen call, in the order the timing hook numbers them
+PREFILL_KERNELS = ("chunk_table", "chunk_intra", "prefill_conv_state", "chunk_scan")
+
+
+def kda_set_timing_events(events):
+    """Record events around each kernel of later kda_prefill_varlen calls on this
+    thread: events[2i] / events[2i+1] bracket kernel i (PREFILL_KERNELS order).
+    `events` is a sequence of torch.cuda.Event(enable_timing=True) that have
+    been recorded once (so that the HIP events exist), or None to stop.  The
+    handle array is kept alive here until the next call."""
+    global _timing_handles
+    lib = load_library()
+    if not events:
+        _check(lib.kda_set_timing_events(None, 0))
+        _timing_handles = None
+        return
+    handles = [int(e.cuda_event) for e in events]
+    if any(h == 0 for h in handles):
+        raise ValueError("record every event once before passing it (HIP events are created lazily)")
+    arr = (ctypes.c_void_p * len(handles))(*handles)
+    _check(lib.kda_set_timing_events(arr, len(handles)))
+    _timing_handles = arr
+
+
+_timing_handles = None

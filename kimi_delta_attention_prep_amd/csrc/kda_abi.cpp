@@ -15,6 +15,8 @@
 namespace {
 
 thread_local char g_err[512] = "";
+thread_local hipEvent_t* g_events = nullptr;  // measurement hook (kda_set_timing_events)
+thread_local int g_nevents = 0;
 
 int fail(int code, const char* fmt, ...) {
   va_list ap;
@@ -90,6 +92,14 @@ extern "C" {
 
 const char* kda_last_error(void) { return g_err; }
 
+int kda_set_timing_events(hipEvent_t* events, int32_t count) {
+  if (count < 0 || (count & 1)) return fail(KDA_E_ARG, "kda_set_timing_events: count must be even and >= 0");
+  if (count > 0 && !events) return fail(KDA_E_ARG, "kda_set_timing_events: NULL events");
+  g_events = count > 0 ? events : nullptr;
+  g_nevents = count > 0 ? count : 0;
+  return ok();
+}
+
 int kda_prep(const kda_dims* d, int32_t num_seqs, int64_t t_tot, const int32_t* cu_seqlens, const int32_t* slots,
              const void* q_raw, const void* k_raw, const void* v_raw, const float* conv_weight,
              const void* conv_state_in, void* conv_state_out, const void* g_raw, const void* beta_logit,
@@ -164,6 +174,7 @@ int kda_prefill_varlen(const kda_dims* d, int32_t num_seqs, int64_t t_tot, const
   L.q_hat = q_hat; L.k_hat = k_hat; L.v = v; L.g = g; L.beta = beta; L.state = state; L.o = o;
   L.workspace = workspace; L.workspace_bytes = workspace_bytes;
   L.in_dtype = d->in_dtype; L.act = d->conv_act;
+  L.events = g_events; L.nevents = g_nevents;
   if (raw) {
     L.fused = 1; L.gate_mode = raw->gate_mode; L.lb = raw->lower_bound;
     L.raw_q = raw->q_raw; L.raw_k = raw->k_raw; L.raw_v = raw->v_raw; L.raw_g = raw->g_raw;

@@ -66,6 +66,9 @@ struct PrefillLaunch {
   const float* conv_w;
   const void* cs_in;
   void* cs_out;
+  // measurement hook: events[2i], events[2i+1] around kernel i (2i+1 < nevents)
+  hipEvent_t* events;
+  int nevents;
 };
 size_t prefill_workspace_bytes(int H, int dk, int dv, int precision, int num_seqs, int64_t t_tot);
 hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t s);

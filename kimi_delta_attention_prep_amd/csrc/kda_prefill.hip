@@ -1188,8 +1188,15 @@ static hipError_t launch_prefill_t(const PrefillLaunch& Lc, hipStream_t s) {
   p.sink = reinterpret_cast<float*>(static_cast<uint8_t*>(Lc.workspace) + table_bytes(Lc.num_seqs) - 1024);
   p.recs = static_cast<uint8_t*>(Lc.workspace) + table_bytes(Lc.num_seqs);
   p.rec_bytes = rec_layout(DK, DV, Frag<POL>::BYTES).bytes;
+  // measurement hook: an event just before / after kernel i
+  auto mark = [&](int i, int end) -> hipError_t {
+    return 2 * i + 1 < Lc.nevents ? hipEventRecord(Lc.events[2 * i + end], s) : hipSuccess;
+  };
+  hipError_t e = mark(0, 0);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(256), 0, s, Lc.cu_seqlens, Lc.num_seqs, p.chunk_off);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
+  if (e == hipSuccess) e = mark(0, 1);
   if (e != hipSuccess) return e;
   const int64_t mc = max_chunks(Lc.num_seqs, Lc.t_tot);
   constexpr size_t intra_bytes = IntraSmem<DK, DV>::BYTES;
@@ -1201,26 +1208,36 @@ static hipError_t launch_prefill_t(const PrefillLaunch& Lc, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
+  e = mark(1, 0);
+  if (e != hipSuccess) return e;
   if (mc > 0 && Lc.t_tot > 0) {
     hipLaunchKernelGGL((chunk_intra_kernel<DK, DV, POL, RawT, FUSED>), dim3((unsigned)mc, (unsigned)Lc.H), dim3(512),
                        intra_bytes, s, p);
     e = hipGetLastError();
-    if (e != hipSuccess) return e;
   }
+  if (e == hipSuccess) e = mark(1, 1);
+  if (e != hipSuccess) return e;
   if constexpr (FUSED) {  // conv state written after every read of the old one (the two may alias)
     const int64_t C = (int64_t)Lc.H * (2 * DK + DV);
+    e = mark(2, 0);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((prefill_conv_state_kernel<RawT>), dim3((unsigned)((C + 255) / 256), (unsigned)Lc.num_seqs),
                        dim3(256), 0, s, p, DK, DV);
     e = hipGetLastError();
+    if (e == hipSuccess) e = mark(2, 1);
     if (e != hipSuccess) return e;
   }
   const int groups = Lc.num_seqs * Lc.H;
+  e = mark(3, 0);
+  if (e != hipSuccess) return e;
   if (groups > 0) {
     const int nsplit = DV / 16;
     const int wgs = (groups + 7) / 8 * 8 * nsplit;
     hipLaunchKernelGGL((chunk_scan_kernel<DK, DV, POL>), dim3((unsigned)wgs), dim3(512), scan_bytes, s, p, groups);
+    e = hipGetLastError();
   }
-  return hipGetLastError();
+  if (e == hipSuccess) e = mark(3, 1);
+  return e;
 }
 
 template <int DK, int DV, int POL>

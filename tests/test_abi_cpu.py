@@ -131,3 +131,12 @@ def test_binding_has_no_fallback(tmp_path, monkeypatch):
     monkeypatch.setattr(K, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         K.load_library(str(tmp_path / "nope.so"))
+
+
+def test_timing_hook_checks(lib):
+    arr = (ctypes.c_void_p * 2)(0x10000, 0x10000)  # never used: no prompt call follows while set
+    assert lib.kda_set_timing_events(arr, -2) == K.KDA_E_ARG
+    assert lib.kda_set_timing_events(arr, 3) == K.KDA_E_ARG
+    assert lib.kda_set_timing_events(None, 2) == K.KDA_E_ARG
+    assert lib.kda_set_timing_events(arr, 2) == K.KDA_OK
+    assert lib.kda_set_timing_events(None, 0) == K.KDA_OK
