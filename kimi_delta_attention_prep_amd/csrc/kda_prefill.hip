@@ -308,6 +308,7 @@ struct RawRowsArgs {
   void* cs_out;
   int act, gate_mode;
   float lb;
+  int esize;  // bytes per raw element; 0 without raw rows (nothing to carry)
 };
 
 struct PrefillArgs {
@@ -939,60 +940,52 @@ __global__ __launch_bounds__(512) void chunk_intra_kernel(PrefillArgs p) {
 // ---------------------------------------------------------------------------
 // inter-chunk scan
 //
-// Workgroup = (sequence, head, 16 state columns j0..j0+15), 8 wavefronts in
-// two roles.  The four state wavefronts carry the sequential chain; state
-// wavefront w owns chunk rows 16w..16w+15 of U and state rows
-// 16*(w*DK/64 + s) + 0..15 (s < DK/64) as fp32 matrix-core accumulators:
-//   U_c = U~_c - W_c S_c          (B operand: S_c^T slice from LDS)
-//   S_{c+1} = gamma_L . S_c + K_<^T U_c
-// The four output wavefronts trail by one chunk, off the critical path:
-//   O_{c-1} = Q^gamma S_{c-1} + P U_{c-1}
-// S^T and U^T slices double-buffer in LDS; every chunk takes two workgroup
-// barriers.  Each role keeps NS register sets of operand fragments (two to
-// four, as registers allow) and loads chunk c+NS-1 while chunk c computes.
+// Workgroup = (sequence, head, 16 state columns j0..j0+15), 4 wavefronts.
+// Wavefront w owns chunk rows 16w..16w+15 of U and O and state rows
+// 16*(w*DK/64 + s) + 0..15 (s < DK/64), kept as fp32 matrix-core accumulators.
+// Per chunk c, with S_c^T and U_c^T slices shared through LDS:
+//   phase 1 (S_c complete):  U_c = U~_c - W_c S_c,  O_c = Q^gamma_c S_c   (one read of S_c^T)
+//   phase 2 (U_c complete):  S_{c+1} = gamma_L . S_c + K_<^T U_c,  O_c += P_c U_c   (one read of U_c^T)
+// Phase 1 reads S^T and writes U^T; phase 2 reads U^T and writes S^T; the two
+// barriers per chunk order every write after the last read of the old
+// contents, so one buffer of each suffices.  Each wavefront keeps NS register
+// sets of its operand fragments and loads chunk c+NS-1 while chunk c computes.
 // ---------------------------------------------------------------------------
-// LDS of the scan: S^T and U^T slices, double-buffered, stored as the B-operand
-// planes of the policy (element (column j, K index k) at plane[j * stride + k]).
 template <int DK, int POL>
 struct ScanSmem {
   using P = typename Frag<POL>::P;
   static constexpr int NP = Frag<POL>::PLANES;
-  static constexpr int PS = DK + 16 / sizeof(P);  // S^T row stride (16 rows = the slice's columns)
+  static constexpr int PS = DK + 16 / sizeof(P);  // S^T row stride (one row per state column)
   static constexpr int PU = 64 + 16 / sizeof(P);  // U^T row stride
   static constexpr int S_PLANE = 16 * PS, U_PLANE = 16 * PU;
-  static constexpr int S_BUF = NP * S_PLANE, U_BUF = NP * U_PLANE;
-  static constexpr size_t BYTES = (size_t)(2 * S_BUF + 2 * U_BUF) * sizeof(P);
+  static constexpr size_t BYTES = (size_t)(NP * S_PLANE + NP * U_PLANE) * sizeof(P);
 };
 
+// one chunk's operand fragments of one wavefront
 template <int DK, int POL>
-struct StateFrags {
+struct ScanFrags {
   using F = Frag<POL>;
   static constexpr int KB = DK / 32, MS = DK / 64;
-  typename F::A w[KB], k[MS][2];
+  typename F::A w[KB], q[KB], k[MS][2], pp[2];
   floatx4 ut;
   float4 gl[MS];
-  __device__ void load(const uint8_t* rec, const RecLayout& rl, int w4, int lane, int split) {
+  // the state chain's operands (W, U~, K_<^T, gamma_L)
+  __device__ void load_state(const uint8_t* rec, const RecLayout& rl, int w4, int lane, int split) {
     constexpr int FB = F::BYTES;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) w[kb] = F::load_a(rec + rl.Wf + ((int64_t)(w4 * KB + kb) * 64 + lane) * FB);
+    ut = *reinterpret_cast<const floatx4*>(rec + rl.Ut + ((int64_t)(split * 4 + w4) * 64 + lane) * 16);
 #pragma unroll
     for (int s = 0; s < MS; ++s)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
         k[s][kb] = F::load_a(rec + rl.Kf + ((int64_t)((w4 * MS + s) * 2 + kb) * 64 + lane) * FB);
-    ut = *reinterpret_cast<const floatx4*>(rec + rl.Ut + ((int64_t)(split * 4 + w4) * 64 + lane) * 16);
 #pragma unroll
     for (int s = 0; s < MS; ++s)
       gl[s] = *reinterpret_cast<const float4*>(rec + rl.gL + (int64_t)(16 * (w4 * MS + s) + 4 * (lane >> 4)) * 4);
   }
-};
-
-template <int DK, int POL>
-struct OutFrags {
-  using F = Frag<POL>;
-  static constexpr int KB = DK / 32;
-  typename F::A q[KB], pp[2];
-  __device__ void load(const uint8_t* rec, const RecLayout& rl, int w4, int lane) {
+  // the output's operands (Q^gamma, P)
+  __device__ void load_out(const uint8_t* rec, const RecLayout& rl, int w4, int lane) {
     constexpr int FB = F::BYTES;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) q[kb] = F::load_a(rec + rl.Qf + ((int64_t)(w4 * KB + kb) * 64 + lane) * FB);
@@ -1001,15 +994,53 @@ struct OutFrags {
   }
 };
 
+// Conv-state carry of a prompt pass with raw rows: conv_state_out[slot][r][c]
+// = raw row (len - 3 + r) of channel c, reaching back into conv_state_in for
+// sequences shorter than 3 rows.  Runs after every read of the old conv state
+// (the intra-chunk kernel is done), so the two may be one buffer; the channels
+// of a sequence are spread over its nwg scan workgroups, and each thread writes
+// rows r = 0, 1, 2 of its channel in order (with in == out, row r reads old row
+// r + len >= r, so nothing is overwritten before it is read).
+template <typename E>
+__device__ __forceinline__ void carry_rows(const PrefillArgs& p, int n, int slot, int64_t c, int64_t C, int64_t qk,
+                                           int64_t vw) {
+  const int64_t t0 = p.cu[n], len = (int64_t)p.cu[n + 1] - t0;
+  const E* in = static_cast<const E*>(p.raw.cs_in) + (int64_t)slot * 3 * C;
+  E* out = static_cast<E*>(p.raw.cs_out) + (int64_t)slot * 3 * C;
+  for (int r = 0; r < 3; ++r) {
+    const int64_t pos = len - 3 + r;
+    E x;
+    if (pos >= 0) {
+      const int64_t row = t0 + pos;
+      if (c < qk) x = static_cast<const E*>(p.raw.q)[row * qk + c];
+      else if (c < 2 * qk) x = static_cast<const E*>(p.raw.k)[row * qk + (c - qk)];
+      else x = static_cast<const E*>(p.raw.v)[row * vw + (c - 2 * qk)];
+    } else {
+      x = in[(3 + pos) * C + c];
+    }
+    out[r * C + c] = x;
+  }
+}
+template <int DK, int DV>
+__device__ __forceinline__ void carry_conv_state(const PrefillArgs& p, int n, int slot, int wid, int nwg) {
+  const int64_t C = (int64_t)p.H * (2 * DK + DV), qk = (int64_t)p.H * DK, vw = (int64_t)p.H * DV;
+  const int64_t per = (C + nwg - 1) / nwg;
+  for (int64_t e = threadIdx.x; e < per; e += blockDim.x) {
+    const int64_t c = wid * per + e;
+    if (c >= C) break;
+    if (p.raw.esize == 2) carry_rows<uint16_t>(p, n, slot, c, C, qk, vw);
+    else carry_rows<uint32_t>(p, n, slot, c, C, qk, vw);
+  }
+}
+
 template <int DK, int DV, int POL>
-__global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillArgs p, int groups) {
+__global__ __launch_bounds__(256) void chunk_scan_kernel(PrefillArgs p, int groups) {
   using SM = ScanSmem<DK, POL>;
   using F = Frag<POL>;
   using P = typename F::P;
   constexpr int L = kChunk, PS = SM::PS, PU = SM::PU;
   constexpr int NSPLIT = DV / 16, KB = DK / 32, MS = DK / 64;
-  // register sets of operand fragments per role: chunk c+NS-1 loads while chunk c computes
-  constexpr int NS = F::BYTES == 16 ? 4 : (DK == 64 ? 3 : 2);
+  constexpr int NS = F::BYTES == 16 ? 3 : 2;  // register sets of operand fragments
   extern __shared__ __align__(16) float smem_f[];
   P* smem = reinterpret_cast<P*>(smem_f);
 
@@ -1021,169 +1052,122 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillArgs p, int grou
   const int H = p.H, n_seq = grp / H, h = grp % H;
   const int slot = p.slots ? p.slots[n_seq] : n_seq;
   if (slot < 0) return;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const bool is_state = wave < 4;
-  const int w4 = wave & 3, col = lane & 15, g4 = lane >> 4;
+  const int t = threadIdx.x, lane = t & 63, w4 = t >> 6;
+  const int col = lane & 15, g4 = lane >> 4;
   const int j0 = 16 * split;
+  if (p.raw.esize) carry_conv_state<DK, DV>(p, n_seq, slot, h * NSPLIT + split, H * NSPLIT);
   const RecLayout rl = rec_layout(DK, DV, F::BYTES);
   float* Sg = p.state + ((int64_t)slot * H + h) * DK * DV;
-  // plane pointers of buffer b; "store" helpers take the rows 4*g4.. of column col
-  auto sS = [&](int b, int plane) { return smem + b * SM::S_BUF + plane * SM::S_PLANE; };
-  auto sU = [&](int b, int plane) { return smem + 2 * SM::S_BUF + b * SM::U_BUF + plane * SM::U_PLANE; };
-  auto put_s = [&](int b, int row0, const floatx4& x) {
-    F::store_b4(sS(b, 0) + col * PS + row0, sS(b, SM::NP - 1) + col * PS + row0, x);
-  };
-  auto put_u = [&](int b, int row0, const floatx4& x) {
-    F::store_b4(sU(b, 0) + col * PU + row0, sU(b, SM::NP - 1) + col * PU + row0, x);
-  };
-  auto get_s = [&](int b, int kb) { return F::load_b(sS(b, 0) + col * PS + 32 * kb, sS(b, SM::NP - 1) + col * PS + 32 * kb, g4); };
-  auto get_u = [&](int b, int kb) { return F::load_b(sU(b, 0) + col * PU + 32 * kb, sU(b, SM::NP - 1) + col * PU + 32 * kb, g4); };
+  P* sS0 = smem;
+  P* sS1 = smem + (SM::NP - 1) * SM::S_PLANE;
+  P* sU0 = smem + SM::NP * SM::S_PLANE;
+  P* sU1 = sU0 + (SM::NP - 1) * SM::U_PLANE;
+  auto put_s = [&](int row0, const floatx4& x) { F::store_b4(sS0 + col * PS + row0, sS1 + col * PS + row0, x); };
+  auto put_u = [&](int row0, const floatx4& x) { F::store_b4(sU0 + col * PU + row0, sU1 + col * PU + row0, x); };
+  auto get_s = [&](int kb) { return F::load_b(sS0 + col * PS + 32 * kb, sS1 + col * PS + 32 * kb, g4); };
+  auto get_u = [&](int kb) { return F::load_b(sU0 + col * PU + 32 * kb, sU1 + col * PU + 32 * kb, g4); };
 
   floatx4 Sacc[MS];
-  if (is_state) {
 #pragma unroll
-    for (int s = 0; s < MS; ++s) {
-      const int r0 = 16 * (w4 * MS + s) + 4 * g4;
+  for (int s = 0; s < MS; ++s) {
+    const int r0 = 16 * (w4 * MS + s) + 4 * g4;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) Sacc[s][v] = Sg[(int64_t)(r0 + v) * DV + j0 + col];
-      put_s(0, r0, Sacc[s]);
-    }
+    for (int v = 0; v < 4; ++v) Sacc[s][v] = Sg[(int64_t)(r0 + v) * DV + j0 + col];
+    put_s(r0, Sacc[s]);
   }
 
   const int c_begin = p.chunk_off[n_seq], n = p.chunk_off[n_seq + 1] - c_begin;
   const int64_t seq_start = p.cu[n_seq], seq_end = p.cu[n_seq + 1];
   auto rec_of = [&](int i) { return p.recs + ((int64_t)(c_begin + i) * H + h) * p.rec_bytes; };
 
-  // Iteration i (0..n): the state role takes chunk i (register set i % 3), the
-  // output role chunk i-1.  Both roles run n+1 iterations of two barriers each.
-  if (is_state) {
-    StateFrags<DK, POL> sf[NS];
-    // Every load below is unconditional (indices clamped to the last chunk), so
-    // the compiler can count outstanding loads exactly and wait only for the
-    // set a chunk needs.
-    auto clampc = [&](int j) { return j < n ? j : n - 1; };
-    if (n > 0) {
+  ScanFrags<DK, POL> fr[NS];
+  // Every load is unconditional (indices clamped to the last chunk), so the
+  // compiler can count outstanding loads exactly and wait only for the set a
+  // chunk needs.
+  auto clampc = [&](int j) { return j < n ? j : n - 1; };
+  if (n > 0) {
 #pragma unroll
-      for (int j = 0; j < NS - 1; ++j) sf[j].load(rec_of(clampc(j)), rl, w4, lane, split);
+    for (int j = 0; j < NS - 1; ++j) {
+      fr[j].load_state(rec_of(clampc(j)), rl, w4, lane, split);
+      fr[j].load_out(rec_of(clampc(j)), rl, w4, lane);
     }
-    auto iter = [&](int i, const StateFrags<DK, POL>& cur, StateFrags<DK, POL>& ahead) {
-      const int bi = i & 1, bp = (i + 1) & 1;
-      __syncthreads();  // S^T_i complete; every read of the buffers rewritten below is done
-      ahead.load(rec_of(clampc(i + NS - 1)), rl, w4, lane, split);
-      if (i < n) {
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  }
+  // Accumulation chains are split in two (even and odd K blocks, or the two
+  // halves of a sum) and the independent chains are interleaved, so the matrix
+  // cores always have a product to issue while a chain waits on its last one.
+  auto iter = [&](int c, const ScanFrags<DK, POL>& cur, ScanFrags<DK, POL>& ahead) {
+    __syncthreads();  // S_c^T complete; the last chunk's reads of U^T are done
+    typename F::B bs[KB];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) acc = F::mma(acc, cur.w[kb], get_s(bi, kb));
-        floatx4 u;
+    for (int kb = 0; kb < KB; ++kb) bs[kb] = get_s(kb);
+    const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
+    floatx4 acc[2] = {z4, z4}, ao[2] = {z4, z4};
 #pragma unroll
-        for (int v = 0; v < 4; ++v) u[v] = cur.ut[v] - acc[v];
-        put_u(bi, 16 * w4 + 4 * g4, u);
-      }
-      __syncthreads();  // U^T_i complete
-      if (i < n) {
-        const typename F::B u0 = get_u(bi, 0), u1 = get_u(bi, 1);
-#pragma unroll
-        for (int s = 0; s < MS; ++s) {
-          const float4 gl = cur.gl[s];
-          Sacc[s][0] *= gl.x; Sacc[s][1] *= gl.y; Sacc[s][2] *= gl.z; Sacc[s][3] *= gl.w;
-          Sacc[s] = F::mma(Sacc[s], cur.k[s][0], u0);
-          Sacc[s] = F::mma(Sacc[s], cur.k[s][1], u1);
-          put_s(bp, 16 * (w4 * MS + s) + 4 * g4, Sacc[s]);
-        }
-      }
-    };
-    // n+1 iterations rounded up to a multiple of NS (the output role trails by one chunk)
-    const int iters = n > 0 ? (n + NS) / NS * NS : 0;
-    for (int base = 0; base < iters; base += NS) {
-#pragma unroll
-      for (int u = 0; u < NS; ++u) iter(base + u, sf[u], sf[(u + NS - 1) % NS]);
+    for (int kb = 0; kb < KB; ++kb) {
+      acc[kb & 1] = F::mma(acc[kb & 1], cur.w[kb], bs[kb]);
+      ao[kb & 1] = F::mma(ao[kb & 1], cur.q[kb], bs[kb]);
     }
+    floatx4 u;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) u[v] = cur.ut[v] - (acc[0][v] + acc[1][v]);
+    put_u(16 * w4 + 4 * g4, u);
+    ahead.load_state(rec_of(clampc(c + NS - 1)), rl, w4, lane, split);
+    __syncthreads();  // U_c^T complete; every read of S_c^T is done
+    const typename F::B u0 = get_u(0), u1 = get_u(1);
+    floatx4 sk[MS];
 #pragma unroll
     for (int s = 0; s < MS; ++s) {
-      const int r0 = 16 * (w4 * MS + s) + 4 * g4;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) Sg[(int64_t)(r0 + v) * DV + j0 + col] = Sacc[s][v];
+      const float4 gl = cur.gl[s];
+      Sacc[s][0] *= gl.x; Sacc[s][1] *= gl.y; Sacc[s][2] *= gl.z; Sacc[s][3] *= gl.w;
+      Sacc[s] = F::mma(Sacc[s], cur.k[s][0], u0);
+      sk[s] = F::mma(z4, cur.k[s][1], u1);
     }
-  } else {
-    OutFrags<DK, POL> of[NS];
-    auto clampc = [&](int j) { return j < n ? j : n - 1; };
-    if (n > 0) {
+    // P is lower triangular: row block w4 needs chunk rows < 16(w4+1)
+    ao[0] = F::mma(ao[0], cur.pp[0], u0);
+    if (w4 >= 2) ao[1] = F::mma(ao[1], cur.pp[1], u1);
 #pragma unroll
-      for (int j = 0; j < NS - 2; ++j) of[j].load(rec_of(clampc(j)), rl, w4, lane);
+    for (int s = 0; s < MS; ++s) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) Sacc[s][v] += sk[s][v];
+      put_s(16 * (w4 * MS + s) + 4 * g4, Sacc[s]);
     }
-    auto iter = [&](int i, const OutFrags<DK, POL>& prev, OutFrags<DK, POL>& next) {
-      const int bp = (i + 1) & 1;  // LDS buffers of chunk i-1
-      floatx4 ao = {0.f, 0.f, 0.f, 0.f};
-      __syncthreads();
-      next.load(rec_of(clampc(i + NS - 2)), rl, w4, lane);
-      const bool live = i >= 1 && i <= n;
-      if (live) {
+    ahead.load_out(rec_of(clampc(c + NS - 1)), rl, w4, lane);
+    const int64_t start = seq_start + (int64_t)c * L;
+    const int len = (int)min((int64_t)L, seq_end - start);
+    // stores are unconditional: rows past the sequence go to the sink
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) ao = F::mma(ao, prev.q[kb], get_s(bp, kb));
-      }
-      __syncthreads();
-      if (live) {
-        // P is lower triangular: row block w4 needs chunk rows < 16(w4+1)
-        ao = F::mma(ao, prev.pp[0], get_u(bp, 0));
-        if (w4 >= 2) ao = F::mma(ao, prev.pp[1], get_u(bp, 1));
-      }
-      // stores are unconditional: rows past the sequence (or iterations without a chunk) go to the sink
-      const int64_t start = seq_start + (int64_t)(i - 1) * L;
-      const int len = live ? (int)min((int64_t)L, seq_end - start) : 0;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int rr = 16 * w4 + 4 * g4 + v;
-        float* dst = rr < len ? &p.o[((start + rr) * H + h) * DV + j0 + col] : &p.sink[lane * 4 + v];
-        *dst = ao[v];
-      }
-    };
-    const int iters = n > 0 ? (n + NS) / NS * NS : 0;
-    for (int base = 0; base < iters; base += NS) {
-#pragma unroll
-      for (int u = 0; u < NS; ++u) iter(base + u, of[(u + NS - 1) % NS], of[(u + NS - 2) % NS]);
+    for (int v = 0; v < 4; ++v) {
+      const int rr = 16 * w4 + 4 * g4 + v;
+      float* dst = rr < len ? &p.o[((start + rr) * H + h) * DV + j0 + col] : &p.sink[lane * 4 + v];
+      *dst = ao[0][v] + ao[1][v];
     }
+  };
+  const int full = n / NS * NS;
+  for (int base = 0; base < full; base += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) iter(base + u, fr[u], fr[(u + NS - 1) % NS]);
+  }
+#pragma unroll
+  for (int u = 0; u < NS - 1; ++u)
+    if (full + u < n) iter(full + u, fr[u], fr[(u + NS - 1) % NS]);
+#pragma unroll
+  for (int s = 0; s < MS; ++s) {
+    const int r0 = 16 * (w4 * MS + s) + 4 * g4;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) Sg[(int64_t)(r0 + v) * DV + j0 + col] = Sacc[s][v];
   }
 }
 
 // ---------------------------------------------------------------------------
 // host launch
 // ---------------------------------------------------------------------------
-template <typename RawT>
-__global__ __launch_bounds__(256) void prefill_conv_state_kernel(PrefillArgs p, int DK, int DV) {
-  // carried conv state after a fused prompt pass: the last 3 raw rows of each sequence
-  // (reaching back into the old conv state for short ones); same order rule as the preamble's
-  const int n = blockIdx.y;
-  const int64_t C = (int64_t)p.H * (2 * DK + DV);
-  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (c >= C) return;
-  const int slot = p.slots ? p.slots[n] : n;
-  if (slot < 0) return;
-  const int64_t t0 = p.cu[n], len = (int64_t)p.cu[n + 1] - t0;
-  const int64_t qk = (int64_t)p.H * DK;
-  const RawT* in = static_cast<const RawT*>(p.raw.cs_in) + (int64_t)slot * 3 * C;
-  RawT* out = static_cast<RawT*>(p.raw.cs_out) + (int64_t)slot * 3 * C;
-  for (int r = 0; r < 3; ++r) {
-    const int64_t pos = len - 3 + r;
-    RawT x;
-    if (pos >= 0) {
-      const int64_t row = t0 + pos;
-      if (c < qk) x = static_cast<const RawT*>(p.raw.q)[row * qk + c];
-      else if (c < 2 * qk) x = static_cast<const RawT*>(p.raw.k)[row * qk + (c - qk)];
-      else x = static_cast<const RawT*>(p.raw.v)[row * (int64_t)p.H * DV + (c - 2 * qk)];
-    } else {
-      x = in[(3 + pos) * C + c];
-    }
-    out[r * C + c] = x;
-  }
-}
-
 template <int DK, int DV, int POL, typename RawT, bool FUSED>
 static hipError_t launch_prefill_t(const PrefillLaunch& Lc, hipStream_t s) {
   PrefillArgs p;
   p.H = Lc.H; p.num_seqs = Lc.num_seqs; p.cu = Lc.cu_seqlens; p.slots = Lc.slots;
   p.q = Lc.q_hat; p.k = Lc.k_hat; p.v = Lc.v; p.g = Lc.g; p.beta = Lc.beta; p.state = Lc.state; p.o = Lc.o;
   p.raw = {Lc.raw_q, Lc.raw_k, Lc.raw_v, Lc.raw_g, Lc.raw_beta, Lc.conv_w, Lc.cs_in, Lc.cs_out,
-           Lc.act, Lc.gate_mode, Lc.lb};
+           Lc.act, Lc.gate_mode, Lc.lb, FUSED ? (int)sizeof(RawT) : 0};
   p.chunk_off = static_cast<int32_t*>(Lc.workspace);
   p.sink = reinterpret_cast<float*>(static_cast<uint8_t*>(Lc.workspace) + table_bytes(Lc.num_seqs) - 1024);
   p.recs = static_cast<uint8_t*>(Lc.workspace) + table_bytes(Lc.num_seqs);
@@ -1217,26 +1201,17 @@ static hipError_t launch_prefill_t(const PrefillLaunch& Lc, hipStream_t s) {
   }
   if (e == hipSuccess) e = mark(1, 1);
   if (e != hipSuccess) return e;
-  if constexpr (FUSED) {  // conv state written after every read of the old one (the two may alias)
-    const int64_t C = (int64_t)Lc.H * (2 * DK + DV);
-    e = mark(2, 0);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prefill_conv_state_kernel<RawT>), dim3((unsigned)((C + 255) / 256), (unsigned)Lc.num_seqs),
-                       dim3(256), 0, s, p, DK, DV);
-    e = hipGetLastError();
-    if (e == hipSuccess) e = mark(2, 1);
-    if (e != hipSuccess) return e;
-  }
+  // (the conv-state carry of a fused call runs inside the scan kernel)
   const int groups = Lc.num_seqs * Lc.H;
-  e = mark(3, 0);
+  e = mark(2, 0);
   if (e != hipSuccess) return e;
   if (groups > 0) {
     const int nsplit = DV / 16;
     const int wgs = (groups + 7) / 8 * 8 * nsplit;
-    hipLaunchKernelGGL((chunk_scan_kernel<DK, DV, POL>), dim3((unsigned)wgs), dim3(512), scan_bytes, s, p, groups);
+    hipLaunchKernelGGL((chunk_scan_kernel<DK, DV, POL>), dim3((unsigned)wgs), dim3(256), scan_bytes, s, p, groups);
     e = hipGetLastError();
   }
-  if (e == hipSuccess) e = mark(3, 1);
+  if (e == hipSuccess) e = mark(2, 1);
   return e;
 }
 
