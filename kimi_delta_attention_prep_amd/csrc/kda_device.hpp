@@ -111,6 +111,16 @@ __device__ __forceinline__ void conv_rows(TAP tap, const float* __restrict__ w, 
   else conv_rows_t<D, NORM, NR, false>(tap, w, out);
 }
 
+// 16-byte state accesses marked non-temporal: every state tile is read once and
+// written once per call, and the state pool is larger than the caches
+__device__ __forceinline__ float4 load_nt4(const float* p) {
+  const floatx4 x = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(p));
+  return make_float4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ void store_nt4(float* p, const float4& v) {
+  __builtin_nontemporal_store(floatx4{v.x, v.y, v.z, v.w}, reinterpret_cast<floatx4*>(p));
+}
+
 // one state element's step: S' = a * S, then S = S' + k * u (explicit fma).
 // decode, verify windows and the commit replay all use exactly this.
 __device__ __forceinline__ float decay(float s, float a) { return a * s; }

@@ -768,14 +768,18 @@ __global__ __launch_bounds__(512) void chunk_intra_kernel(PrefillArgs p) {
   for (int idx = t; idx < L * L; idx += NT) sXi[(idx / L) * PL + idx % L] = 0.f;
   __syncthreads();
   if (t < L) {  // diagonal blocks by forward substitution, one column per thread
+    // right-looking: once x_r is final, every later row takes its term at once,
+    // so the dependent chain is 16 steps long
     const int R = t / 16, cc = t % 16, b0 = 16 * R;
     float xv[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float sacc = (r == cc) ? 1.f : 0.f;
+    for (int r = 0; r < 16; ++r) xv[r] = (r == cc) ? 1.f : 0.f;
 #pragma unroll
-      for (int i = 0; i < r; ++i) sacc = fmaf(-sA[(b0 + r) * PL + b0 + i], xv[i], sacc);
-      xv[r] = (r >= cc) ? sacc : 0.f;
+    for (int r = 0; r < 16; ++r) {
+      const float x = (r >= cc) ? xv[r] : 0.f;
+      xv[r] = x;
+#pragma unroll
+      for (int i = r + 1; i < 16; ++i) xv[i] = fmaf(-sA[(b0 + i) * PL + b0 + r], x, xv[i]);
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) sXi[(b0 + r) * PL + b0 + cc] = xv[r];

@@ -198,12 +198,12 @@ __global__ __launch_bounds__(256) void kda_rows_kernel(RowsArgs<RawT> p) {
   __shared__ float s_scal[4];
   RowStep<DK, DV, RawT> rs{s_q, s_k, s_v, s_a, s_red, s_pk, s_pq, s_scal};
 
-  // 1. issue the state loads first (64 KB per head at d=128)
+  // 1. issue the state loads first (64 KB per head at d=128), non-temporal
   float* Sg = p.state + ((int64_t)slot * H + h) * DK * DV;
   float4 S[SH::RPT];
 #pragma unroll
   for (int m = 0; m < SH::RPT; ++m)
-    S[m] = *reinterpret_cast<const float4*>(Sg + (int64_t)(rg + SH::RG * m) * DV + 4 * cg);
+    S[m] = load_nt4(Sg + (int64_t)(rg + SH::RG * m) * DV + 4 * cg);
 
   // 2. conv weights and carried conv rows of the channels this thread owns
   ChanHist<RawT> ch;
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(256) void kda_rows_kernel(RowsArgs<RawT> p) {
     if (nc > 0) {
 #pragma unroll
       for (int m = 0; m < SH::RPT; ++m)
-        *reinterpret_cast<float4*>(Sg + (int64_t)(rg + SH::RG * m) * DV + 4 * cg) = S[m];
+        store_nt4(Sg + (int64_t)(rg + SH::RG * m) * DV + 4 * cg, S[m]);
       if (cq_ch >= 0)
         for (int r = 0; r < 3; ++r) cs[r * C + cq_ch] = ch.hq[r];
       if (ck_ch >= 0)
@@ -289,7 +289,7 @@ __global__ __launch_bounds__(256) void kda_rows_kernel(RowsArgs<RawT> p) {
     rs.step(S, qk, u, o);
 #pragma unroll
     for (int m = 0; m < SH::RPT; ++m)
-      *reinterpret_cast<float4*>(Sg + (int64_t)(rg + SH::RG * m) * DV + 4 * cg) = S[m];
+      store_nt4(Sg + (int64_t)(rg + SH::RG * m) * DV + 4 * cg, S[m]);
     if (rg == 0) *reinterpret_cast<float4*>(p.o + row_h * DV + 4 * cg) = o;
     if (cq_ch >= 0)
       for (int r = 0; r < 3; ++r) cs[r * C + cq_ch] = ch.hq[r];
