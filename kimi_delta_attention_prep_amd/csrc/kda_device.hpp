@@ -52,13 +52,30 @@ __device__ __forceinline__ float conv4_act(float w0, float w1, float w2, float w
   return act ? conv4<true>(w0, w1, w2, w3, x0, x1, x2, x3) : conv4<false>(w0, w1, w2, w3, x0, x1, x2, x3);
 }
 
-// sum over the 64 lanes of a wavefront (xor butterfly: at every step both
-// partners add the same two values, so all lanes end with identical bits)
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+// Sum over the 64 lanes of a wavefront, in registers: DPP within each 16-lane
+// row (pairs lane^1, lane^2, then the mirrored half-rows and rows), then the
+// four row sums read as uniform values and added in a fixed order.  At every
+// DPP step each lane adds its own value and its partner's, and fp addition is
+// commutative bit for bit, so all lanes end with identical bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_partner(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp_partner<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_partner<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_partner<0x141>(x);  // row_half_mirror
+  x += dpp_partner<0x140>(x);  // row_mirror
   return x;
 }
+__device__ __forceinline__ float lane_value(float x, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
+// x holds its 16-lane row's sum in every lane of the row
+__device__ __forceinline__ float rows_total(float x) {
+  return (lane_value(x, 0) + lane_value(x, 16)) + (lane_value(x, 32) + lane_value(x, 48));
+}
+__device__ __forceinline__ float wave_sum(float x) { return rows_total(row_sum16(x)); }
 
 // NR rows (of one head and stream) of the prompt preamble, computed by a whole
 // wavefront: lane l owns channels E*l .. E*l+E-1 (E = D/64) of every row.
@@ -92,9 +109,9 @@ __device__ __forceinline__ void conv_rows_t(TAP tap, const float* __restrict__ w
   }
   if constexpr (NORM) {  // wave_sum of every row, side by side
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
+    for (int rr = 0; rr < NR; ++rr) ss[rr] = row_sum16(ss[rr]);
 #pragma unroll
-      for (int rr = 0; rr < NR; ++rr) ss[rr] += __shfl_xor(ss[rr], off, 64);
+    for (int rr = 0; rr < NR; ++rr) ss[rr] = rows_total(ss[rr]);
 #pragma unroll
     for (int rr = 0; rr < NR; ++rr) {
       const float r = 1.0f / sqrtf(ss[rr] + kL2Eps);

@@ -394,8 +394,10 @@ struct IntraSmem {
   static constexpr int TA = T2 + L * PK;      // A                                   [L][PL]
   static constexpr int TP = TA + L * PL;      // P, then X                           [L][PL]
   static constexpr int TB = TP + L * PL;      // beta                                [L]
-  static constexpr int TGF = TB + L;          // G_{16R} from the chunk start        [4][DK]
-  static constexpr int TX = TGF + 4 * DK;     // G_last - G_{16I}                    [4][DK]
+  static constexpr int TGF = TB + L;          // G_{16R} from the chunk start; pivoted
+                                              // path: then e^{G_{16R}}              [4][DK]
+  static constexpr int TX = TGF + 4 * DK;     // G_last - G_{16I}; pivoted path: then
+                                              // the K_<^T factor of block I          [4][DK]
   static constexpr int TD = TX + 4 * DK;      // e^{G_{16R} - G_{16I+16}}, I + 1 < R  [6][DK]
   static constexpr int TG0 = TD + 6 * DK;     // g at each block's first row, then
                                               // T_I = G_{16I+16} - G_{16I}            [4][DK]
@@ -582,9 +584,13 @@ __global__ __launch_bounds__(512) void chunk_intra_kernel(PrefillArgs p) {
     for (int i = 0; i < NGK; ++i) {
       const int idx = t + i * NT, r = idx / (DK / VE), c0 = (idx % (DK / VE)) * VE;
       if (idx < L * (DK / VE)) {
+        float gv[VE];
 #pragma unroll
         for (int e = 0; e < VE; ++e)
-          sG[r * PK + c0 + e] = r < len ? log_decay(piece_elem<RawT>(xg[i], e), p.raw.gate_mode, p.raw.lb) : 0.f;
+          gv[e] = r < len ? log_decay(piece_elem<RawT>(xg[i], e), p.raw.gate_mode, p.raw.lb) : 0.f;
+#pragma unroll
+        for (int e = 0; e < VE; e += 4)
+          *reinterpret_cast<float4*>(&sG[r * PK + c0 + e]) = make_float4(gv[e], gv[e + 1], gv[e + 2], gv[e + 3]);
       }
     }
     if (t < L) sBeta[t] = t < len ? sigmoid(braw) : 0.f;
@@ -656,14 +662,17 @@ __global__ __launch_bounds__(512) void chunk_intra_kernel(PrefillArgs p) {
   __syncthreads();
   const bool exact = sFlag[0] != 0;
 
-  // 4. operand fragments of Q^gamma = e^{G_r} q_r and K_<^T (e^{G_last - G_i} k_i), from q, k and gl
-  write_afrags<POL, NT>(rec + rl.Qf, 4, DK / 32, [&](int r, int d) {
-    return sQ[r * PK + d] * pexp<POL>(sGF[(r / 16) * DK + d] + sG[r * PK + d]);
-  });
-  write_afrags<POL, NT>(rec + rl.Kf, DK / 16, 2, [&](int d, int r) {
-    return sK[r * PK + d] * pexp<POL>(sX[(r / 16) * DK + d] - sG[r * PK + d]);
-  });
-  __syncthreads();
+  // 4. exact path: operand fragments of Q^gamma = e^{G_r} q_r and K_<^T (e^{G_last - G_i} k_i),
+  //    one exponential per element (the pivoted path forms them from its factors in step 5)
+  if (exact) {
+    write_afrags<POL, NT>(rec + rl.Qf, 4, DK / 32, [&](int r, int d) {
+      return sQ[r * PK + d] * pexp<POL>(sGF[(r / 16) * DK + d] + sG[r * PK + d]);
+    });
+    write_afrags<POL, NT>(rec + rl.Kf, DK / 16, 2, [&](int d, int r) {
+      return sK[r * PK + d] * pexp<POL>(sX[(r / 16) * DK + d] - sG[r * PK + d]);
+    });
+    __syncthreads();
+  }
 
   // 5. A and P.  Per block pair (R, I <= R), with pivots at the blocks' first rows:
   //      A_ri = b_r sum_d [k_r e^{gl_r}] E_RI [k_i e^{T_I - gl_i}]     (I < R)
@@ -675,8 +684,21 @@ __global__ __launch_bounds__(512) void chunk_intra_kernel(PrefillArgs p) {
   //    T0 = k e^{gl}, T1 = q e^{gl}, T2 = k e^{-gl}, and k e^{T_I - gl} for
   //    blocks 0..2 over the A / P tiles; each wavefront then computes whole
   //    block pairs, A and P together, sharing the right operand.
+  //    Q^gamma and K_<^T come from the same factors, one product each:
+  //      e^{G_r} q_r = e^{G_{16R}} (q_r e^{gl_r}),
+  //      e^{G_last - G_i} k_i = e^{G_last - G_{16I+16}} (k_i e^{T_I - gl_i})   (I < 3)
+  //                           = e^{G_last - G_48} (k_i e^{-gl_i})             (I = 3)
+  //    (every factor at most 1, or within the span guard for the last block),
+  //    with the per-(block, key dim) exponentials in place of G_{16R} and
+  //    G_last - G_{16I} (read raw only on the exact path).
   if (!exact) {
     float* sRk = sA;  // [48][PK] k e^{T_I - gl}, over the A and P tiles until the products are done
+    if (t < 4 * DK) {
+      const int R = t / DK, d = t % DK;
+      const float x = sX[R * DK + d];
+      sX[R * DK + d] = pexp<POL>(R < 3 ? x - sG0[R * DK + d] : x);
+      sGF[R * DK + d] = pexp<POL>(sGF[R * DK + d]);
+    }
     for (int idx = t; idx < L * (DK / 4); idx += NT) {
       const int r = idx / (DK / 4), d4 = 4 * (idx % (DK / 4));
       const float4 kk = *reinterpret_cast<const float4*>(&sK[r * PK + d4]);
@@ -698,6 +720,12 @@ __global__ __launch_bounds__(512) void chunk_intra_kernel(PrefillArgs p) {
       if (r < 48) *reinterpret_cast<float4*>(&sRk[r * PK + d4]) = make_float4(rk[0], rk[1], rk[2], rk[3]);
     }
     __syncthreads();
+    write_afrags<POL, NT>(rec + rl.Qf, 4, DK / 32, [&](int r, int d) {
+      return sGF[(r / 16) * DK + d] * sQ[r * PK + d];
+    });
+    write_afrags<POL, NT>(rec + rl.Kf, DK / 16, 2, [&](int d, int r) {
+      return sX[(r / 16) * DK + d] * (r < 48 ? sRk[r * PK + d] : sG[r * PK + d]);
+    });
     floatx4 acc[2][2];  // [pair of this wavefront][A, P]
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -815,7 +843,6 @@ __global__ __launch_bounds__(512) void chunk_intra_kernel(PrefillArgs p) {
   //    directly from gl on the exact path.
   using FI = Frag<IP>;
   using FB = typename FI::B;
-  constexpr bool kContig = FI::kof(0, 1) == 1;  // a lane's 8 rows lie in one 16-row block
   constexpr int NFK = (DK / 16) * 2 * 64, PFK = (NFK + NT - 1) / NT;
   constexpr int NFV = (DV / 16) * 2 * 64, PFV = (NFV + NT - 1) / NT;
   {
@@ -827,13 +854,12 @@ __global__ __launch_bounds__(512) void chunk_intra_kernel(PrefillArgs p) {
         const int ln = item & 63, kb = (item >> 6) & 1, c = item >> 7;
         const int d = 16 * c + (ln & 15), g = ln >> 4;
         float x[8];
-        const float eg0 = pexp<POL>(sGF[((32 * kb + FI::kof(g, 0)) / 16) * DK + d]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int r = 32 * kb + FI::kof(g, e);
-          const float gf = sGF[(r / 16) * DK + d];
+          const float gf = sGF[(r / 16) * DK + d];  // G_{16R}, or e^{G_{16R}} off the exact path
           if (exact) x[e] = sBeta[r] * (sK[r * PK + d] * pexp<POL>(gf + sG[r * PK + d]));
-          else x[e] = sBeta[r] * (sK[r * PK + d] * (kContig ? eg0 : pexp<POL>(gf)));
+          else x[e] = sBeta[r] * (sK[r * PK + d] * gf);
         }
         fk[i] = FI::make_b(x);
       }
