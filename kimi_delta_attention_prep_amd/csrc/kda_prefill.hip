@@ -545,12 +545,30 @@ __global__ __launch_bounds__(512) void chunk_intra_kernel(PrefillArgs p) {
     RawT* stk = stq + (L + 3) * DK;
     const int64_t wk = (int64_t)H * DK;
     const int64_t chq = (int64_t)h * DK, chk = wk + (int64_t)h * DK;
+    // q and k load together; q is staged and convolved while k lands, and g and
+    // beta load while k is convolved
     uint4 xq[NSK], xk[NSK], xg[NGK];
 #pragma unroll
-    for (int i = 0; i < NSK; ++i) {
-      xq[i] = load_staged(static_cast<const RawT*>(p.raw.q), DK, chq, t + i * NT);
-      xk[i] = load_staged(static_cast<const RawT*>(p.raw.k), DK, chk, t + i * NT);
-    }
+    for (int i = 0; i < NSK; ++i) xq[i] = load_staged(static_cast<const RawT*>(p.raw.q), DK, chq, t + i * NT);
+#pragma unroll
+    for (int i = 0; i < NSK; ++i) xk[i] = load_staged(static_cast<const RawT*>(p.raw.k), DK, chk, t + i * NT);
+    auto conv_stream = [&](const RawT* st, float* dst, int64_t ch) {  // rows wave + 8 rr
+      float x[L / 8][E];
+      conv_rows<DK, true, L / 8>([&](int rr, int j, int d) { return to_f32(st[(wave + 8 * rr + j) * DK + d]); },
+                                 p.raw.conv_w + ch * 4, p.raw.act, x);
+#pragma unroll
+      for (int rr = 0; rr < L / 8; ++rr) {
+        const int r = wave + 8 * rr;
+#pragma unroll
+        for (int e = 0; e < E; ++e) dst[r * PK + E * lane + e] = r < len ? x[rr][e] : 0.f;
+      }
+    };
+#pragma unroll
+    for (int i = 0; i < NSK; ++i) store_staged(stq, DK, t + i * NT, xq[i]);
+    __syncthreads();
+    conv_stream(stq, sQ, chq);
+#pragma unroll
+    for (int i = 0; i < NSK; ++i) store_staged(stk, DK, t + i * NT, xk[i]);
     const RawT* rg = static_cast<const RawT*>(p.raw.g);
 #pragma unroll
     for (int i = 0; i < NGK; ++i) {
@@ -559,26 +577,8 @@ __global__ __launch_bounds__(512) void chunk_intra_kernel(PrefillArgs p) {
       if (idx < L * (DK / VE) && r < len) xg[i] = *reinterpret_cast<const uint4*>(rg + ((start + r) * H + h) * DK + c0);
     }
     const float braw = (t < len) ? to_f32(static_cast<const RawT*>(p.raw.beta)[(start + t) * H + h]) : 0.f;
-#pragma unroll
-    for (int i = 0; i < NSK; ++i) {
-      store_staged(stq, DK, t + i * NT, xq[i]);
-      store_staged(stk, DK, t + i * NT, xk[i]);
-    }
     __syncthreads();
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {  // q, then k: rows wave + 8 rr
-      const RawT* st = s == 0 ? stq : stk;
-      float* dst = s == 0 ? sQ : sK;
-      float x[L / 8][E];
-      conv_rows<DK, true, L / 8>([&](int rr, int j, int d) { return to_f32(st[(wave + 8 * rr + j) * DK + d]); },
-                                 p.raw.conv_w + (s == 0 ? chq : chk) * 4, p.raw.act, x);
-#pragma unroll
-      for (int rr = 0; rr < L / 8; ++rr) {
-        const int r = wave + 8 * rr;
-#pragma unroll
-        for (int e = 0; e < E; ++e) dst[r * PK + E * lane + e] = r < len ? x[rr][e] : 0.f;
-      }
-    }
+    conv_stream(stk, sK, chk);
     __syncthreads();  // the staged rows over T2 are consumed
 #pragma unroll
     for (int i = 0; i < NGK; ++i) {
