@@ -1,0 +1,94 @@
+"""Edge and degenerate cases of the GPU path against the fp64 oracle: empty
+inputs, a gate that freezes the state, and one long sequence next to a short
+one at the full head size."""
+import numpy as np
+import pytest
+import torch
+
+import kimi_delta_attention_prep_amd as K
+from kimi_delta_attention_prep_amd import inputs as I
+
+from helpers import TOL_BF16, dims_for, gpu_decode_steps, gpu_layer_prefill, oracle_layer, rel
+
+pytestmark = pytest.mark.gpu
+
+
+def _small(lens, dtype=torch.bfloat16, H=2, d=128, gate=I.GATE_SOFTPLUS, seed=5):
+    return I.generate("edge", lengths=list(lens), H=H, dk=d, dv=d, dtype=dtype, gate_mode=gate, state_std=0.02,
+                      conv_state_std=1.0, seed=seed)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_prefill_every_sequence_empty(fused):
+    """Sequences of length 0 only: the call succeeds and state and conv state keep their bits."""
+    w = _small((0, 0, 0))
+    print(f"empty prompt fused={fused}", flush=True)
+    r = gpu_layer_prefill(w, fused=fused)
+    assert torch.equal(r["state"].cpu(), w.state0)
+    if fused:
+        assert torch.equal(r["prep"]["conv_state"].cpu(), w.conv_state0)
+
+
+def test_prefill_no_sequences_is_a_no_op():
+    w = _small((5,))
+    d = dims_for(w)
+    state = torch.zeros(1, w.H, w.dk, w.dv, device="cuda")
+    o = torch.empty(0, w.H, w.dv, device="cuda")
+    ws = torch.empty(1, dtype=torch.uint8, device="cuda")
+    cu = torch.zeros(1, dtype=torch.int32, device="cuda")
+    empty = torch.empty(0, w.H, w.dk, device="cuda")
+    K.kda_prefill_varlen(d, cu, empty, empty, torch.empty(0, w.H, w.dv, device="cuda"), empty,
+                         torch.empty(0, w.H, device="cuda"), state, o, ws)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(state) == 0
+
+
+@pytest.mark.parametrize("precision", [K.PREC_BF16X3, K.PREC_FP16])
+@pytest.mark.parametrize("fused", [False, True])
+def test_prefill_beta_zero_and_unit_decay_freezes_the_state(precision, fused):
+    """beta logits of -100 (beta = 0) and softplus raw gates of -100 (a = 1 to fp32): the state stays S0
+    and o_t = S0^T q_t; the A and P products see nothing but zero keys' weights."""
+    w = _small((150, 64, 9), seed=7)
+    w.beta.fill_(-100.0)
+    w.g.fill_(-100.0)
+    print(f"frozen state precision={precision} fused={fused}", flush=True)
+    r = gpu_layer_prefill(w, precision=precision, fused=fused)
+    ref = oracle_layer(w)
+    assert np.allclose(ref.state, w.state0.double().numpy(), rtol=0, atol=1e-12)  # the oracle agrees it froze
+    assert rel(r["state"], ref.state) < 1e-6
+    assert rel(r["o"], ref.o) < TOL_BF16
+
+
+def test_decode_beta_zero_only_decays():
+    w = I.generate("edge_decode", lengths=[4] * 8, H=4, dk=128, dv=128, dtype=torch.bfloat16,
+                   gate_mode=I.GATE_SAFE, state_std=0.02, conv_state_std=1.0, seed=8)
+    w.beta.fill_(-100.0)
+    dec = gpu_decode_steps(w, 4)
+    ref = oracle_layer(w)
+    assert rel(dec["state"], ref.state) < 1e-6
+    o = dec["o"].transpose(0, 1).reshape(w.T, w.H, w.dv)
+    assert rel(o, ref.o) < TOL_BF16
+
+
+def test_long_sequence_next_to_a_short_one():
+    """512 chunks of one sequence packed with a 3-row one (H=2, d=128): oracle parity, and the long one
+    cut at row 16384 with the state and conv state carried gives the same bits."""
+    n_long = 32768
+    w = _small((n_long, 3), H=2, seed=9, gate=I.GATE_SAFE)
+    print(f"long prompt T={w.T}", flush=True)
+    r = gpu_layer_prefill(w, precision=K.PREC_FP16, fused=True)
+    ref = oracle_layer(w)
+    assert rel(r["o"], ref.o) < TOL_BF16 and rel(r["state"], ref.state) < TOL_BF16
+    cut = 16384
+    sl = slice(0, cut)
+    a = I.Workload("a", w.H, w.dk, w.dv, torch.tensor([0, cut], dtype=torch.int32), w.q[sl], w.k[sl], w.v[sl],
+                   w.g[sl], w.beta[sl], w.z[sl], w.conv_w, w.norm_w, w.state0[:1], w.conv_state0[:1], w.gate_mode,
+                   w.lower_bound)
+    ra = gpu_layer_prefill(a, precision=K.PREC_FP16, fused=True)
+    sl = slice(cut, n_long)
+    b = I.Workload("b", w.H, w.dk, w.dv, torch.tensor([0, n_long - cut], dtype=torch.int32), w.q[sl], w.k[sl],
+                   w.v[sl], w.g[sl], w.beta[sl], w.z[sl], w.conv_w, w.norm_w, ra["state"].cpu(),
+                   ra["prep"]["conv_state"].cpu(), w.gate_mode, w.lower_bound)
+    rb = gpu_layer_prefill(b, precision=K.PREC_FP16, fused=True)
+    assert torch.equal(torch.cat([ra["o"], rb["o"]]), r["o"][:n_long])
+    assert torch.equal(rb["state"][0], r["state"][0])
