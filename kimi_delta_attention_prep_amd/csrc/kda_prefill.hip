@@ -552,13 +552,15 @@ __global__ __launch_bounds__(512) void chunk_intra_kernel(PrefillArgs p) {
     for (int i = 0; i < NSK; ++i) xq[i] = load_staged(static_cast<const RawT*>(p.raw.q), DK, chq, t + i * NT);
 #pragma unroll
     for (int i = 0; i < NSK; ++i) xk[i] = load_staged(static_cast<const RawT*>(p.raw.k), DK, chk, t + i * NT);
-    auto conv_stream = [&](const RawT* st, float* dst, int64_t ch) {  // rows wave + 8 rr
+    // each wavefront takes 8 consecutive rows, so its 32 taps per channel come from
+    // 11 staged rows, each read and widened once
+    auto conv_stream = [&](const RawT* st, float* dst, int64_t ch) {  // rows 8 wave + rr
       float x[L / 8][E];
-      conv_rows<DK, true, L / 8>([&](int rr, int j, int d) { return to_f32(st[(wave + 8 * rr + j) * DK + d]); },
+      conv_rows<DK, true, L / 8>([&](int rr, int j, int d) { return to_f32(st[(8 * wave + rr + j) * DK + d]); },
                                  p.raw.conv_w + ch * 4, p.raw.act, x);
 #pragma unroll
       for (int rr = 0; rr < L / 8; ++rr) {
-        const int r = wave + 8 * rr;
+        const int r = 8 * wave + rr;
 #pragma unroll
         for (int e = 0; e < E; ++e) dst[r * PK + E * lane + e] = r < len ? x[rr][e] : 0.f;
       }
@@ -879,20 +881,20 @@ __global__ __launch_bounds__(512) void chunk_intra_kernel(PrefillArgs p) {
 #pragma unroll
       for (int i = 0; i < NSV; ++i) store_staged(stv, DV, t + i * NT, xv[i]);
       __syncthreads();
-      conv_rows<DV, false, L / 8>([&](int rr, int j, int d) { return to_f32(stv[(wave + 8 * rr + j) * DV + d]); },
+      conv_rows<DV, false, L / 8>([&](int rr, int j, int d) { return to_f32(stv[(8 * wave + rr + j) * DV + d]); },
                                   p.raw.conv_w + chv * 4, p.raw.act, x);
     } else {
       const RawT* rv = static_cast<const RawT*>(p.raw.v);
-      const int64_t wv = (int64_t)H * DV, rel0 = start - t0 + wave;
+      const int64_t wv = (int64_t)H * DV, rel0 = start - t0 + 8 * wave;
       conv_rows<DV, false, L / 8>([&](int rr, int j, int d) {
-        const int64_t pos = rel0 + 8 * rr - 3 + j;
-        if (wave + 8 * rr >= len) return 0.f;
+        const int64_t pos = rel0 + rr - 3 + j;
+        if (8 * wave + rr >= len) return 0.f;
         return pos >= 0 ? to_f32(rv[(t0 + pos) * wv + (int64_t)h * DV + d]) : to_f32(raw_cs[(3 + pos) * Cch + chv + d]);
       }, p.raw.conv_w + chv * 4, p.raw.act, x);
     }
 #pragma unroll
     for (int rr = 0; rr < L / 8; ++rr) {
-      const int r = wave + 8 * rr;
+      const int r = 8 * wave + rr;
 #pragma unroll
       for (int e = 0; e < EV; ++e) sQ[r * PK + EV * lane + e] = r < len ? sBeta[r] * x[rr][e] : 0.f;
     }
