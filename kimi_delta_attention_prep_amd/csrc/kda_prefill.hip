@@ -535,6 +535,12 @@ __global__ __launch_bounds__(512) void chunk_intra_kernel(PrefillArgs p) {
   auto store_staged = [&](RawT* st, int D, int idx, uint4 x) {
     if (idx < (L + 3) * (D / VE)) *reinterpret_cast<uint4*>(st + idx * VE) = x;
   };
+  // Fused: the v rows are loaded with the preamble's rows and land long before step 7
+  // (staged over A there where they fit; fp32 rows read their taps from HBM)
+  constexpr bool kVStaged = FUSED && (L + 3) * DV * sizeof(RawT) <= (size_t)L * PL * sizeof(float);
+  constexpr int NSV = kVStaged ? ((L + 3) * (DV / VE) + NT - 1) / NT : 1;
+  const int64_t chv = 2 * (int64_t)H * DK + (int64_t)h * DV;
+  uint4 xv[NSV];
   if constexpr (FUSED) {
     constexpr int E = DK / 64;
     constexpr int NSK = ((L + 3) * (DK / VE) + NT - 1) / NT;  // pieces per thread of a staged q or k stream
@@ -579,6 +585,10 @@ __global__ __launch_bounds__(512) void chunk_intra_kernel(PrefillArgs p) {
       if (idx < L * (DK / VE) && r < len) xg[i] = *reinterpret_cast<const uint4*>(rg + ((start + r) * H + h) * DK + c0);
     }
     const float braw = (t < len) ? to_f32(static_cast<const RawT*>(p.raw.beta)[(start + t) * H + h]) : 0.f;
+    if constexpr (kVStaged) {
+#pragma unroll
+      for (int i = 0; i < NSV; ++i) xv[i] = load_staged(static_cast<const RawT*>(p.raw.v), DV, chv, t + i * NT);
+    }
     __syncthreads();
     conv_stream(stk, sK, chk);
     __syncthreads();  // the staged rows over T2 are consumed
@@ -784,37 +794,34 @@ __global__ __launch_bounds__(512) void chunk_intra_kernel(PrefillArgs p) {
   __syncthreads();
 
   // 6. X = (I + A)^{-1} into the P tile
-  // Fused: the v rows the chunk needs are loaded here and land during the solve
-  // (staged over A in step 7 where they fit; fp32 rows read their taps from HBM)
-  constexpr bool kVStaged = FUSED && (L + 3) * DV * sizeof(RawT) <= (size_t)L * PL * sizeof(float);
-  constexpr int NSV = kVStaged ? ((L + 3) * (DV / VE) + NT - 1) / NT : 1;
-  const int64_t chv = 2 * (int64_t)H * DK + (int64_t)h * DV;
-  uint4 xv[NSV];
-  if constexpr (kVStaged) {
-#pragma unroll
-    for (int i = 0; i < NSV; ++i) xv[i] = load_staged(static_cast<const RawT*>(p.raw.v), DV, chv, t + i * NT);
-  }
   float* sXi = sP;
   for (int idx = t; idx < L * L; idx += NT) sXi[(idx / L) * PL + idx % L] = 0.f;
   __syncthreads();
-  if (t < L) {  // diagonal blocks by forward substitution, one column per thread
-    // right-looking: once x_r is final, every later row takes its term at once,
-    // so the dependent chain is 16 steps long
-    const int R = t / 16, cc = t % 16, b0 = 16 * R;
-    float xv[16];
+  if (wave < 4) {  // diagonal block R = wavefront, by forward substitution
+    // lane 4 cc + qq owns column cc, rows 4 qq .. 4 qq + 3 of the block.  Right-looking:
+    // once x_r is final it is broadcast in the lane quad and every later row takes its
+    // term, in the order r = 0, 1, ... (rows at or above r see a zero of A's strictly
+    // lower block and keep their value).
+    const int R = wave, b0 = 16 * R, cc = lane >> 2, qq = lane & 3;
+    float xv[4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) xv[r] = (r == cc) ? 1.f : 0.f;
+    for (int j = 0; j < 4; ++j) xv[j] = (4 * qq + j == cc) ? 1.f : 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float x = (r >= cc) ? xv[r] : 0.f;
-      xv[r] = x;
+      constexpr int kQuad[4] = {0x00, 0x55, 0xAA, 0xFF};  // quad_perm broadcast of lane 0..3 of each quad
+      float x = xv[r & 3];
+      if ((r >> 2) == 0) x = dpp_partner<kQuad[0]>(x);
+      else if ((r >> 2) == 1) x = dpp_partner<kQuad[1]>(x);
+      else if ((r >> 2) == 2) x = dpp_partner<kQuad[2]>(x);
+      else x = dpp_partner<kQuad[3]>(x);
+      x = (r >= cc) ? x : 0.f;
 #pragma unroll
-      for (int i = r + 1; i < 16; ++i) xv[i] = fmaf(-sA[(b0 + i) * PL + b0 + r], x, xv[i]);
+      for (int j = 0; j < 4; ++j) xv[j] = fmaf(-sA[(b0 + 4 * qq + j) * PL + b0 + r], x, xv[j]);
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sXi[(b0 + r) * PL + b0 + cc] = xv[r];
+    for (int j = 0; j < 4; ++j) sXi[(b0 + 4 * qq + j) * PL + b0 + cc] = xv[j];
   }
-  __syncthreads();
+  __syncthreads();  // X_RR of every diagonal block is complete: block (R, I) reads it from wavefront R
   // off-diagonal blocks, nearest diagonals first, one wavefront per block on the matrix cores (fp32):
   //   Y = sum_{J=I}^{R-1} A_RJ X_JI,  X_RI = -X_RR Y
   for (int dist = 1; dist < 4; ++dist) {
