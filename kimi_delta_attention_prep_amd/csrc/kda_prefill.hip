@@ -469,11 +469,14 @@ __device__ __forceinline__ void pair_mma(floatx4& acc_a, floatx4& acc_p, const f
   }
 }
 
+constexpr int kIntraThreads = 1024;  // 16 wavefronts: 4 per SIMD with one workgroup per CU
+
 template <int DK, int DV, int POL, typename RawT, bool FUSED>
-__global__ __launch_bounds__(512) void chunk_intra_kernel(PrefillArgs p) {
+__global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs p) {
   using SM = IntraSmem<DK, DV>;
   constexpr int IP = IntraPol<POL>::value;
-  constexpr int L = SM::L, PK = SM::PK, PL = SM::PL, NT = 512;
+  constexpr int L = SM::L, PK = SM::PK, PL = SM::PL, NT = kIntraThreads;
+  constexpr int NW = NT / 64, RW = L / NW;  // wavefronts; consecutive rows per wavefront in the convolutions
   extern __shared__ __align__(16) float smem[];
   float* sK = smem + SM::T0;
   float* sQ = smem + SM::T1;
@@ -508,7 +511,7 @@ __global__ __launch_bounds__(512) void chunk_intra_kernel(PrefillArgs p) {
   // The q and k streams are staged in LDS as 67 rows each (3 halo rows, then
   // the chunk's rows; halo rows come from the sequence's previous rows, or
   // from its carried conv state at the sequence start) and each wavefront
-  // then runs the preamble of 8 rows side by side, reading its taps there.
+  // then runs the preamble of RW consecutive rows side by side, reading its taps there.
   constexpr int VE = 16 / sizeof(RawT);  // raw elements per 16-byte piece
   // piece idx of a staged stream (row sr = idx / (D / VE) of the 67): zero past the chunk's last row
   auto load_staged = [&](const RawT* src, int D, int64_t ch0, int idx) {
@@ -558,15 +561,15 @@ __global__ __launch_bounds__(512) void chunk_intra_kernel(PrefillArgs p) {
     for (int i = 0; i < NSK; ++i) xq[i] = load_staged(static_cast<const RawT*>(p.raw.q), DK, chq, t + i * NT);
 #pragma unroll
     for (int i = 0; i < NSK; ++i) xk[i] = load_staged(static_cast<const RawT*>(p.raw.k), DK, chk, t + i * NT);
-    // each wavefront takes 8 consecutive rows, so its 32 taps per channel come from
-    // 11 staged rows, each read and widened once
-    auto conv_stream = [&](const RawT* st, float* dst, int64_t ch) {  // rows 8 wave + rr
-      float x[L / 8][E];
-      conv_rows<DK, true, L / 8>([&](int rr, int j, int d) { return to_f32(st[(8 * wave + rr + j) * DK + d]); },
+    // each wavefront takes RW consecutive rows, so its 4 RW taps per channel come
+    // from RW + 3 staged rows, each read and widened once
+    auto conv_stream = [&](const RawT* st, float* dst, int64_t ch) {  // rows RW wave + rr
+      float x[RW][E];
+      conv_rows<DK, true, RW>([&](int rr, int j, int d) { return to_f32(st[(RW * wave + rr + j) * DK + d]); },
                                  p.raw.conv_w + ch * 4, p.raw.act, x);
 #pragma unroll
-      for (int rr = 0; rr < L / 8; ++rr) {
-        const int r = 8 * wave + rr;
+      for (int rr = 0; rr < RW; ++rr) {
+        const int r = RW * wave + rr;
 #pragma unroll
         for (int e = 0; e < E; ++e) dst[r * PK + E * lane + e] = r < len ? x[rr][e] : 0.f;
       }
@@ -738,10 +741,11 @@ __global__ __launch_bounds__(512) void chunk_intra_kernel(PrefillArgs p) {
     write_afrags<POL, NT>(rec + rl.Kf, DK / 16, 2, [&](int d, int r) {
       return sX[(r / 16) * DK + d] * (r < 48 ? sRk[r * PK + d] : sG[r * PK + d]);
     });
-    floatx4 acc[2][2];  // [pair of this wavefront][A, P]
+    constexpr int NJ = (10 + NW - 1) / NW;  // block pairs per wavefront
+    floatx4 acc[NJ][2];  // [pair of this wavefront][A, P]
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int pr = wave + 8 * j;  // pairs in order (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) ...
+    for (int j = 0; j < NJ; ++j) {
+      const int pr = wave + NW * j;  // pairs in order (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) ...
       acc[j][0] = acc[j][1] = floatx4{0.f, 0.f, 0.f, 0.f};
       if (pr < 10) {
         int R = 0, I = pr;
@@ -753,8 +757,8 @@ __global__ __launch_bounds__(512) void chunk_intra_kernel(PrefillArgs p) {
     }
     __syncthreads();  // every wavefront is done with the factors over A and P
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int pr = wave + 8 * j;
+    for (int j = 0; j < NJ; ++j) {
+      const int pr = wave + NW * j;
       if (pr < 10) {
         int R = 0, I = pr;
         while (I > R) { I -= R + 1; ++R; }
@@ -879,29 +883,29 @@ __global__ __launch_bounds__(512) void chunk_intra_kernel(PrefillArgs p) {
       if (t + i * NT < NFK) reinterpret_cast<FB*>(sG)[t + i * NT] = fk[i];
   }
   if constexpr (FUSED) {
-    // v rows: conv (no norm), 8 rows per wavefront side by side, b_r v_r into T1
+    // v rows: conv (no norm), RW rows per wavefront side by side, b_r v_r into T1
     constexpr int EV = DV / 64;
-    float x[L / 8][EV];
+    float x[RW][EV];
     if constexpr (kVStaged) {
       RawT* stv = reinterpret_cast<RawT*>(sA);  // [67][DV] staged v rows over A, which the solve no longer reads
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < NSV; ++i) store_staged(stv, DV, t + i * NT, xv[i]);
       __syncthreads();
-      conv_rows<DV, false, L / 8>([&](int rr, int j, int d) { return to_f32(stv[(8 * wave + rr + j) * DV + d]); },
+      conv_rows<DV, false, RW>([&](int rr, int j, int d) { return to_f32(stv[(RW * wave + rr + j) * DV + d]); },
                                   p.raw.conv_w + chv * 4, p.raw.act, x);
     } else {
       const RawT* rv = static_cast<const RawT*>(p.raw.v);
-      const int64_t wv = (int64_t)H * DV, rel0 = start - t0 + 8 * wave;
-      conv_rows<DV, false, L / 8>([&](int rr, int j, int d) {
+      const int64_t wv = (int64_t)H * DV, rel0 = start - t0 + RW * wave;
+      conv_rows<DV, false, RW>([&](int rr, int j, int d) {
         const int64_t pos = rel0 + rr - 3 + j;
-        if (8 * wave + rr >= len) return 0.f;
+        if (RW * wave + rr >= len) return 0.f;
         return pos >= 0 ? to_f32(rv[(t0 + pos) * wv + (int64_t)h * DV + d]) : to_f32(raw_cs[(3 + pos) * Cch + chv + d]);
       }, p.raw.conv_w + chv * 4, p.raw.act, x);
     }
 #pragma unroll
-    for (int rr = 0; rr < L / 8; ++rr) {
-      const int r = 8 * wave + rr;
+    for (int rr = 0; rr < RW; ++rr) {
+      const int r = RW * wave + rr;
 #pragma unroll
       for (int e = 0; e < EV; ++e) sQ[r * PK + EV * lane + e] = r < len ? sBeta[r] * x[rr][e] : 0.f;
     }
@@ -939,15 +943,17 @@ __global__ __launch_bounds__(512) void chunk_intra_kernel(PrefillArgs p) {
   __syncthreads();
 
   // 8. W = X (b K^gamma), U~ = X (b V).  X is lower triangular, so row block R
-  //    needs K = 16(R+1) rounded up to 32.  Two wavefronts per row block R, each
-  //    holding its split rows of X and taking half of the W and U~ column tiles.
+  //    needs K = 16(R+1) rounded up to 32.  NW / 4 wavefronts per row block R, each
+  //    holding its split rows of X and taking an equal share of the W and U~ column tiles.
   //    U~ goes to the record in result layout; W through LDS (T1) into fragments.
   {
     constexpr int NTW = DK / 16, NTU = DV / 16, NTT = NTW + NTU;
     const FB* fRk = reinterpret_cast<const FB*>(sG);
     const FB* fV = reinterpret_cast<const FB*>(sK);
     float* sW = sQ;  // b v rows in T1 are consumed
-    const int R = 3 - (wave >> 1), half = wave & 1, KBR = (16 * (R + 1) + 31) / 32;
+    constexpr int WPR = NW / 4, TPW = NTT / WPR;  // wavefronts per row block, column tiles per wavefront
+    static_assert(NTT % WPR == 0, "column tiles split evenly");
+    const int R = 3 - wave / WPR, part = wave % WPR, KBR = (16 * (R + 1) + 31) / 32;
     const int col = lane & 15, g4 = lane >> 4;
     typename FI::A xa[2];
 #pragma unroll
@@ -957,7 +963,7 @@ __global__ __launch_bounds__(512) void chunk_intra_kernel(PrefillArgs p) {
       for (int e = 0; e < 8; ++e) x[e] = sXi[(16 * R + col) * PL + 32 * kb + FI::kof(g4, e)];
       xa[kb] = FI::make_b(x);
     }
-    for (int c = half * (NTT / 2); c < (half + 1) * (NTT / 2); ++c) {
+    for (int c = part * TPW; c < (part + 1) * TPW; ++c) {
       const bool isW = c < NTW;
       const int cb = isW ? c : c - NTW;
       const FB* bsrc = isW ? fRk : fV;
@@ -1234,7 +1240,7 @@ static hipError_t launch_prefill_t(const PrefillLaunch& Lc, hipStream_t s) {
   e = mark(1, 0);
   if (e != hipSuccess) return e;
   if (mc > 0 && Lc.t_tot > 0) {
-    hipLaunchKernelGGL((chunk_intra_kernel<DK, DV, POL, RawT, FUSED>), dim3((unsigned)mc, (unsigned)Lc.H), dim3(512),
+    hipLaunchKernelGGL((chunk_intra_kernel<DK, DV, POL, RawT, FUSED>), dim3((unsigned)mc, (unsigned)Lc.H), dim3(kIntraThreads),
                        intra_bytes, s, p);
     e = hipGetLastError();
   }
