@@ -381,6 +381,9 @@ __device__ __forceinline__ int chunk_seq(const int32_t* chunk_off, int num_seqs,
 // standalone preamble kernel, so the fused and unfused paths agree bit for bit.
 // ---------------------------------------------------------------------------
 constexpr float kSpanGuard = 80.0f;
+// and a block's full decay T_I = G_{16I+16} - G_{16I} (one more row) must keep
+// e^{T_I} a normal fp32 number, which the pivoted path multiplies by
+constexpr float kBlockDecayGuard = 86.0f;
 
 template <int DK, int DV>
 struct IntraSmem {
@@ -394,16 +397,17 @@ struct IntraSmem {
   static constexpr int TA = T2 + L * PK;      // A                                   [L][PL]
   static constexpr int TP = TA + L * PL;      // P, then X                           [L][PL]
   static constexpr int TB = TP + L * PL;      // beta                                [L]
-  static constexpr int TGF = TB + L;          // G_{16R} from the chunk start; pivoted
-                                              // path: then e^{G_{16R}}              [4][DK]
-  static constexpr int TX = TGF + 4 * DK;     // G_last - G_{16I}; pivoted path: then
-                                              // the K_<^T factor of block I          [4][DK]
+  static constexpr int TGF = TB + L;          // G_{16R} from the chunk start         [4][DK]
+  static constexpr int TX = TGF + 4 * DK;     // G_last - G_{16I}                     [4][DK]
   static constexpr int TD = TX + 4 * DK;      // e^{G_{16R} - G_{16I+16}}, I + 1 < R  [6][DK]
-  static constexpr int TG0 = TD + 6 * DK;     // g at each block's first row, then
-                                              // T_I = G_{16I+16} - G_{16I}            [4][DK]
+  static constexpr int TG0 = TD + 6 * DK;     // g at each block's first row          [4][DK]
   static constexpr int TY = TG0 + 4 * DK;     // solve scratch, one per wavefront    [3][16][17]
   static constexpr int TFLAG = TY + 3 * 16 * 17;
-  static constexpr int FLOATS = TFLAG + 4;
+  // pivoted path: e^{G_{16R}}, the K_<^T factor of block I, and e^{T_I}      [4][DK], [4][DK], [3][DK]
+  static constexpr int TGFE = TFLAG + 4;
+  static constexpr int TXE = TGFE + 4 * DK;
+  static constexpr int TET = TXE + 4 * DK;
+  static constexpr int FLOATS = TET + 3 * DK;
   static constexpr size_t BYTES = FLOATS * sizeof(float);
 };
 
@@ -420,44 +424,93 @@ __device__ __forceinline__ float piece_elem(const uint4& x, int e) {
 
 __device__ __forceinline__ int pair_index(int R, int I) { return R * (R - 1) / 2 + I; }  // I < R
 
-// One block pair of A and P: acc_a += (s . La) Rt^T and acc_p += (s . Lq) Rt^T over
-// K = DK, where La, Lq, Rt point at 16 rows of row stride PK and s is a per-K
-// scale (none when null).  The right operand is split once for both products.
+// Pivoted factor tiles of the intra-chunk kernel, [64 rows] x [row stride PK
+// floats] in LDS.  With fp32 intra products an element is the float at
+// [r * PK + d].  With split (bf16 x 3) products each row is a run of 8-column
+// groups of 32 bytes, the 8 bf16 high parts and then the 8 bf16 low parts
+// (hi + lo within about 2^-17 of the value), so the operands of a 32-wide K
+// block load straight into the matrix-core registers and every element is
+// split once per chunk instead of once per product that reads it.
+template <int IP, int PK>
+struct FacTile {
+  static constexpr bool SPLIT = IP != POL_FP32;
+  __device__ static uint8_t* at(float* base, int r, int d) {
+    return reinterpret_cast<uint8_t*>(base + r * PK) + (d >> 3) * 32 + (d & 7) * 2;
+  }
+  __device__ static const uint8_t* at(const float* base, int r, int d) {
+    return reinterpret_cast<const uint8_t*>(base + r * PK) + (d >> 3) * 32 + (d & 7) * 2;
+  }
+  // elements d4 .. d4 + 3 of row r (d4 a multiple of 4)
+  __device__ static void store4(float* base, int r, int d4, const float (&x)[4]) {
+    if constexpr (!SPLIT) {
+      *reinterpret_cast<float4*>(&base[r * PK + d4]) = make_float4(x[0], x[1], x[2], x[3]);
+    } else {
+      // hi = x rounded to bf16, lo = (x - hi) rounded to bf16, two elements per packed
+      // conversion; hi widens back to fp32 exactly from its bits
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      typedef float floatx2 __attribute__((ext_vector_type(2)));
+      uint32_t hb[2], lb[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const floatx2 v = {x[2 * j], x[2 * j + 1]};
+        hb[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+        const floatx2 w = {v[0] - __uint_as_float(hb[j] << 16), v[1] - __uint_as_float(hb[j] & 0xffff0000u)};
+        lb[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(w, bf16x2));
+      }
+      uint8_t* q = at(base, r, d4);
+      *reinterpret_cast<uint2*>(q) = make_uint2(hb[0], hb[1]);
+      *reinterpret_cast<uint2*>(q + 16) = make_uint2(lb[0], lb[1]);
+    }
+  }
+  __device__ static float load1(const float* base, int r, int d) {
+    if constexpr (!SPLIT) {
+      return base[r * PK + d];
+    } else {
+      const uint8_t* q = at(base, r, d);
+      return static_cast<float>(*reinterpret_cast<const __bf16*>(q)) +
+             static_cast<float>(*reinterpret_cast<const __bf16*>(q + 16));
+    }
+  }
+  // high and low parts of row r, columns kk .. kk + 7 (kk a multiple of 8)
+  __device__ static void load8(const float* base, int r, int kk, bf16x8& hi, bf16x8& lo) {
+    const uint8_t* q = at(base, r, kk);
+    hi = *reinterpret_cast<const bf16x8*>(q);
+    lo = *reinterpret_cast<const bf16x8*>(q + 16);
+  }
+};
+
+// One block pair of A and P: acc_a += La (s . Rt)^T and acc_p += Lq (s . Rt)^T over
+// K = DK, where La, Lq, Rt point at 16 factor rows (FacTile layout) and s is a
+// per-K scale (none when null), applied to the right operand, which both
+// products share.
 template <int IP, int DK, int PK>
 __device__ __forceinline__ void pair_mma(floatx4& acc_a, floatx4& acc_p, const float* La, const float* Lq,
                                          const float* Rt, const float* s) {
+  using FT = FacTile<IP, PK>;
   const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   if constexpr (IP == POL_FP32) {
-    auto fa = [&](int i, int kk) { return s ? La[i * PK + kk] * s[kk] : La[i * PK + kk]; };
-    auto fq = [&](int i, int kk) { return s ? Lq[i * PK + kk] * s[kk] : Lq[i * PK + kk]; };
-    auto fb = [&](int kk, int j) { return Rt[j * PK + kk]; };
+    auto fa = [&](int i, int kk) { return La[i * PK + kk]; };
+    auto fq = [&](int i, int kk) { return Lq[i * PK + kk]; };
+    auto fb = [&](int kk, int j) { return s ? Rt[j * PK + kk] * s[kk] : Rt[j * PK + kk]; };
     mma16<IP>(acc_a, DK, fa, fb);
     mma16<IP>(acc_p, DK, fq, fb);
   } else {
 #pragma unroll
     for (int k0 = 0; k0 < DK; k0 += 32) {
       const int kk = k0 + 8 * g;
-      float a[8], q[8], b[8];
-      auto ld8 = [&](const float* p, float (&x)[8]) {
-        const float4 u = *reinterpret_cast<const float4*>(p), w = *reinterpret_cast<const float4*>(p + 4);
-        x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w; x[4] = w.x; x[5] = w.y; x[6] = w.z; x[7] = w.w;
-      };
-      ld8(La + r * PK + kk, a);
-      ld8(Lq + r * PK + kk, q);
-      ld8(Rt + r * PK + kk, b);
-      if (s) {
-        float sc[8];
-        ld8(s + kk, sc);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { a[e] *= sc[e]; q[e] *= sc[e]; }
-      }
       bf16x8 ah, al, qh, ql, bh, bl;
+      FT::load8(La, r, kk, ah, al);
+      FT::load8(Lq, r, kk, qh, ql);
+      FT::load8(Rt, r, kk, bh, bl);
+      if (s) {
+        const float4 s0 = *reinterpret_cast<const float4*>(s + kk), s1 = *reinterpret_cast<const float4*>(s + kk + 4);
+        const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        __bf16 h, l;
-        split_bf16(a[e], h, l); ah[e] = h; al[e] = l;
-        split_bf16(q[e], h, l); qh[e] = h; ql[e] = l;
-        split_bf16(b[e], h, l); bh[e] = h; bl[e] = l;
+        for (int e = 0; e < 8; ++e) {
+          __bf16 h, l;
+          split_bf16((static_cast<float>(bh[e]) + static_cast<float>(bl[e])) * sc[e], h, l);
+          bh[e] = h; bl[e] = l;
+        }
       }
       acc_a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc_a, 0, 0, 0);
       acc_a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc_a, 0, 0, 0);
@@ -477,6 +530,7 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
   constexpr int IP = IntraPol<POL>::value;
   constexpr int L = SM::L, PK = SM::PK, PL = SM::PL, NT = kIntraThreads;
   constexpr int NW = NT / 64, RW = L / NW;  // wavefronts; consecutive rows per wavefront in the convolutions
+  using FT = FacTile<IP, PK>;               // layout of the pivoted factors over T0, T1, T2 and A / P
   extern __shared__ __align__(16) float smem[];
   float* sK = smem + SM::T0;
   float* sQ = smem + SM::T1;
@@ -488,6 +542,9 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
   float* sX = smem + SM::TX;
   float* sD = smem + SM::TD;
   float* sG0 = smem + SM::TG0;
+  float* sGFe = smem + SM::TGFE;
+  float* sXe = smem + SM::TXE;
+  float* sET = smem + SM::TET;
   float* sY = smem + SM::TY;
   int* sFlag = reinterpret_cast<int*>(smem + SM::TFLAG);
 
@@ -643,7 +700,10 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
   __syncthreads();
 
   // 3. per key dim, from block-local sums: T_R = G_{16R+16} - G_{16R}, G_{16R}, G_last - G_{16I},
-  //    e^{G_{16R} - G_{16I+16}} for the off-diagonal block pairs, and gamma_L
+  //    e^{G_{16R} - G_{16I+16}} for the off-diagonal block pairs, and gamma_L; for the
+  //    pivoted path also e^{G_{16R}}, e^{G_last - G_{16I+16}} (I < 3) or e^{G_last - G_48},
+  //    and e^{T_I}.  Both sets are written: which path the chunk takes is known after
+  //    the barrier.
   if (t < DK) {
     const int d = t;
     float T[3];
@@ -652,27 +712,33 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
     const int Rl = (len - 1) / 16;
     const float glL = sG[(len - 1) * PK + d];
     float gf = sG0[d];
+    bool steep = false;
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
       sGF[R * DK + d] = gf;
+      sGFe[R * DK + d] = pexp<POL>(gf);
       float x = 0.f;  // G_last - G_{16R}: blocks past the last row hold only zero rows
       if (R <= Rl) {
         x = glL;
         for (int J = R; J < Rl; ++J) x += T[J];
       }
       sX[R * DK + d] = x;
+      sXe[R * DK + d] = pexp<POL>(R < 3 ? x - T[R] : x);
       for (int I = 0; I + 1 < R; ++I) {
         float dd = 0.f;
         for (int J = I + 1; J < R; ++J) dd += T[J];
         sD[pair_index(R, I) * DK + d] = pexp<POL>(dd);
       }
-      if (R < 3) gf += T[R];
+      if (R < 3) {
+        sET[R * DK + d] = pexp<POL>(T[R]);
+        steep |= -T[R] > kBlockDecayGuard;
+        gf += T[R];
+      }
     }
+    if (steep) atomicOr(sFlag, 1);
     float glast = sG0[d];
     for (int J = 0; J < Rl; ++J) glast += T[J];
     reinterpret_cast<float*>(rec + rl.gL)[d] = pexp<POL>(glast + glL);
-#pragma unroll
-    for (int R = 0; R < 3; ++R) sG0[R * DK + d] = T[R];  // g at the first rows is no longer needed
   }
   __syncthreads();
   const bool exact = sFlag[0] != 0;
@@ -695,31 +761,29 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
   //    with E_RI = e^{G_{16R} - G_{16I+16}} (1 for R = I + 1), and the same with q_r for P.
   //    Off the diagonal every factor is at most 1, so a factor that underflows
   //    belongs to a term below e^-87; on the diagonal the span guard keeps both
-  //    factors within e^{+-80}.  The factors are formed once per chunk in place:
-  //    T0 = k e^{gl}, T1 = q e^{gl}, T2 = k e^{-gl}, and k e^{T_I - gl} for
-  //    blocks 0..2 over the A / P tiles; each wavefront then computes whole
-  //    block pairs, A and P together, sharing the right operand.
+  //    factors within e^{+-80}.  The factors are formed once per chunk in place
+  //    (already split for split products): T0 = k e^{gl}, T1 = q e^{gl},
+  //    T2 = k e^{-gl}, and k e^{T_I - gl} for blocks 0..2 over the A / P tiles;
+  //    each wavefront then computes whole block pairs, A and P together, sharing
+  //    the right operand, which carries E_RI where it is not 1.
   //    Q^gamma and K_<^T come from the same factors, one product each:
   //      e^{G_r} q_r = e^{G_{16R}} (q_r e^{gl_r}),
   //      e^{G_last - G_i} k_i = e^{G_last - G_{16I+16}} (k_i e^{T_I - gl_i})   (I < 3)
   //                           = e^{G_last - G_48} (k_i e^{-gl_i})             (I = 3)
   //    (every factor at most 1, or within the span guard for the last block),
-  //    with the per-(block, key dim) exponentials in place of G_{16R} and
-  //    G_last - G_{16I} (read raw only on the exact path).
+  //    with the per-(block, key dim) exponentials of step 3 in place of G_{16R}
+  //    and G_last - G_{16I} (read raw only on the exact path), and
+  //    k e^{T_I - gl} = (k e^{-gl}) e^{T_I}, one product.
   if (!exact) {
     float* sRk = sA;  // [48][PK] k e^{T_I - gl}, over the A and P tiles until the products are done
-    if (t < 4 * DK) {
-      const int R = t / DK, d = t % DK;
-      const float x = sX[R * DK + d];
-      sX[R * DK + d] = pexp<POL>(R < 3 ? x - sG0[R * DK + d] : x);
-      sGF[R * DK + d] = pexp<POL>(sGF[R * DK + d]);
-    }
     for (int idx = t; idx < L * (DK / 4); idx += NT) {
       const int r = idx / (DK / 4), d4 = 4 * (idx % (DK / 4));
       const float4 kk = *reinterpret_cast<const float4*>(&sK[r * PK + d4]);
       const float4 qq = *reinterpret_cast<const float4*>(&sQ[r * PK + d4]);
       const float4 gg = *reinterpret_cast<const float4*>(&sG[r * PK + d4]);
+      const float4 ee = *reinterpret_cast<const float4*>(&sET[min(r >> 4, 2) * DK + d4]);  // used for r < 48
       const float kv[4] = {kk.x, kk.y, kk.z, kk.w}, qv[4] = {qq.x, qq.y, qq.z, qq.w}, gv[4] = {gg.x, gg.y, gg.z, gg.w};
+      const float ev[4] = {ee.x, ee.y, ee.z, ee.w};
       float lk[4], lq[4], rd[4], rk[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -727,25 +791,29 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
         lk[e] = kv[e] * ep;
         lq[e] = qv[e] * ep;
         rd[e] = kv[e] * pexp<POL>(-gv[e]);
-        if (r < 48) rk[e] = kv[e] * pexp<POL>(sG0[(r / 16) * DK + d4 + e] - gv[e]);
+        rk[e] = rd[e] * ev[e];  // k e^{T_I - gl}: e^{-gl} <= e^80 and e^{T_I} >= e^-86, both normal
       }
-      *reinterpret_cast<float4*>(&sK[r * PK + d4]) = make_float4(lk[0], lk[1], lk[2], lk[3]);
-      *reinterpret_cast<float4*>(&sQ[r * PK + d4]) = make_float4(lq[0], lq[1], lq[2], lq[3]);
-      *reinterpret_cast<float4*>(&sG[r * PK + d4]) = make_float4(rd[0], rd[1], rd[2], rd[3]);
-      if (r < 48) *reinterpret_cast<float4*>(&sRk[r * PK + d4]) = make_float4(rk[0], rk[1], rk[2], rk[3]);
+      FT::store4(sK, r, d4, lk);
+      FT::store4(sQ, r, d4, lq);
+      FT::store4(sG, r, d4, rd);
+      if (r < 48) FT::store4(sRk, r, d4, rk);
     }
     __syncthreads();
     write_afrags<POL, NT>(rec + rl.Qf, 4, DK / 32, [&](int r, int d) {
-      return sGF[(r / 16) * DK + d] * sQ[r * PK + d];
+      return sGFe[(r / 16) * DK + d] * FT::load1(sQ, r, d);
     });
     write_afrags<POL, NT>(rec + rl.Kf, DK / 16, 2, [&](int d, int r) {
-      return sX[(r / 16) * DK + d] * (r < 48 ? sRk[r * PK + d] : sG[r * PK + d]);
+      return sXe[(r / 16) * DK + d] * FT::load1(r < 48 ? sRk : sG, r, d);
     });
     constexpr int NJ = (10 + NW - 1) / NW;  // block pairs per wavefront
+    // pair indices in order (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3);
+    // the three that carry a scale, (2,0) (3,0) (3,1), go to wavefronts 0..2
+    constexpr int kPairOrder[10] = {3, 6, 7, 0, 1, 2, 4, 5, 8, 9};
+    auto pair_of = [&](int j) { const int w = wave + NW * j; return w < 10 ? kPairOrder[w] : 10; };
     floatx4 acc[NJ][2];  // [pair of this wavefront][A, P]
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int pr = wave + NW * j;  // pairs in order (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) ...
+      const int pr = pair_of(j);  // pairs in order (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) ...
       acc[j][0] = acc[j][1] = floatx4{0.f, 0.f, 0.f, 0.f};
       if (pr < 10) {
         int R = 0, I = pr;
@@ -758,7 +826,7 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
     __syncthreads();  // every wavefront is done with the factors over A and P
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int pr = wave + NW * j;
+      const int pr = pair_of(j);
       if (pr < 10) {
         int R = 0, I = pr;
         while (I > R) { I -= R + 1; ++R; }
@@ -870,9 +938,9 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int r = 32 * kb + FI::kof(g, e);
-          const float gf = sGF[(r / 16) * DK + d];  // G_{16R}, or e^{G_{16R}} off the exact path
+          const float gf = (exact ? sGF : sGFe)[(r / 16) * DK + d];  // G_{16R}, or e^{G_{16R}} off the exact path
           if (exact) x[e] = sBeta[r] * (sK[r * PK + d] * pexp<POL>(gf + sG[r * PK + d]));
-          else x[e] = sBeta[r] * (sK[r * PK + d] * gf);
+          else x[e] = sBeta[r] * (FT::load1(sK, r, d) * gf);
         }
         fk[i] = FI::make_b(x);
       }

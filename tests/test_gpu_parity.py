@@ -263,6 +263,25 @@ def test_prefill_steep_decay_takes_exact_path():
     assert rel(r["state"], ref.state) < 1e-4
 
 
+@pytest.mark.parametrize("boundary", [20.0, 10.0])
+def test_prefill_steep_gate_on_block_first_rows(boundary):
+    """Softplus gate of about 5 on every row inside each 16-row block (a within-block span of 75, under
+    the guard of 80) and a steeper one on each block's first row.  With 20 a block's full decay is about
+    95 and the chunk takes the exact path; with 10 it is about 85 and the pivoted path keeps e^{T}
+    a normal fp32 number."""
+    w = small(torch.float32, lens=(150, 40), H=2, d=64, gate=I.GATE_SOFTPLUS, seed=33)
+    cu = w.cu_seqlens.tolist()
+    for n in range(w.N):
+        for t in range(cu[n], cu[n + 1]):
+            w.g[t] = boundary if (t - cu[n]) % 16 == 0 else 5.0
+    print(f"block-boundary gate {boundary}", flush=True)
+    r = gpu_layer_prefill(w)
+    ref = oracle_layer(w)
+    assert np.all(np.isfinite(r["o"].cpu().numpy()))
+    assert rel(r["o"], ref.o) < 1e-4
+    assert rel(r["state"], ref.state) < 1e-4
+
+
 @pytest.mark.parametrize("precision", [K.PREC_BF16X3, K.PREC_FP16])
 def test_prefill_packed_equals_alone_bitwise(precision):
     w = small(torch.bfloat16, lens=(100, 64, 3, 129), H=2, d=128, seed=41)
