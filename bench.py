@@ -135,8 +135,7 @@ def pmc_summary(fetch_csv, write_csv, command, precision):
     ff = copy_kib / f[copy] if copy else 1.0
     fw = copy_kib / w[find(w, "copyBuffer")] if copy else 1.0
     keys = {"chunk_intra": "chunk_intra_kernel", "chunk_scan": "chunk_scan_kernel",
-            "gated_rmsnorm": "gated_rmsnorm_kernel", "kda_rows (decode)": "kda_rows_kernel",
-            "chunk_table": "chunk_table_kernel"}
+            "gated_rmsnorm": "gated_rmsnorm_kernel", "kda_rows (decode)": "kda_rows_kernel"}
     out = {"command": command, "source_sha256": source_digest(), "precision": precision,
            "copy_calibration": {"kernel": copy, "bytes": COPY_BYTES, "fetch_kib": f.get(copy), "write_kib":
                                 w.get(find(w, "copyBuffer")), "fetch_scale": ff, "write_scale": fw},

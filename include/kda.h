@@ -201,8 +201,8 @@ const char* kda_last_error(void);
  * call, every kda_prefill_varlen call made by this thread records events[2i]
  * and events[2i+1] on its stream immediately before and after its kernel i,
  * for 2i+1 < count:
- *   i = 0 chunk table,  1 intra-chunk kernel,  2 inter-chunk scan (which also
- *   carries the conv state when `raw` is given).
+ *   i = 0 intra-chunk kernel,  1 inter-chunk scan (which also carries the conv
+ *   state when `raw` is given).
  * The events are caller-owned hipEvent_t handles, already created; the library
  * keeps only the pointer, which must stay valid while set.  count = 0 (events
  * may be NULL) turns the hook off.  Errors: KDA_E_ARG for a negative or odd

@@ -296,7 +296,7 @@ def gated_rmsnorm_out(o, z, w, eps, y):
 
 
 # kernels of one kda_prefill_varlen call, in the order the timing hook numbers them
-PREFILL_KERNELS = ("chunk_table", "chunk_intra", "chunk_scan")
+PREFILL_KERNELS = ("chunk_intra", "chunk_scan")
 
 
 def kda_set_timing_events(events):

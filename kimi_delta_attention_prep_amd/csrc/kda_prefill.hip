@@ -292,12 +292,12 @@ __host__ __device__ inline RecLayout rec_layout(int dk, int dv, int fb) {
 }
 static inline int frag_bytes(int precision) { return precision == POL_FP16 ? 16 : 32; }
 static inline int64_t max_chunks(int num_seqs, int64_t t_tot) { return t_tot / kChunk + num_seqs; }
-// chunk table, then a 1 KiB sink that absorbs stores of rows past a sequence's end
-static inline size_t table_bytes(int num_seqs) { return ((size_t)(num_seqs + 1) * 4 + 255) / 256 * 256 + 1024; }
+// workspace: a 1 KiB sink that absorbs stores of rows past a sequence's end, then the records
+constexpr size_t kSinkBytes = 1024;
 
 size_t prefill_workspace_bytes(int H, int dk, int dv, int precision, int num_seqs, int64_t t_tot) {
   const RecLayout rl = rec_layout(dk, dv, frag_bytes(precision));
-  return table_bytes(num_seqs) + (size_t)max_chunks(num_seqs, t_tot) * H * (size_t)rl.bytes;
+  return kSinkBytes + (size_t)max_chunks(num_seqs, t_tot) * H * (size_t)rl.bytes;
 }
 
 // raw rows and preamble parameters when the preamble runs inside the prompt kernels
@@ -317,44 +317,25 @@ struct PrefillArgs {
   const int32_t *cu, *slots;
   const float *q, *k, *v, *g, *beta;
   float *state, *o;
-  int32_t* chunk_off;  // [num_seqs + 1]
   float* sink;         // [256] target of stores that must not land in o
   uint8_t* recs;       // [max_chunks][H][rec bytes]
   int64_t rec_bytes;
 };
 
 // ---------------------------------------------------------------------------
-// chunk table: chunk_off[n] = sum_{m<n} ceil(len_m / 64)
+// Record slots, with no table: chunk i of sequence n lives in slot
+// base(n) + i, base(n) = floor(cu[n] / 64) + n.  From one sequence to the next
+// base grows by floor(cu[n+1] / 64) - floor(cu[n] / 64) + 1 >= ceil(len_n / 64),
+// so no two chunks share a slot, and the last slot is below T / 64 + num_seqs.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void chunk_table_kernel(const int32_t* cu, int num_seqs, int32_t* chunk_off) {
-  __shared__ int32_t s[256];
-  __shared__ int32_t carry;
-  if (threadIdx.x == 0) carry = 0;
-  __syncthreads();
-  for (int base = 0; base < num_seqs; base += 256) {
-    const int n = base + threadIdx.x;
-    const int32_t c = (n < num_seqs) ? (cu[n + 1] - cu[n] + kChunk - 1) / kChunk : 0;
-    s[threadIdx.x] = c;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {  // inclusive Hillis-Steele scan
-      const int32_t x = threadIdx.x >= off ? s[threadIdx.x - off] : 0;
-      __syncthreads();
-      s[threadIdx.x] += x;
-      __syncthreads();
-    }
-    if (n < num_seqs) chunk_off[n] = carry + s[threadIdx.x] - c;
-    __syncthreads();
-    if (threadIdx.x == 255) carry += s[255];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) chunk_off[num_seqs] = carry;
-}
+__device__ __forceinline__ int64_t slot_base(const int32_t* cu, int n) { return cu[n] / kChunk + n; }
 
-__device__ __forceinline__ int chunk_seq(const int32_t* chunk_off, int num_seqs, int c) {
-  int lo = 0, hi = num_seqs;  // largest n with chunk_off[n] <= c
+// the sequence whose slots include slot c: the largest n < num_seqs with base(n) <= c
+__device__ __forceinline__ int slot_seq(const int32_t* cu, int num_seqs, int64_t c) {
+  int lo = 0, hi = num_seqs;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (chunk_off[mid] <= c) lo = mid; else hi = mid;
+    if (slot_base(cu, mid) <= c) lo = mid; else hi = mid;
   }
   return lo;
 }
@@ -550,13 +531,12 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int c = blockIdx.x, h = blockIdx.y, H = p.H;
-  const int total = p.chunk_off[p.num_seqs];
-  if (c >= total) return;
-  const int n = chunk_seq(p.chunk_off, p.num_seqs, c);
+  const int n = slot_seq(p.cu, p.num_seqs, c);
+  const int64_t t0 = p.cu[n];
+  const int64_t start = t0 + (c - slot_base(p.cu, n)) * L;
+  if (start >= p.cu[n + 1]) return;  // a slot past the sequence's last chunk
   const int slot = p.slots ? p.slots[n] : n;
   if (slot < 0) return;  // the sequence is skipped: nothing of it is read or written
-  const int64_t t0 = p.cu[n];
-  const int64_t start = t0 + (int64_t)(c - p.chunk_off[n]) * L;
   const int len = (int)min((int64_t)L, (int64_t)p.cu[n + 1] - start);
   uint8_t* rec = p.recs + ((int64_t)c * H + h) * p.rec_bytes;
   const RecLayout rl = rec_layout(DK, DV, Frag<POL>::BYTES);
@@ -1189,7 +1169,8 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(PrefillArgs p, int grou
     put_s(r0, Sacc[s]);
   }
 
-  const int c_begin = p.chunk_off[n_seq], n = p.chunk_off[n_seq + 1] - c_begin;
+  const int64_t c_begin = slot_base(p.cu, n_seq);
+  const int n = (int)((p.cu[n_seq + 1] - p.cu[n_seq] + L - 1) / L);
   const int64_t seq_start = p.cu[n_seq], seq_end = p.cu[n_seq + 1];
   auto rec_of = [&](int i) { return p.recs + ((int64_t)(c_begin + i) * H + h) * p.rec_bytes; };
 
@@ -1281,20 +1262,14 @@ static hipError_t launch_prefill_t(const PrefillLaunch& Lc, hipStream_t s) {
   p.q = Lc.q_hat; p.k = Lc.k_hat; p.v = Lc.v; p.g = Lc.g; p.beta = Lc.beta; p.state = Lc.state; p.o = Lc.o;
   p.raw = {Lc.raw_q, Lc.raw_k, Lc.raw_v, Lc.raw_g, Lc.raw_beta, Lc.conv_w, Lc.cs_in, Lc.cs_out,
            Lc.act, Lc.gate_mode, Lc.lb, FUSED ? (int)sizeof(RawT) : 0};
-  p.chunk_off = static_cast<int32_t*>(Lc.workspace);
-  p.sink = reinterpret_cast<float*>(static_cast<uint8_t*>(Lc.workspace) + table_bytes(Lc.num_seqs) - 1024);
-  p.recs = static_cast<uint8_t*>(Lc.workspace) + table_bytes(Lc.num_seqs);
+  p.sink = static_cast<float*>(Lc.workspace);
+  p.recs = static_cast<uint8_t*>(Lc.workspace) + kSinkBytes;
   p.rec_bytes = rec_layout(DK, DV, Frag<POL>::BYTES).bytes;
   // measurement hook: an event just before / after kernel i
   auto mark = [&](int i, int end) -> hipError_t {
     return 2 * i + 1 < Lc.nevents ? hipEventRecord(Lc.events[2 * i + end], s) : hipSuccess;
   };
-  hipError_t e = mark(0, 0);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(256), 0, s, Lc.cu_seqlens, Lc.num_seqs, p.chunk_off);
-  e = hipGetLastError();
-  if (e == hipSuccess) e = mark(0, 1);
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
   const int64_t mc = max_chunks(Lc.num_seqs, Lc.t_tot);
   constexpr size_t intra_bytes = IntraSmem<DK, DV>::BYTES;
   constexpr size_t scan_bytes = ScanSmem<DK, POL>::BYTES;
@@ -1305,18 +1280,18 @@ static hipError_t launch_prefill_t(const PrefillLaunch& Lc, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  e = mark(1, 0);
+  e = mark(0, 0);
   if (e != hipSuccess) return e;
-  if (mc > 0 && Lc.t_tot > 0) {
+  if (mc > 0 && Lc.t_tot > 0 && Lc.num_seqs > 0) {
     hipLaunchKernelGGL((chunk_intra_kernel<DK, DV, POL, RawT, FUSED>), dim3((unsigned)mc, (unsigned)Lc.H), dim3(kIntraThreads),
                        intra_bytes, s, p);
     e = hipGetLastError();
   }
-  if (e == hipSuccess) e = mark(1, 1);
+  if (e == hipSuccess) e = mark(0, 1);
   if (e != hipSuccess) return e;
   // (the conv-state carry of a fused call runs inside the scan kernel)
   const int groups = Lc.num_seqs * Lc.H;
-  e = mark(2, 0);
+  e = mark(1, 0);
   if (e != hipSuccess) return e;
   if (groups > 0) {
     const int nsplit = DV / 16;
@@ -1324,7 +1299,7 @@ static hipError_t launch_prefill_t(const PrefillLaunch& Lc, hipStream_t s) {
     hipLaunchKernelGGL((chunk_scan_kernel<DK, DV, POL>), dim3((unsigned)wgs), dim3(256), scan_bytes, s, p, groups);
     e = hipGetLastError();
   }
-  if (e == hipSuccess) e = mark(2, 1);
+  if (e == hipSuccess) e = mark(1, 1);
   return e;
 }
 
