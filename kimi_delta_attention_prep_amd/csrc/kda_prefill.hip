@@ -1033,12 +1033,14 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
 // ---------------------------------------------------------------------------
 // inter-chunk scan
 //
-// Workgroup = (sequence, head, 16 state columns j0..j0+15), 4 wavefronts.
-// Wavefront w owns chunk rows 16w..16w+15 of U and O and state rows
-// 16*(w*DK/64 + s) + 0..15 (s < DK/64), kept as fp32 matrix-core accumulators.
-// Per chunk c, with S_c^T and U_c^T slices shared through LDS:
-//   phase 1 (S_c complete):  U_c = U~_c - W_c S_c,  O_c = Q^gamma_c S_c   (one read of S_c^T)
-//   phase 2 (U_c complete):  S_{c+1} = gamma_L . S_c + K_<^T U_c,  O_c += P_c U_c   (one read of U_c^T)
+// Workgroup = (sequence, head, 16 state columns j0..j0+15), 8 wavefronts in two
+// roles, so that only the state recurrence sits on the serial path.  State
+// wavefront w (0..3) owns chunk rows 16w..16w+15 of U and state rows
+// 16*(w*DK/64 + s) + 0..15 (s < DK/64), kept as fp32 matrix-core accumulators;
+// output wavefront 4 + w owns chunk rows 16w..16w+15 of O.  Per chunk c, with
+// S_c^T and U_c^T slices shared through LDS:
+//   phase 1 (S_c complete):  U_c = U~_c - W_c S_c  (state),  O_c = Q^gamma_c S_c  (output)
+//   phase 2 (U_c complete):  S_{c+1} = gamma_L . S_c + K_<^T U_c  (state),  O_c += P_c U_c  (output)
 // Phase 1 reads S^T and writes U^T; phase 2 reads U^T and writes S^T; the two
 // barriers per chunk order every write after the last read of the old
 // contents, so one buffer of each suffices.  Each wavefront keeps NS register
@@ -1054,16 +1056,16 @@ struct ScanSmem {
   static constexpr size_t BYTES = (size_t)(NP * S_PLANE + NP * U_PLANE) * sizeof(P);
 };
 
-// one chunk's operand fragments of one wavefront
+// one chunk's operand fragments of a state wavefront: the state chain's
+// operands (W, U~, K_<^T, gamma_L)
 template <int DK, int POL>
-struct ScanFrags {
+struct StateFrags {
   using F = Frag<POL>;
   static constexpr int KB = DK / 32, MS = DK / 64;
-  typename F::A w[KB], q[KB], k[MS][2], pp[2];
+  typename F::A w[KB], k[MS][2];
   floatx4 ut;
   float4 gl[MS];
-  // the state chain's operands (W, U~, K_<^T, gamma_L)
-  __device__ void load_state(const uint8_t* rec, const RecLayout& rl, int w4, int lane, int split) {
+  __device__ void load(const uint8_t* rec, const RecLayout& rl, int w4, int lane, int split) {
     constexpr int FB = F::BYTES;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) w[kb] = F::load_a(rec + rl.Wf + ((int64_t)(w4 * KB + kb) * 64 + lane) * FB);
@@ -1077,13 +1079,21 @@ struct ScanFrags {
     for (int s = 0; s < MS; ++s)
       gl[s] = *reinterpret_cast<const float4*>(rec + rl.gL + (int64_t)(16 * (w4 * MS + s) + 4 * (lane >> 4)) * 4);
   }
-  // the output's operands (Q^gamma, P)
-  __device__ void load_out(const uint8_t* rec, const RecLayout& rl, int w4, int lane) {
+};
+
+// one chunk's operand fragments of an output wavefront (Q^gamma, and P up to
+// the diagonal: row block w4 needs chunk rows < 16 (w4 + 1))
+template <int DK, int POL>
+struct OutFrags {
+  using F = Frag<POL>;
+  static constexpr int KB = DK / 32;
+  typename F::A q[KB], pp[2];
+  __device__ void load(const uint8_t* rec, const RecLayout& rl, int w4, int lane) {
     constexpr int FB = F::BYTES;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) q[kb] = F::load_a(rec + rl.Qf + ((int64_t)(w4 * KB + kb) * 64 + lane) * FB);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) pp[kb] = F::load_a(rec + rl.Pf + ((int64_t)(w4 * 2 + kb) * 64 + lane) * FB);
+    pp[0] = F::load_a(rec + rl.Pf + ((int64_t)(w4 * 2) * 64 + lane) * FB);
+    if (w4 >= 2) pp[1] = F::load_a(rec + rl.Pf + ((int64_t)(w4 * 2 + 1) * 64 + lane) * FB);
   }
 };
 
@@ -1127,7 +1137,7 @@ __device__ __forceinline__ void carry_conv_state(const PrefillArgs& p, int n, in
 }
 
 template <int DK, int DV, int POL>
-__global__ __launch_bounds__(256) void chunk_scan_kernel(PrefillArgs p, int groups) {
+__global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillArgs p, int groups) {
   using SM = ScanSmem<DK, POL>;
   using F = Frag<POL>;
   using P = typename F::P;
@@ -1145,7 +1155,7 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(PrefillArgs p, int grou
   const int H = p.H, n_seq = grp / H, h = grp % H;
   const int slot = p.slots ? p.slots[n_seq] : n_seq;
   if (slot < 0) return;
-  const int t = threadIdx.x, lane = t & 63, w4 = t >> 6;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, w4 = wave & 3;
   const int col = lane & 15, g4 = lane >> 4;
   const int j0 = 16 * split;
   if (p.raw.esize) carry_conv_state<DK, DV>(p, n_seq, slot, h * NSPLIT + split, H * NSPLIT);
@@ -1160,95 +1170,118 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(PrefillArgs p, int grou
   auto get_s = [&](int kb) { return F::load_b(sS0 + col * PS + 32 * kb, sS1 + col * PS + 32 * kb, g4); };
   auto get_u = [&](int kb) { return F::load_b(sU0 + col * PU + 32 * kb, sU1 + col * PU + 32 * kb, g4); };
 
-  floatx4 Sacc[MS];
-#pragma unroll
-  for (int s = 0; s < MS; ++s) {
-    const int r0 = 16 * (w4 * MS + s) + 4 * g4;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) Sacc[s][v] = Sg[(int64_t)(r0 + v) * DV + j0 + col];
-    put_s(r0, Sacc[s]);
-  }
-
   const int64_t c_begin = slot_base(p.cu, n_seq);
   const int n = (int)((p.cu[n_seq + 1] - p.cu[n_seq] + L - 1) / L);
   const int64_t seq_start = p.cu[n_seq], seq_end = p.cu[n_seq + 1];
   auto rec_of = [&](int i) { return p.recs + ((int64_t)(c_begin + i) * H + h) * p.rec_bytes; };
-
-  ScanFrags<DK, POL> fr[NS];
   // Every load is unconditional (indices clamped to the last chunk), so the
   // compiler can count outstanding loads exactly and wait only for the set a
   // chunk needs.
   auto clampc = [&](int j) { return j < n ? j : n - 1; };
-  if (n > 0) {
-#pragma unroll
-    for (int j = 0; j < NS - 1; ++j) {
-      fr[j].load_state(rec_of(clampc(j)), rl, w4, lane, split);
-      fr[j].load_out(rec_of(clampc(j)), rl, w4, lane);
-    }
-  }
+  // Both roles walk the chunks in step, two barriers per chunk:
+  //   A: S_c^T complete (and every read of U_{c-1}^T done),
+  //   B: U_c^T complete (and every read of S_c^T done).
   // Accumulation chains are split in two (even and odd K blocks, or the two
   // halves of a sum) and the independent chains are interleaved, so the matrix
   // cores always have a product to issue while a chain waits on its last one.
-  auto iter = [&](int c, const ScanFrags<DK, POL>& cur, ScanFrags<DK, POL>& ahead) {
-    __syncthreads();  // S_c^T complete; the last chunk's reads of U^T are done
-    typename F::B bs[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) bs[kb] = get_s(kb);
-    const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
-    floatx4 acc[2] = {z4, z4}, ao[2] = {z4, z4};
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      acc[kb & 1] = F::mma(acc[kb & 1], cur.w[kb], bs[kb]);
-      ao[kb & 1] = F::mma(ao[kb & 1], cur.q[kb], bs[kb]);
-    }
-    floatx4 u;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) u[v] = cur.ut[v] - (acc[0][v] + acc[1][v]);
-    put_u(16 * w4 + 4 * g4, u);
-    ahead.load_state(rec_of(clampc(c + NS - 1)), rl, w4, lane, split);
-    __syncthreads();  // U_c^T complete; every read of S_c^T is done
-    const typename F::B u0 = get_u(0), u1 = get_u(1);
-    floatx4 sk[MS];
+  const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
+  if (wave < 4) {
+    // state wavefronts: U_c = U~_c - W_c S_c, then S_{c+1} = gamma_L . S_c + K_<^T U_c
+    floatx4 Sacc[MS];
 #pragma unroll
     for (int s = 0; s < MS; ++s) {
-      const float4 gl = cur.gl[s];
-      Sacc[s][0] *= gl.x; Sacc[s][1] *= gl.y; Sacc[s][2] *= gl.z; Sacc[s][3] *= gl.w;
-      Sacc[s] = F::mma(Sacc[s], cur.k[s][0], u0);
-      sk[s] = F::mma(z4, cur.k[s][1], u1);
+      const int r0 = 16 * (w4 * MS + s) + 4 * g4;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) Sacc[s][v] = Sg[(int64_t)(r0 + v) * DV + j0 + col];
+      put_s(r0, Sacc[s]);
     }
-    // P is lower triangular: row block w4 needs chunk rows < 16(w4+1)
-    ao[0] = F::mma(ao[0], cur.pp[0], u0);
-    if (w4 >= 2) ao[1] = F::mma(ao[1], cur.pp[1], u1);
+    StateFrags<DK, POL> fr[NS];
+    if (n > 0) {
+#pragma unroll
+      for (int j = 0; j < NS - 1; ++j) fr[j].load(rec_of(clampc(j)), rl, w4, lane, split);
+    }
+    auto iter = [&](int c, const StateFrags<DK, POL>& cur, StateFrags<DK, POL>& ahead) {
+      __syncthreads();  // A
+      typename F::B bs[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) bs[kb] = get_s(kb);
+      floatx4 acc[2] = {z4, z4};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) acc[kb & 1] = F::mma(acc[kb & 1], cur.w[kb], bs[kb]);
+      floatx4 u;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) u[v] = cur.ut[v] - (acc[0][v] + acc[1][v]);
+      put_u(16 * w4 + 4 * g4, u);
+      ahead.load(rec_of(clampc(c + NS - 1)), rl, w4, lane, split);
+      __syncthreads();  // B
+      const typename F::B u0 = get_u(0), u1 = get_u(1);
+      floatx4 sk[MS];
+#pragma unroll
+      for (int s = 0; s < MS; ++s) {
+        const float4 gl = cur.gl[s];
+        Sacc[s][0] *= gl.x; Sacc[s][1] *= gl.y; Sacc[s][2] *= gl.z; Sacc[s][3] *= gl.w;
+        Sacc[s] = F::mma(Sacc[s], cur.k[s][0], u0);
+        sk[s] = F::mma(z4, cur.k[s][1], u1);
+      }
+#pragma unroll
+      for (int s = 0; s < MS; ++s) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) Sacc[s][v] += sk[s][v];
+        put_s(16 * (w4 * MS + s) + 4 * g4, Sacc[s]);
+      }
+    };
+    const int full = n / NS * NS;
+    for (int base = 0; base < full; base += NS) {
+#pragma unroll
+      for (int u = 0; u < NS; ++u) iter(base + u, fr[u], fr[(u + NS - 1) % NS]);
+    }
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u)
+      if (full + u < n) iter(full + u, fr[u], fr[(u + NS - 1) % NS]);
 #pragma unroll
     for (int s = 0; s < MS; ++s) {
+      const int r0 = 16 * (w4 * MS + s) + 4 * g4;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) Sacc[s][v] += sk[s][v];
-      put_s(16 * (w4 * MS + s) + 4 * g4, Sacc[s]);
+      for (int v = 0; v < 4; ++v) Sg[(int64_t)(r0 + v) * DV + j0 + col] = Sacc[s][v];
     }
-    ahead.load_out(rec_of(clampc(c + NS - 1)), rl, w4, lane);
-    const int64_t start = seq_start + (int64_t)c * L;
-    const int len = (int)min((int64_t)L, seq_end - start);
-    // stores are unconditional: rows past the sequence go to the sink
+  } else {
+    // output wavefronts: O_c = Q^gamma_c S_c + P_c U_c, rows 16 w4 .. 16 w4 + 15
+    OutFrags<DK, POL> fr[NS];
+    if (n > 0) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int rr = 16 * w4 + 4 * g4 + v;
-      float* dst = rr < len ? &p.o[((start + rr) * H + h) * DV + j0 + col] : &p.sink[lane * 4 + v];
-      *dst = ao[0][v] + ao[1][v];
+      for (int j = 0; j < NS - 1; ++j) fr[j].load(rec_of(clampc(j)), rl, w4, lane);
     }
-  };
-  const int full = n / NS * NS;
-  for (int base = 0; base < full; base += NS) {
+    auto iter = [&](int c, const OutFrags<DK, POL>& cur, OutFrags<DK, POL>& ahead) {
+      __syncthreads();  // A
+      typename F::B bs[KB];
 #pragma unroll
-    for (int u = 0; u < NS; ++u) iter(base + u, fr[u], fr[(u + NS - 1) % NS]);
-  }
+      for (int kb = 0; kb < KB; ++kb) bs[kb] = get_s(kb);
+      floatx4 ao[2] = {z4, z4};
 #pragma unroll
-  for (int u = 0; u < NS - 1; ++u)
-    if (full + u < n) iter(full + u, fr[u], fr[(u + NS - 1) % NS]);
+      for (int kb = 0; kb < KB; ++kb) ao[kb & 1] = F::mma(ao[kb & 1], cur.q[kb], bs[kb]);
+      ahead.load(rec_of(clampc(c + NS - 1)), rl, w4, lane);
+      __syncthreads();  // B
+      const typename F::B u0 = get_u(0);
+      ao[0] = F::mma(ao[0], cur.pp[0], u0);
+      if (w4 >= 2) ao[1] = F::mma(ao[1], cur.pp[1], get_u(1));  // P is lower triangular
+      const int64_t start = seq_start + (int64_t)c * L;
+      const int len = (int)min((int64_t)L, seq_end - start);
+      // stores are unconditional: rows past the sequence go to the sink
 #pragma unroll
-  for (int s = 0; s < MS; ++s) {
-    const int r0 = 16 * (w4 * MS + s) + 4 * g4;
+      for (int v = 0; v < 4; ++v) {
+        const int rr = 16 * w4 + 4 * g4 + v;
+        float* dst = rr < len ? &p.o[((start + rr) * H + h) * DV + j0 + col] : &p.sink[lane * 4 + v];
+        *dst = ao[0][v] + ao[1][v];
+      }
+    };
+    const int full = n / NS * NS;
+    for (int base = 0; base < full; base += NS) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) Sg[(int64_t)(r0 + v) * DV + j0 + col] = Sacc[s][v];
+      for (int u = 0; u < NS; ++u) iter(base + u, fr[u], fr[(u + NS - 1) % NS]);
+    }
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u)
+      if (full + u < n) iter(full + u, fr[u], fr[(u + NS - 1) % NS]);
   }
 }
 
@@ -1296,7 +1329,7 @@ static hipError_t launch_prefill_t(const PrefillLaunch& Lc, hipStream_t s) {
   if (groups > 0) {
     const int nsplit = DV / 16;
     const int wgs = (groups + 7) / 8 * 8 * nsplit;
-    hipLaunchKernelGGL((chunk_scan_kernel<DK, DV, POL>), dim3((unsigned)wgs), dim3(256), scan_bytes, s, p, groups);
+    hipLaunchKernelGGL((chunk_scan_kernel<DK, DV, POL>), dim3((unsigned)wgs), dim3(512), scan_bytes, s, p, groups);
     e = hipGetLastError();
   }
   if (e == hipSuccess) e = mark(1, 1);
