@@ -1065,19 +1065,30 @@ struct StateFrags {
   typename F::A w[KB], k[MS][2];
   floatx4 ut;
   float4 gl[MS];
-  __device__ void load(const uint8_t* rec, const RecLayout& rl, int w4, int lane, int split) {
+  // in three groups, so that each iteration can spread its loads over the chunk
+  __device__ void load_w(const uint8_t* rec, const RecLayout& rl, int w4, int lane) {
     constexpr int FB = F::BYTES;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) w[kb] = F::load_a(rec + rl.Wf + ((int64_t)(w4 * KB + kb) * 64 + lane) * FB);
+  }
+  __device__ void load_ug(const uint8_t* rec, const RecLayout& rl, int w4, int lane, int split) {
     ut = *reinterpret_cast<const floatx4*>(rec + rl.Ut + ((int64_t)(split * 4 + w4) * 64 + lane) * 16);
+#pragma unroll
+    for (int s = 0; s < MS; ++s)
+      gl[s] = *reinterpret_cast<const float4*>(rec + rl.gL + (int64_t)(16 * (w4 * MS + s) + 4 * (lane >> 4)) * 4);
+  }
+  __device__ void load_k(const uint8_t* rec, const RecLayout& rl, int w4, int lane) {
+    constexpr int FB = F::BYTES;
 #pragma unroll
     for (int s = 0; s < MS; ++s)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
         k[s][kb] = F::load_a(rec + rl.Kf + ((int64_t)((w4 * MS + s) * 2 + kb) * 64 + lane) * FB);
-#pragma unroll
-    for (int s = 0; s < MS; ++s)
-      gl[s] = *reinterpret_cast<const float4*>(rec + rl.gL + (int64_t)(16 * (w4 * MS + s) + 4 * (lane >> 4)) * 4);
+  }
+  __device__ void load(const uint8_t* rec, const RecLayout& rl, int w4, int lane, int split) {
+    load_w(rec, rl, w4, lane);
+    load_ug(rec, rl, w4, lane, split);
+    load_k(rec, rl, w4, lane);
   }
 };
 
@@ -1088,12 +1099,19 @@ struct OutFrags {
   using F = Frag<POL>;
   static constexpr int KB = DK / 32;
   typename F::A q[KB], pp[2];
-  __device__ void load(const uint8_t* rec, const RecLayout& rl, int w4, int lane) {
+  __device__ void load_q(const uint8_t* rec, const RecLayout& rl, int w4, int lane) {
     constexpr int FB = F::BYTES;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) q[kb] = F::load_a(rec + rl.Qf + ((int64_t)(w4 * KB + kb) * 64 + lane) * FB);
+  }
+  __device__ void load_p(const uint8_t* rec, const RecLayout& rl, int w4, int lane) {
+    constexpr int FB = F::BYTES;
     pp[0] = F::load_a(rec + rl.Pf + ((int64_t)(w4 * 2) * 64 + lane) * FB);
     if (w4 >= 2) pp[1] = F::load_a(rec + rl.Pf + ((int64_t)(w4 * 2 + 1) * 64 + lane) * FB);
+  }
+  __device__ void load(const uint8_t* rec, const RecLayout& rl, int w4, int lane) {
+    load_q(rec, rl, w4, lane);
+    load_p(rec, rl, w4, lane);
   }
 };
 
@@ -1201,10 +1219,16 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillArgs p, int grou
       for (int j = 0; j < NS - 1; ++j) fr[j].load(rec_of(clampc(j)), rl, w4, lane, split);
     }
     auto iter = [&](int c, const StateFrags<DK, POL>& cur, StateFrags<DK, POL>& ahead) {
+      // the next-but-one chunk's operands load in three groups (W while S_c^T is
+      // read, U~ and gamma after U is written, K_<^T while U_c^T is read), so no
+      // group waits long for the CU's load path
+      const uint8_t* nrec = rec_of(clampc(c + NS - 1));
       __syncthreads();  // A
       typename F::B bs[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) bs[kb] = get_s(kb);
+      ahead.load_w(nrec, rl, w4, lane);
+      __builtin_amdgcn_sched_barrier(0);
       floatx4 acc[2] = {z4, z4};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) acc[kb & 1] = F::mma(acc[kb & 1], cur.w[kb], bs[kb]);
@@ -1212,9 +1236,12 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillArgs p, int grou
 #pragma unroll
       for (int v = 0; v < 4; ++v) u[v] = cur.ut[v] - (acc[0][v] + acc[1][v]);
       put_u(16 * w4 + 4 * g4, u);
-      ahead.load(rec_of(clampc(c + NS - 1)), rl, w4, lane, split);
+      __builtin_amdgcn_sched_barrier(0);
+      ahead.load_ug(nrec, rl, w4, lane, split);
       __syncthreads();  // B
       const typename F::B u0 = get_u(0), u1 = get_u(1);
+      ahead.load_k(nrec, rl, w4, lane);
+      __builtin_amdgcn_sched_barrier(0);
       floatx4 sk[MS];
 #pragma unroll
       for (int s = 0; s < MS; ++s) {
@@ -1259,7 +1286,9 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillArgs p, int grou
       floatx4 ao[2] = {z4, z4};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) ao[kb & 1] = F::mma(ao[kb & 1], cur.q[kb], bs[kb]);
-      ahead.load(rec_of(clampc(c + NS - 1)), rl, w4, lane);
+      const uint8_t* nrec = rec_of(clampc(c + NS - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      ahead.load_q(nrec, rl, w4, lane);
       __syncthreads();  // B
       const typename F::B u0 = get_u(0);
       ao[0] = F::mma(ao[0], cur.pp[0], u0);
@@ -1273,6 +1302,8 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillArgs p, int grou
         float* dst = rr < len ? &p.o[((start + rr) * H + h) * DV + j0 + col] : &p.sink[lane * 4 + v];
         *dst = ao[0][v] + ao[1][v];
       }
+      __builtin_amdgcn_sched_barrier(0);
+      ahead.load_p(nrec, rl, w4, lane);
     };
     const int full = n / NS * NS;
     for (int base = 0; base < full; base += NS) {
