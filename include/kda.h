@@ -38,8 +38,8 @@
  *     the sequence: nothing of it is read or written.
  *   - Alignment: buffers the kernels move with 128-bit accesses must be 16-byte
  *     aligned: the state, the fp32 rows q_hat/k_hat/v/g of the prompt path, the
- *     raw q/k/v/g rows handed to kda_prefill_varlen in `raw`, the outputs o of
- *     decode and verify, a log's u, and every buffer of gated_rmsnorm_out.  Every other pointer needs its element alignment.
+ *     raw q/k/v/g rows handed to kda_prefill_varlen in `raw`, the output o of
+ *     every call, a log's u, and every buffer of gated_rmsnorm_out.  Every other pointer needs its element alignment.
  *   - Errors: each call returns KDA_OK or one KDA_E_* code.  All validation
  *     happens before the first launch; on error nothing is enqueued and no
  *     output is written.  kda_last_error() gives a message (thread-local).

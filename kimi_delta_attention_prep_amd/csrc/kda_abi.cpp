@@ -156,7 +156,7 @@ int kda_prefill_varlen(const kda_dims* d, int32_t num_seqs, int64_t t_tot, const
       KDA_TRY(check_ptrs("kda_prefill_varlen", {q_hat, k_hat, v, g}));
       KDA_TRY(check_ptrs("kda_prefill_varlen", {beta}, 4));
     }
-    KDA_TRY(check_ptrs("kda_prefill_varlen: o", {o}, 4));
+    KDA_TRY(check_ptrs("kda_prefill_varlen: o", {o}));
   }
   const size_t need =
       kda::prefill_workspace_bytes(d->num_heads, d->head_dim_k, d->head_dim_v, d->precision, num_seqs, t_tot);

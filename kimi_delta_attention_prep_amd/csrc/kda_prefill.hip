@@ -117,6 +117,13 @@ struct Frag<POL_FP32> {
     for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], acc, 0, 0, 0);
     return acc;
   }
+  // the transposed product (A B)^T = B^T A^T from the same registers: a B fragment
+  // holds B^T in the A layout and an A fragment holds A^T in the B layout
+  __device__ static floatx4 mma_t(floatx4 acc, const B& b, const A& a) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(b.v[e], a.v[e], acc, 0, 0, 0);
+    return acc;
+  }
   // B operand kept in LDS as one fp32 plane [16 columns][K]: 4 consecutive K values per write
   using P = float;
   static constexpr int PLANES = 1;
@@ -160,6 +167,11 @@ struct Frag<POL_BF16X3> {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, acc, 0, 0, 0);
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
+  }
+  __device__ static floatx4 mma_t(floatx4 acc, const B& b, const A& a) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b.hi, a.lo, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b.lo, a.hi, acc, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(b.hi, a.hi, acc, 0, 0, 0);
   }
   // B operand kept in LDS already split: hi and lo planes [16 columns][K] of bf16
   using P = __bf16;
@@ -214,6 +226,10 @@ struct Frag<POL_FP16> {
   __device__ static floatx4 mma(floatx4 acc, const A& a, const B& b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.v, b.lo, acc, 0, 0, 0);
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a.v, b.hi, acc, 0, 0, 0);
+  }
+  __device__ static floatx4 mma_t(floatx4 acc, const B& b, const A& a) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(b.lo, a.v, acc, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(b.hi, a.v, acc, 0, 0, 0);
   }
   // B operand kept in LDS already split: hi and lo planes [16 columns][K] of fp16
   using P = _Float16;
@@ -1272,7 +1288,9 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillArgs p, int grou
       for (int v = 0; v < 4; ++v) Sg[(int64_t)(r0 + v) * DV + j0 + col] = Sacc[s][v];
     }
   } else {
-    // output wavefronts: O_c = Q^gamma_c S_c + P_c U_c, rows 16 w4 .. 16 w4 + 15
+    // output wavefronts: O_c = Q^gamma_c S_c + P_c U_c for chunk rows 16 w4 .. 16 w4 + 15,
+    // formed transposed, O^T = S^T Q^gamma^T + U^T P^T, from the same fragments: lane l
+    // then holds 4 consecutive columns of row 16 w4 + l % 16 (one 16-byte store)
     OutFrags<DK, POL> fr[NS];
     if (n > 0) {
 #pragma unroll
@@ -1285,23 +1303,20 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillArgs p, int grou
       for (int kb = 0; kb < KB; ++kb) bs[kb] = get_s(kb);
       floatx4 ao[2] = {z4, z4};
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) ao[kb & 1] = F::mma(ao[kb & 1], cur.q[kb], bs[kb]);
+      for (int kb = 0; kb < KB; ++kb) ao[kb & 1] = F::mma_t(ao[kb & 1], bs[kb], cur.q[kb]);
       const uint8_t* nrec = rec_of(clampc(c + NS - 1));
       __builtin_amdgcn_sched_barrier(0);
       ahead.load_q(nrec, rl, w4, lane);
       __syncthreads();  // B
       const typename F::B u0 = get_u(0);
-      ao[0] = F::mma(ao[0], cur.pp[0], u0);
-      if (w4 >= 2) ao[1] = F::mma(ao[1], cur.pp[1], get_u(1));  // P is lower triangular
+      ao[0] = F::mma_t(ao[0], u0, cur.pp[0]);
+      if (w4 >= 2) ao[1] = F::mma_t(ao[1], get_u(1), cur.pp[1]);  // P is lower triangular
       const int64_t start = seq_start + (int64_t)c * L;
       const int len = (int)min((int64_t)L, seq_end - start);
       // stores are unconditional: rows past the sequence go to the sink
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int rr = 16 * w4 + 4 * g4 + v;
-        float* dst = rr < len ? &p.o[((start + rr) * H + h) * DV + j0 + col] : &p.sink[lane * 4 + v];
-        *dst = ao[0][v] + ao[1][v];
-      }
+      const int rr = 16 * w4 + col;
+      float* dst = rr < len ? &p.o[((start + rr) * H + h) * DV + j0 + 4 * g4] : &p.sink[lane * 4];
+      *reinterpret_cast<floatx4*>(dst) = ao[0] + ao[1];
       __builtin_amdgcn_sched_barrier(0);
       ahead.load_p(nrec, rl, w4, lane);
     };

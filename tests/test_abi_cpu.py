@@ -115,6 +115,9 @@ def test_prep_and_prefill_checks(lib):
     assert pf(A, need - 1) == K.KDA_E_WORKSPACE
     assert pf(None, need) == K.KDA_E_WORKSPACE
     assert pf(ctypes.c_void_p(0x10010), need) == K.KDA_E_ALIGN
+    # o is written with 16-byte stores: an element-aligned o is refused
+    assert lib.kda_prefill_varlen(ctypes.byref(d), 2, 1000, A, None, A, A, A, A, A, None, A, MIS4, A, need,
+                                  None) == K.KDA_E_ALIGN
     assert lib.kda_prefill_workspace_bytes(ctypes.byref(dims(dk=96)), 2, 1000) == 0
 
 
