@@ -682,14 +682,18 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
   __syncthreads();
 
   // 2. per (block R, key dim d): gl_r = sum of g over rows 16R+1..r (block-local prefix)
-  if (t < 4 * DK) {
+  if (t < 4 * DK) {  // the block's 16 values are read at once, then summed in registers
     const int R = t / DK, d = t % DK;
-    sG0[R * DK + d] = sG[(16 * R) * PK + d];
+    float gv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) gv[i] = sG[(16 * R + i) * PK + d];
+    sG0[R * DK + d] = gv[0];
     sG[(16 * R) * PK + d] = 0.f;
     float run = 0.f;
-    for (int r = 16 * R + 1; r < 16 * R + 16; ++r) {
-      run += sG[r * PK + d];
-      sG[r * PK + d] = run;
+#pragma unroll
+    for (int i = 1; i < 16; ++i) {
+      run += gv[i];
+      sG[(16 * R + i) * PK + d] = run;
     }
     if (-run > kSpanGuard) atomicOr(sFlag, 1);  // the block's decay span G_{16R} - G_{16R+15}
   }
@@ -699,42 +703,39 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
   //    e^{G_{16R} - G_{16I+16}} for the off-diagonal block pairs, and gamma_L; for the
   //    pivoted path also e^{G_{16R}}, e^{G_last - G_{16I+16}} (I < 3) or e^{G_last - G_48},
   //    and e^{T_I}.  Both sets are written: which path the chunk takes is known after
-  //    the barrier.
-  if (t < DK) {
-    const int d = t;
+  //    the barrier.  One thread per (block R, key dim d); every sum runs over J in order.
+  if (t < 4 * DK) {
+    const int R = t / DK, d = t % DK;
     float T[3];
 #pragma unroll
-    for (int R = 0; R < 3; ++R) T[R] = sG[(16 * R + 15) * PK + d] + sG0[(R + 1) * DK + d];
+    for (int J = 0; J < 3; ++J) T[J] = sG[(16 * J + 15) * PK + d] + sG0[(J + 1) * DK + d];
     const int Rl = (len - 1) / 16;
     const float glL = sG[(len - 1) * PK + d];
-    float gf = sG0[d];
-    bool steep = false;
-#pragma unroll
-    for (int R = 0; R < 4; ++R) {
-      sGF[R * DK + d] = gf;
-      sGFe[R * DK + d] = pexp<POL>(gf);
-      float x = 0.f;  // G_last - G_{16R}: blocks past the last row hold only zero rows
-      if (R <= Rl) {
-        x = glL;
-        for (int J = R; J < Rl; ++J) x += T[J];
-      }
-      sX[R * DK + d] = x;
-      sXe[R * DK + d] = pexp<POL>(R < 3 ? x - T[R] : x);
-      for (int I = 0; I + 1 < R; ++I) {
-        float dd = 0.f;
-        for (int J = I + 1; J < R; ++J) dd += T[J];
-        sD[pair_index(R, I) * DK + d] = pexp<POL>(dd);
-      }
-      if (R < 3) {
-        sET[R * DK + d] = pexp<POL>(T[R]);
-        steep |= -T[R] > kBlockDecayGuard;
-        gf += T[R];
-      }
+    const float g0 = sG0[d];
+    float gf = g0;  // G_{16R}
+    for (int J = 0; J < R; ++J) gf += T[J];
+    sGF[R * DK + d] = gf;
+    sGFe[R * DK + d] = pexp<POL>(gf);
+    float x = 0.f;  // G_last - G_{16R}: blocks past the last row hold only zero rows
+    if (R <= Rl) {
+      x = glL;
+      for (int J = R; J < Rl; ++J) x += T[J];
     }
-    if (steep) atomicOr(sFlag, 1);
-    float glast = sG0[d];
-    for (int J = 0; J < Rl; ++J) glast += T[J];
-    reinterpret_cast<float*>(rec + rl.gL)[d] = pexp<POL>(glast + glL);
+    sX[R * DK + d] = x;
+    sXe[R * DK + d] = pexp<POL>(R < 3 ? x - T[R] : x);
+    for (int I = 0; I + 1 < R; ++I) {
+      float dd = 0.f;
+      for (int J = I + 1; J < R; ++J) dd += T[J];
+      sD[pair_index(R, I) * DK + d] = pexp<POL>(dd);
+    }
+    if (R < 3) {
+      sET[R * DK + d] = pexp<POL>(T[R]);
+      if (-T[R] > kBlockDecayGuard) atomicOr(sFlag, 1);
+    } else {
+      float glast = g0;
+      for (int J = 0; J < Rl; ++J) glast += T[J];
+      reinterpret_cast<float*>(rec + rl.gL)[d] = pexp<POL>(glast + glL);
+    }
   }
   __syncthreads();
   const bool exact = sFlag[0] != 0;
