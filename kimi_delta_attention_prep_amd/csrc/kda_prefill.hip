@@ -519,6 +519,27 @@ __device__ __forceinline__ void pair_mma(floatx4& acc_a, floatx4& acc_p, const f
   }
 }
 
+// 32-byte matrix-core fragments kept in LDS as two planes of 16-byte halves
+// ([item] first halves, then [item] second halves), so that a wavefront's
+// 16-byte accesses run at a 16-byte stride across lanes
+struct FragHalves {
+  uint4 a, b;
+};
+template <class FR>
+__device__ __forceinline__ void put_frag(void* base, int nitems, int idx, const FR& f) {
+  static_assert(sizeof(FR) == 32, "32-byte fragments");
+  const FragHalves h = __builtin_bit_cast(FragHalves, f);
+  reinterpret_cast<uint4*>(base)[idx] = h.a;
+  reinterpret_cast<uint4*>(base)[nitems + idx] = h.b;
+}
+template <class FR>
+__device__ __forceinline__ FR get_frag(const void* base, int nitems, int idx) {
+  FragHalves h;
+  h.a = reinterpret_cast<const uint4*>(base)[idx];
+  h.b = reinterpret_cast<const uint4*>(base)[nitems + idx];
+  return __builtin_bit_cast(FR, h);
+}
+
 constexpr int kIntraThreads = 1024;  // 16 wavefronts: 4 per SIMD with one workgroup per CU
 
 template <int DK, int DV, int POL, typename RawT, bool FUSED>
@@ -945,7 +966,7 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
     __syncthreads();  // every read of T2 is done
 #pragma unroll
     for (int i = 0; i < PFK; ++i)
-      if (t + i * NT < NFK) reinterpret_cast<FB*>(sG)[t + i * NT] = fk[i];
+      if (t + i * NT < NFK) put_frag(sG, NFK, t + i * NT, fk[i]);
   }
   if constexpr (FUSED) {
     // v rows: conv (no norm), RW rows per wavefront side by side, b_r v_r into T1
@@ -1003,7 +1024,7 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
     // T0 (k e^{gl}, or k) was last read before the barrier above
 #pragma unroll
     for (int i = 0; i < PFV; ++i)
-      if (t + i * NT < NFV) reinterpret_cast<FB*>(sK)[t + i * NT] = fv[i];
+      if (t + i * NT < NFV) put_frag(sK, NFV, t + i * NT, fv[i]);
   }
   __syncthreads();
 
@@ -1013,8 +1034,7 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
   //    U~ goes to the record in result layout; W through LDS (T1) into fragments.
   {
     constexpr int NTW = DK / 16, NTU = DV / 16, NTT = NTW + NTU;
-    const FB* fRk = reinterpret_cast<const FB*>(sG);
-    const FB* fV = reinterpret_cast<const FB*>(sK);
+    // right-hand side fragments: b e^{G} k in T2 (NFK items), b v in T0 (NFV items)
     float* sW = sQ;  // b v rows in T1 are consumed
     constexpr int WPR = NW / 4, TPW = NTT / WPR;  // wavefronts per row block, column tiles per wavefront
     static_assert(NTT % WPR == 0, "column tiles split evenly");
@@ -1031,11 +1051,12 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
     for (int c = part * TPW; c < (part + 1) * TPW; ++c) {
       const bool isW = c < NTW;
       const int cb = isW ? c : c - NTW;
-      const FB* bsrc = isW ? fRk : fV;
+      const float* bsrc = isW ? sG : sK;
+      const int nb = isW ? NFK : NFV;
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        if (kb < KBR) acc = FI::mma(acc, xa[kb], bsrc[(cb * 2 + kb) * 64 + lane]);
+        if (kb < KBR) acc = FI::mma(acc, xa[kb], get_frag<FB>(bsrc, nb, (cb * 2 + kb) * 64 + lane));
       if (!isW) *reinterpret_cast<floatx4*>(rec + rl.Ut + ((int64_t)(cb * 4 + R) * 64 + lane) * 16) = acc;
       else {
 #pragma unroll
@@ -1067,8 +1088,9 @@ template <int DK, int POL>
 struct ScanSmem {
   using P = typename Frag<POL>::P;
   static constexpr int NP = Frag<POL>::PLANES;
-  static constexpr int PS = DK + 16 / sizeof(P);  // S^T row stride (one row per state column)
-  static constexpr int PU = 64 + 16 / sizeof(P);  // U^T row stride
+  // row strides padded by 32 bytes (16 bytes measured slower on the LDS)
+  static constexpr int PS = DK + 32 / sizeof(P);  // S^T row stride (one row per state column)
+  static constexpr int PU = 64 + 32 / sizeof(P);  // U^T row stride
   static constexpr int S_PLANE = 16 * PS, U_PLANE = 16 * PU;
   static constexpr size_t BYTES = (size_t)(NP * S_PLANE + NP * U_PLANE) * sizeof(P);
 };
@@ -1236,16 +1258,16 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillArgs p, int grou
       for (int j = 0; j < NS - 1; ++j) fr[j].load(rec_of(clampc(j)), rl, w4, lane, split);
     }
     auto iter = [&](int c, const StateFrags<DK, POL>& cur, StateFrags<DK, POL>& ahead) {
-      // the next-but-one chunk's operands load in three groups (W while S_c^T is
-      // read, U~ and gamma after U is written, K_<^T while U_c^T is read), so no
-      // group waits long for the CU's load path
+      // the next-but-one chunk's operands load in three groups (W right after A,
+      // U~ and gamma after U is written, K_<^T while U_c^T is read), so no group
+      // waits long for the CU's load path
       const uint8_t* nrec = rec_of(clampc(c + NS - 1));
       __syncthreads();  // A
+      ahead.load_w(nrec, rl, w4, lane);
+      __builtin_amdgcn_sched_barrier(0);
       typename F::B bs[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) bs[kb] = get_s(kb);
-      ahead.load_w(nrec, rl, w4, lane);
-      __builtin_amdgcn_sched_barrier(0);
       floatx4 acc[2] = {z4, z4};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) acc[kb & 1] = F::mma(acc[kb & 1], cur.w[kb], bs[kb]);
@@ -1298,16 +1320,16 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillArgs p, int grou
       for (int j = 0; j < NS - 1; ++j) fr[j].load(rec_of(clampc(j)), rl, w4, lane);
     }
     auto iter = [&](int c, const OutFrags<DK, POL>& cur, OutFrags<DK, POL>& ahead) {
+      const uint8_t* nrec = rec_of(clampc(c + NS - 1));
       __syncthreads();  // A
+      ahead.load_q(nrec, rl, w4, lane);  // the next-but-one chunk's Q^gamma right after A
+      __builtin_amdgcn_sched_barrier(0);
       typename F::B bs[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) bs[kb] = get_s(kb);
       floatx4 ao[2] = {z4, z4};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) ao[kb & 1] = F::mma_t(ao[kb & 1], bs[kb], cur.q[kb]);
-      const uint8_t* nrec = rec_of(clampc(c + NS - 1));
-      __builtin_amdgcn_sched_barrier(0);
-      ahead.load_q(nrec, rl, w4, lane);
       __syncthreads();  // B
       const typename F::B u0 = get_u(0);
       ao[0] = F::mma_t(ao[0], u0, cur.pp[0]);
