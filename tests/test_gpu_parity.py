@@ -204,6 +204,27 @@ def test_prefill_varlen_parity(dtype, precision, gate, dk, dv):
     assert rel(r["state"], ref.state) < tol
 
 
+@pytest.mark.parametrize("dk,dv,precision,fused", [(64, 64, None, False), (128, 128, K.PREC_FP16, False),
+                                                    (128, 128, K.PREC_FP16, True), (128, 64, K.PREC_BF16X3, True)])
+def test_prefill_many_ragged_sequences(dk, dv, precision, fused):
+    """400 sequences, many empty, single-row or one row either side of a chunk boundary: the chunk-record
+    slot of every sequence and thousands of scan workgroups over eight XCD groups."""
+    rng = np.random.default_rng(dk + dv)
+    lens = rng.choice([0, 1, 2, 63, 64, 65, 127, 128, 129], size=300).tolist() + rng.integers(0, 200, 100).tolist()
+    w = small(torch.bfloat16, lens=lens, H=2, d=dk, dv=dv, gate=I.GATE_SOFTPLUS, seed=81)
+    print(f"many sequences N={w.N} T={w.T} dk={dk} dv={dv} precision={precision} fused={fused}", flush=True)
+    r = gpu_layer_prefill(w, precision=precision, fused=fused)
+    ref = oracle_layer(w)
+    assert rel(r["o"], ref.o) < TOL_BF16
+    assert rel(r["y"], ref.y) < TOL_BF16
+    assert rel(r["state"], ref.state) < TOL_BF16
+    assert np.array_equal(r["prep"]["conv_state"].cpu().double().numpy(), ref.prep.conv_state)
+    # every sequence on its own, including the ones that start with an empty prompt
+    st = r["state"].cpu().double().numpy()
+    for n in range(w.N):
+        assert rel(st[n], ref.state[n]) < 4 * TOL_BF16, f"sequence {n} (length {lens[n]})"
+
+
 @pytest.mark.parametrize("precision", [K.PREC_FP32, K.PREC_BF16X3, K.PREC_FP16])
 def test_prefill_precision_policies_on_bf16_rows(precision):
     w = small(torch.bfloat16, lens=(300, 77), H=2, d=128, gate=I.GATE_SAFE, seed=21)
