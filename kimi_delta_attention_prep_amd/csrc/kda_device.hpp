@@ -80,21 +80,33 @@ __device__ __forceinline__ float wave_sum(float x) { return rows_total(row_sum16
 // NR rows (of one head and stream) of the prompt preamble, computed by a whole
 // wavefront: lane l owns channels E*l .. E*l+E-1 (E = D/64) of every row.
 // tap(rr, j, d) returns conv input tap j (0 = oldest, 3 = current row) of
-// channel d for row rr; w points at the head's first conv weight row of the
-// stream.  out[rr] gets the conv output after the activation, L2-normalised
-// over the D channels when NORM.  The rows are independent and computed side
-// by side; each row's arithmetic does not depend on NR, so the standalone
-// preamble kernel (one row, taps from HBM) and the fused prompt kernel (eight
-// rows, taps from LDS) produce the same bits.
-template <int D, bool NORM, int NR, bool ACT, class TAP>
-__device__ __forceinline__ void conv_rows_t(TAP tap, const float* __restrict__ w, float (&out)[NR][D / 64]) {
+// channel d for row rr; wt holds the lane's conv weights (load_conv_w).
+// out[rr] gets the conv output after the activation, L2-normalised over the D
+// channels when NORM.  The rows are independent and computed side by side;
+// each row's arithmetic does not depend on NR, so the standalone preamble
+// kernel (one row, taps from HBM) and the fused prompt kernel (several rows,
+// taps from LDS) produce the same bits.
+
+// the conv weights lane l uses: channels E*l .. E*l+E-1 of the head's stream, 4 taps each
+template <int D>
+struct ConvW {
+  float v[D / 64][4];
+};
+template <int D>
+__device__ __forceinline__ ConvW<D> load_conv_w(const float* __restrict__ w) {
   constexpr int E = D / 64;
   const int lane = threadIdx.x & 63;
-  float wt[E][4];
+  ConvW<D> wt;
 #pragma unroll
   for (int e = 0; e < E; ++e)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) wt[e][j] = w[(int64_t)(E * lane + e) * 4 + j];
+    for (int j = 0; j < 4; ++j) wt.v[e][j] = w[(int64_t)(E * lane + e) * 4 + j];
+  return wt;
+}
+template <int D, bool NORM, int NR, bool ACT, class TAP>
+__device__ __forceinline__ void conv_rows_t(TAP tap, const ConvW<D>& wt, float (&out)[NR][D / 64]) {
+  constexpr int E = D / 64;
+  const int lane = threadIdx.x & 63;
   float ss[NR];
 #pragma unroll
   for (int rr = 0; rr < NR; ++rr) {
@@ -102,8 +114,8 @@ __device__ __forceinline__ void conv_rows_t(TAP tap, const float* __restrict__ w
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int d = E * lane + e;
-      out[rr][e] = conv4<ACT>(wt[e][0], wt[e][1], wt[e][2], wt[e][3], tap(rr, 0, d), tap(rr, 1, d), tap(rr, 2, d),
-                              tap(rr, 3, d));
+      out[rr][e] = conv4<ACT>(wt.v[e][0], wt.v[e][1], wt.v[e][2], wt.v[e][3], tap(rr, 0, d), tap(rr, 1, d),
+                              tap(rr, 2, d), tap(rr, 3, d));
       ss[rr] = fmaf(out[rr][e], out[rr][e], ss[rr]);
     }
   }
@@ -121,11 +133,17 @@ __device__ __forceinline__ void conv_rows_t(TAP tap, const float* __restrict__ w
   }
 }
 // the activation is chosen once for the whole batch of rows, so that the rows'
-// loads and arithmetic interleave freely
+// loads and arithmetic interleave freely; the weights are either loaded here
+// (w points at the head's first conv weight row of the stream) or loaded
+// earlier by the caller
+template <int D, bool NORM, int NR, class TAP>
+__device__ __forceinline__ void conv_rows(TAP tap, const ConvW<D>& wt, int act, float (&out)[NR][D / 64]) {
+  if (act) conv_rows_t<D, NORM, NR, true>(tap, wt, out);
+  else conv_rows_t<D, NORM, NR, false>(tap, wt, out);
+}
 template <int D, bool NORM, int NR, class TAP>
 __device__ __forceinline__ void conv_rows(TAP tap, const float* __restrict__ w, int act, float (&out)[NR][D / 64]) {
-  if (act) conv_rows_t<D, NORM, NR, true>(tap, w, out);
-  else conv_rows_t<D, NORM, NR, false>(tap, w, out);
+  conv_rows<D, NORM, NR>(tap, load_conv_w<D>(w), act, out);
 }
 
 // 16-byte state accesses marked non-temporal: every state tile is read once and

@@ -618,6 +618,7 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
   constexpr int NSV = kVStaged ? ((L + 3) * (DV / VE) + NT - 1) / NT : 1;
   const int64_t chv = 2 * (int64_t)H * DK + (int64_t)h * DV;
   uint4 xv[NSV];
+  ConvW<DV> cwv;  // the v conv weights, loaded with the v rows
   if constexpr (FUSED) {
     constexpr int E = DK / 64;
     constexpr int NSK = ((L + 3) * (DK / VE) + NT - 1) / NT;  // pieces per thread of a staged q or k stream
@@ -633,14 +634,18 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
     uint4 xq[NSK], xk[NSK], xg[NGK];
 #pragma unroll
     for (int i = 0; i < NSK; ++i) xq[i] = load_staged(static_cast<const RawT*>(p.raw.q), DK, chq, t + i * NT);
+    // each stream's conv weights load right after its rows (a wait for them is then no
+    // longer than the wait for the rows)
+    const ConvW<DK> cwq = load_conv_w<DK>(p.raw.conv_w + chq * 4);
 #pragma unroll
     for (int i = 0; i < NSK; ++i) xk[i] = load_staged(static_cast<const RawT*>(p.raw.k), DK, chk, t + i * NT);
+    const ConvW<DK> cwk = load_conv_w<DK>(p.raw.conv_w + chk * 4);
     // each wavefront takes RW consecutive rows, so its 4 RW taps per channel come
     // from RW + 3 staged rows, each read and widened once
-    auto conv_stream = [&](const RawT* st, float* dst, int64_t ch) {  // rows RW wave + rr
+    auto conv_stream = [&](const RawT* st, float* dst, const ConvW<DK>& wt) {  // rows RW wave + rr
       float x[RW][E];
       conv_rows<DK, true, RW>([&](int rr, int j, int d) { return to_f32(st[(RW * wave + rr + j) * DK + d]); },
-                                 p.raw.conv_w + ch * 4, p.raw.act, x);
+                                 wt, p.raw.act, x);
 #pragma unroll
       for (int rr = 0; rr < RW; ++rr) {
         const int r = RW * wave + rr;
@@ -651,7 +656,7 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
 #pragma unroll
     for (int i = 0; i < NSK; ++i) store_staged(stq, DK, t + i * NT, xq[i]);
     __syncthreads();
-    conv_stream(stq, sQ, chq);
+    conv_stream(stq, sQ, cwq);
 #pragma unroll
     for (int i = 0; i < NSK; ++i) store_staged(stk, DK, t + i * NT, xk[i]);
     const RawT* rg = static_cast<const RawT*>(p.raw.g);
@@ -666,8 +671,9 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
 #pragma unroll
       for (int i = 0; i < NSV; ++i) xv[i] = load_staged(static_cast<const RawT*>(p.raw.v), DV, chv, t + i * NT);
     }
+    cwv = load_conv_w<DV>(p.raw.conv_w + chv * 4);
     __syncthreads();
-    conv_stream(stk, sK, chk);
+    conv_stream(stk, sK, cwk);
     __syncthreads();  // the staged rows over T2 are consumed
 #pragma unroll
     for (int i = 0; i < NGK; ++i) {
@@ -826,8 +832,10 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
     constexpr int NJ = (10 + NW - 1) / NW;  // block pairs per wavefront
     // pair indices in order (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3);
     // the three that carry a scale, (2,0) (3,0) (3,1), go to wavefronts 0..2
-    constexpr int kPairOrder[10] = {3, 6, 7, 0, 1, 2, 4, 5, 8, 9};
-    auto pair_of = [&](int j) { const int w = wave + NW * j; return w < 10 ? kPairOrder[w] : 10; };
+    // (packed 4 bits per entry, so that the lookup is arithmetic: a constant table is read
+    // with a vector load, and its wait would also drain the record stores in flight)
+    constexpr uint64_t kPairOrder = 0x9854210763ull;  // 3, 6, 7, 0, 1, 2, 4, 5, 8, 9 from the low end
+    auto pair_of = [&](int j) { const int w = wave + NW * j; return w < 10 ? (int)((kPairOrder >> (4 * w)) & 15) : 10; };
     floatx4 acc[NJ][2];  // [pair of this wavefront][A, P]
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
@@ -979,7 +987,7 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
       for (int i = 0; i < NSV; ++i) store_staged(stv, DV, t + i * NT, xv[i]);
       __syncthreads();
       conv_rows<DV, false, RW>([&](int rr, int j, int d) { return to_f32(stv[(RW * wave + rr + j) * DV + d]); },
-                                  p.raw.conv_w + chv * 4, p.raw.act, x);
+                                  cwv, p.raw.act, x);
     } else {
       const RawT* rv = static_cast<const RawT*>(p.raw.v);
       const int64_t wv = (int64_t)H * DV, rel0 = start - t0 + RW * wave;
@@ -987,7 +995,7 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
         const int64_t pos = rel0 + rr - 3 + j;
         if (RW * wave + rr >= len) return 0.f;
         return pos >= 0 ? to_f32(rv[(t0 + pos) * wv + (int64_t)h * DV + d]) : to_f32(raw_cs[(3 + pos) * Cch + chv + d]);
-      }, p.raw.conv_w + chv * 4, p.raw.act, x);
+      }, cwv, p.raw.act, x);
     }
 #pragma unroll
     for (int rr = 0; rr < RW; ++rr) {
