@@ -587,31 +587,43 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
   // from its carried conv state at the sequence start) and each wavefront
   // then runs the preamble of RW consecutive rows side by side, reading its taps there.
   constexpr int VE = 16 / sizeof(RawT);  // raw elements per 16-byte piece
-  // piece idx of a staged stream (row sr = idx / (D / VE) of the 67): zero past the chunk's last row
-  auto load_staged = [&](const RawT* src, int D, int64_t ch0, int idx) {
+  // piece idx of a staged stream (row sr = idx / (D / VE) of the 67).  Every load is
+  // unconditional (pieces with nothing to load read the stream's first piece): a load
+  // inside a branch is waited for where the branches join, which serialises the loads.
+  auto load_staged = [&](const RawT* src, int D, int idx) {
     const int per_row = D / VE;
     const int sr = idx / per_row, c0 = (idx % per_row) * VE;
     const int64_t pos = start - 3 + sr;  // packed row of this staged row
-    uint4 x = {0u, 0u, 0u, 0u};
-    if (idx < (L + 3) * per_row && sr < len + 3) {
-      if (pos >= t0) x = *reinterpret_cast<const uint4*>(src + pos * ((int64_t)H * D) + (int64_t)h * D + c0);
-      else {
-        // carried conv state row 3 + (pos - t0); its channels are not 16-byte aligned in general
-        const RawT* cr = raw_cs + (3 + (pos - t0)) * Cch + ch0 + c0;
-        uint32_t wv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if constexpr (sizeof(RawT) == 2) wv[e] = (uint32_t)cr[2 * e] | ((uint32_t)cr[2 * e + 1] << 16);
-          else wv[e] = __float_as_uint(cr[e]);
-        }
-        x = {wv[0], wv[1], wv[2], wv[3]};
-      }
-    }
-    return x;
+    const bool live = idx < (L + 3) * per_row && sr < len + 3 && pos >= t0;
+    return *reinterpret_cast<const uint4*>(src + (live ? pos * ((int64_t)H * D) + (int64_t)h * D + c0 : 0));
   };
+  // the value that lands in LDS is chosen here, where it is needed anyway: the
+  // loaded row, or zero past the chunk's last row
   auto store_staged = [&](RawT* st, int D, int idx, uint4 x) {
-    if (idx < (L + 3) * (D / VE)) *reinterpret_cast<uint4*>(st + idx * VE) = x;
+    const int per_row = D / VE;
+    if (idx >= (L + 3) * per_row) return;
+    if (idx / per_row >= len + 3) x = {0u, 0u, 0u, 0u};
+    *reinterpret_cast<uint4*>(st + idx * VE) = x;
   };
+  // the halo rows before a sequence's first row, from its carried conv state row
+  // 3 + (pos - t0) (channels not 16-byte aligned in general), written over what
+  // store_staged left there by the same thread.  Only the first chunk of a sequence
+  // has such rows, and its workgroup alone takes this branch.
+  auto store_halo = [&](RawT* st, int D, int64_t ch0, int idx) {
+    const int per_row = D / VE;
+    const int sr = idx / per_row, c0 = (idx % per_row) * VE;
+    const int64_t pos = start - 3 + sr;
+    if (idx >= (L + 3) * per_row || pos >= t0 || sr >= len + 3) return;
+    const RawT* cr = raw_cs + (3 + (pos - t0)) * Cch + ch0 + c0;
+    uint32_t wv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (sizeof(RawT) == 2) wv[e] = (uint32_t)cr[2 * e] | ((uint32_t)cr[2 * e + 1] << 16);
+      else wv[e] = __float_as_uint(cr[e]);
+    }
+    *reinterpret_cast<uint4*>(st + idx * VE) = uint4{wv[0], wv[1], wv[2], wv[3]};
+  };
+  const bool seq_first = start == t0;  // uniform over the workgroup
   // Fused: the v rows are loaded with the preamble's rows and land long before step 7
   // (staged over A there where they fit; fp32 rows read their taps from HBM)
   constexpr bool kVStaged = FUSED && (L + 3) * DV * sizeof(RawT) <= (size_t)L * PL * sizeof(float);
@@ -633,12 +645,12 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
     // beta load while k is convolved
     uint4 xq[NSK], xk[NSK], xg[NGK];
 #pragma unroll
-    for (int i = 0; i < NSK; ++i) xq[i] = load_staged(static_cast<const RawT*>(p.raw.q), DK, chq, t + i * NT);
+    for (int i = 0; i < NSK; ++i) xq[i] = load_staged(static_cast<const RawT*>(p.raw.q), DK, t + i * NT);
     // each stream's conv weights load right after its rows (a wait for them is then no
     // longer than the wait for the rows)
     const ConvW<DK> cwq = load_conv_w<DK>(p.raw.conv_w + chq * 4);
 #pragma unroll
-    for (int i = 0; i < NSK; ++i) xk[i] = load_staged(static_cast<const RawT*>(p.raw.k), DK, chk, t + i * NT);
+    for (int i = 0; i < NSK; ++i) xk[i] = load_staged(static_cast<const RawT*>(p.raw.k), DK, t + i * NT);
     const ConvW<DK> cwk = load_conv_w<DK>(p.raw.conv_w + chk * 4);
     // each wavefront takes RW consecutive rows, so its 4 RW taps per channel come
     // from RW + 3 staged rows, each read and widened once
@@ -655,21 +667,26 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
     };
 #pragma unroll
     for (int i = 0; i < NSK; ++i) store_staged(stq, DK, t + i * NT, xq[i]);
+    if (seq_first)
+#pragma unroll
+      for (int i = 0; i < NSK; ++i) store_halo(stq, DK, chq, t + i * NT);
     __syncthreads();
     conv_stream(stq, sQ, cwq);
 #pragma unroll
     for (int i = 0; i < NSK; ++i) store_staged(stk, DK, t + i * NT, xk[i]);
+    if (seq_first)
+#pragma unroll
+      for (int i = 0; i < NSK; ++i) store_halo(stk, DK, chk, t + i * NT);
     const RawT* rg = static_cast<const RawT*>(p.raw.g);
 #pragma unroll
     for (int i = 0; i < NGK; ++i) {
       const int idx = t + i * NT, r = idx / (DK / VE), c0 = (idx % (DK / VE)) * VE;
-      xg[i] = {0u, 0u, 0u, 0u};
-      if (idx < L * (DK / VE) && r < len) xg[i] = *reinterpret_cast<const uint4*>(rg + ((start + r) * H + h) * DK + c0);
+      xg[i] = *reinterpret_cast<const uint4*>(rg + (idx < L * (DK / VE) && r < len ? ((start + r) * H + h) * DK + c0 : 0));
     }
-    const float braw = (t < len) ? to_f32(static_cast<const RawT*>(p.raw.beta)[(start + t) * H + h]) : 0.f;
+    const RawT braw = static_cast<const RawT*>(p.raw.beta)[t < len ? (start + t) * H + h : 0];
     if constexpr (kVStaged) {
 #pragma unroll
-      for (int i = 0; i < NSV; ++i) xv[i] = load_staged(static_cast<const RawT*>(p.raw.v), DV, chv, t + i * NT);
+      for (int i = 0; i < NSV; ++i) xv[i] = load_staged(static_cast<const RawT*>(p.raw.v), DV, t + i * NT);
     }
     cwv = load_conv_w<DV>(p.raw.conv_w + chv * 4);
     __syncthreads();
@@ -688,7 +705,7 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
           *reinterpret_cast<float4*>(&sG[r * PK + c0 + e]) = make_float4(gv[e], gv[e + 1], gv[e + 2], gv[e + 3]);
       }
     }
-    if (t < L) sBeta[t] = t < len ? sigmoid(braw) : 0.f;
+    if (t < L) sBeta[t] = t < len ? sigmoid(to_f32(braw)) : 0.f;
   } else {
     for (int idx = t; idx < L * (DK / 4); idx += NT) {
       const int r = idx / (DK / 4), c4 = 4 * (idx % (DK / 4));
@@ -985,6 +1002,9 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < NSV; ++i) store_staged(stv, DV, t + i * NT, xv[i]);
+      if (seq_first)
+#pragma unroll
+        for (int i = 0; i < NSV; ++i) store_halo(stv, DV, chv, t + i * NT);
       __syncthreads();
       conv_rows<DV, false, RW>([&](int rr, int j, int d) { return to_f32(stv[(RW * wave + rr + j) * DV + d]); },
                                   cwv, p.raw.act, x);
