@@ -641,17 +641,16 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
     RawT* stk = stq + (L + 3) * DK;
     const int64_t wk = (int64_t)H * DK;
     const int64_t chq = (int64_t)h * DK, chk = wk + (int64_t)h * DK;
-    // q and k load together; q is staged and convolved while k lands, and g and
-    // beta load while k is convolved
+    // q loads first and alone; k loads once q has landed and lands while q is
+    // convolved; g and beta load while k is convolved.  The workgroups of a round
+    // start together, so the first load of every CU meets the others' in HBM:
+    // keeping that burst to the q rows gets q in sooner.
     uint4 xq[NSK], xk[NSK], xg[NGK];
 #pragma unroll
     for (int i = 0; i < NSK; ++i) xq[i] = load_staged(static_cast<const RawT*>(p.raw.q), DK, t + i * NT);
     // each stream's conv weights load right after its rows (a wait for them is then no
     // longer than the wait for the rows)
     const ConvW<DK> cwq = load_conv_w<DK>(p.raw.conv_w + chq * 4);
-#pragma unroll
-    for (int i = 0; i < NSK; ++i) xk[i] = load_staged(static_cast<const RawT*>(p.raw.k), DK, t + i * NT);
-    const ConvW<DK> cwk = load_conv_w<DK>(p.raw.conv_w + chk * 4);
     // each wavefront takes RW consecutive rows, so its 4 RW taps per channel come
     // from RW + 3 staged rows, each read and widened once
     auto conv_stream = [&](const RawT* st, float* dst, const ConvW<DK>& wt) {  // rows RW wave + rr
@@ -671,6 +670,9 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
 #pragma unroll
       for (int i = 0; i < NSK; ++i) store_halo(stq, DK, chq, t + i * NT);
     __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NSK; ++i) xk[i] = load_staged(static_cast<const RawT*>(p.raw.k), DK, t + i * NT);
+    const ConvW<DK> cwk = load_conv_w<DK>(p.raw.conv_w + chk * 4);
     conv_stream(stq, sQ, cwq);
 #pragma unroll
     for (int i = 0; i < NSK; ++i) store_staged(stk, DK, t + i * NT, xk[i]);
