@@ -142,6 +142,19 @@ typedef struct kda_raw_rows {
   float lower_bound;          /* safe mode only: finite, < 0 */
 } kda_raw_rows;
 
+/* The gated output norm as the epilogue of a prompt call (kda_prefill_varlen
+ * with a non-NULL `norm`): y = o / sqrt(mean(o^2) + eps) * weight * sigmoid(z)
+ * over each row of d_v values, as gated_rmsnorm_out computes it.  Device
+ * pointers, 16-byte aligned. */
+typedef struct kda_norm_args {
+  const void* z;              /* [t_tot, H, d_v] of z_dtype */
+  int32_t z_dtype;            /* kda_dtype: F32 or BF16 */
+  const float* weight;        /* [d_v] fp32 */
+  float eps;                  /* finite, >= 0 */
+  void* y;                    /* [t_tot, H, d_v] of y_dtype, written */
+  int32_t y_dtype;            /* kda_dtype: F32 or BF16 */
+} kda_norm_args;
+
 /* kda_prefill_varlen -- the delta rule (part 4) over packed prompt rows, in
  * 64-row chunks anchored at each sequence's first row (WY/UT form with an
  * intra-chunk lower-triangular solve, then a sequential pass over chunks).
@@ -150,16 +163,21 @@ typedef struct kda_raw_rows {
  *   raw     NULL, or raw rows + preamble parameters: the preamble (parts 1-3)
  *           then runs inside the prompt kernels, with the same bits as kda_prep,
  *           and the conv state is carried as kda_prep would carry it
+ *   norm    NULL, or the output norm (part 5) as the call's epilogue: y gets
+ *           the same bits as gated_rmsnorm_out on o would give.  A row's norm
+ *           spans all d_v columns, which the scan spreads over several
+ *           workgroups, so the epilogue is one more launch on the stream, after
+ *           the scan; rows of a skipped sequence (negative slot) keep their y.
  *   state   fp32 [slots, H, d_k, d_v], read as the initial state and
  *           overwritten with the final state of each sequence
- *   o       fp32 [t_tot, H, d_v], pre-norm output
+ *   o       fp32 [t_tot, H, d_v], pre-norm output (written also when `norm` is given)
  *   workspace  device scratch of at least kda_prefill_workspace_bytes(), 256-byte aligned
  * A prompt cut at a multiple of 64 rows, with the state carried, gives the same
  * bits as the uncut prompt. */
 int kda_prefill_varlen(const kda_dims* d, int32_t num_seqs, int64_t t_tot, const int32_t* cu_seqlens,
                        const int32_t* slots, const float* q_hat, const float* k_hat, const float* v,
-                       const float* g, const float* beta, const kda_raw_rows* raw, float* state, float* o,
-                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+                       const float* g, const float* beta, const kda_raw_rows* raw, const kda_norm_args* norm,
+                       float* state, float* o, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* kda_decode -- one row per sequence (parts 1-4 fused): conv step on the conv
  * state, gates, norms, state step, readout.
@@ -202,7 +220,7 @@ const char* kda_last_error(void);
  * and events[2i+1] on its stream immediately before and after its kernel i,
  * for 2i+1 < count:
  *   i = 0 intra-chunk kernel,  1 inter-chunk scan (which also carries the conv
- *   state when `raw` is given).
+ *   state when `raw` is given),  2 the output norm when `norm` is given.
  * The events are caller-owned hipEvent_t handles, already created; the library
  * keeps only the pointer, which must stay valid while set.  count = 0 (events
  * may be NULL) turns the hook off.  Errors: KDA_E_ARG for a negative or odd

@@ -51,6 +51,11 @@ class KdaRawRows(ctypes.Structure):
                 ("gate_mode", ctypes.c_int32), ("lower_bound", ctypes.c_float)]
 
 
+class KdaNormArgs(ctypes.Structure):
+    _fields_ = [("z", ctypes.c_void_p), ("z_dtype", ctypes.c_int32), ("weight", ctypes.c_void_p),
+                ("eps", ctypes.c_float), ("y", ctypes.c_void_p), ("y_dtype", ctypes.c_int32)]
+
+
 class KdaLog(ctypes.Structure):
     _fields_ = [("a", ctypes.c_void_p), ("k_hat", ctypes.c_void_p), ("u", ctypes.c_void_p),
                 ("conv_rows", ctypes.c_void_p), ("window", ctypes.c_int32)]
@@ -72,8 +77,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.kda_prep.argtypes = [D, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp, vp, vp, vp, vp]
         lib.kda_prefill_workspace_bytes.argtypes = [D, i32, i64]
         lib.kda_prefill_workspace_bytes.restype = ctypes.c_size_t
-        lib.kda_prefill_varlen.argtypes = [D, i32, i64, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(KdaRawRows), vp, vp,
-                                           vp, ctypes.c_size_t, vp]
+        lib.kda_prefill_varlen.argtypes = [D, i32, i64, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(KdaRawRows),
+                                           ctypes.POINTER(KdaNormArgs), vp, vp, vp, ctypes.c_size_t, vp]
         lib.kda_decode.argtypes = [D, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp]
         lib.kda_verify_window.argtypes = [D, i32, i32, vp, vp, vp, vp, vp, Lg, Lg, vp, vp, vp, vp, vp, i32, f32, vp, vp]
         lib.gated_rmsnorm_out.argtypes = [i64, i32, vp, vp, i32, vp, f32, vp, i32, vp]
@@ -170,9 +175,11 @@ def kda_prefill_workspace_bytes(d: Dims, num_seqs: int, t_tot: int) -> int:
     return int(load_library().kda_prefill_workspace_bytes(ctypes.byref(dims), int(num_seqs), int(t_tot)))
 
 
-def kda_prefill_varlen(d: Dims, cu_seqlens, q_hat, k_hat, v, g, beta, state, o, workspace, slots=None, raw=None):
+def kda_prefill_varlen(d: Dims, cu_seqlens, q_hat, k_hat, v, g, beta, state, o, workspace, slots=None, raw=None,
+                       norm=None):
     """Chunked prompt pass.  With raw=dict(q_raw, k_raw, v_raw, g_raw, beta_logit, conv_weight, conv_state_in,
-    conv_state_out, gate_mode, lower_bound) the preamble runs inside the prompt kernels and q_hat..beta may be None."""
+    conv_state_out, gate_mode, lower_bound) the preamble runs inside the prompt kernels and q_hat..beta may be None.
+    With norm=dict(z, weight, eps, y) the gated output norm runs as the call's epilogue (y as gated_rmsnorm_out)."""
     lib = load_library()
     N = cu_seqlens.numel() - 1
     H, dk, dv = d.num_heads, d.head_dim_k, d.head_dim_v
@@ -196,6 +203,13 @@ def kda_prefill_varlen(d: Dims, cu_seqlens, q_hat, k_hat, v, g, beta, state, o, 
                                                       "conv_state_in", "conv_state_out")),
                         int(raw["gate_mode"]), float(raw["lower_bound"]))
     _need(o, "o", torch.float32, (T, H, dv))
+    nn = None
+    if norm is not None:
+        _need(norm["z"], "z", shape=(T, H, dv))
+        _need(norm["weight"], "weight", torch.float32, (dv,))
+        _need(norm["y"], "y", shape=(T, H, dv))
+        nn = KdaNormArgs(norm["z"].data_ptr(), _dtype_code(norm["z"].dtype), norm["weight"].data_ptr(),
+                         float(norm["eps"]), norm["y"].data_ptr(), _dtype_code(norm["y"].dtype))
     _need(state, "state", torch.float32)
     if state.dim() != 4 or tuple(state.shape[1:]) != (H, dk, dv):
         raise ValueError(f"state must be [slots, {H}, {dk}, {dv}]")
@@ -205,7 +219,7 @@ def kda_prefill_varlen(d: Dims, cu_seqlens, q_hat, k_hat, v, g, beta, state, o, 
     dims = d.c()
     _check(lib.kda_prefill_varlen(ctypes.byref(dims), N, T, _ptr(cu_seqlens), _ptr(slots), _ptr(q_hat), _ptr(k_hat),
                                   _ptr(v), _ptr(g), _ptr(beta), ctypes.byref(rr) if rr is not None else None,
-                                  _ptr(state), _ptr(o), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  ctypes.byref(nn) if nn is not None else None, _ptr(state), _ptr(o), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                   _stream()))
 
 
@@ -296,7 +310,8 @@ def gated_rmsnorm_out(o, z, w, eps, y):
 
 
 # kernels of one kda_prefill_varlen call, in the order the timing hook numbers them
-PREFILL_KERNELS = ("chunk_intra", "chunk_scan")
+# (the third only when the call has the norm epilogue)
+PREFILL_KERNELS = ("chunk_intra", "chunk_scan", "gated_rmsnorm")
 
 
 def kda_set_timing_events(events):

@@ -132,10 +132,18 @@ size_t kda_prefill_workspace_bytes(const kda_dims* d, int32_t num_seqs, int64_t 
 
 int kda_prefill_varlen(const kda_dims* d, int32_t num_seqs, int64_t t_tot, const int32_t* cu_seqlens,
                        const int32_t* slots, const float* q_hat, const float* k_hat, const float* v,
-                       const float* g, const float* beta, const kda_raw_rows* raw, float* state, float* o,
-                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                       const float* g, const float* beta, const kda_raw_rows* raw, const kda_norm_args* norm,
+                       float* state, float* o, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   KDA_TRY(check_dims(d));
   if (num_seqs < 0 || t_tot < 0) return fail(KDA_E_ARG, "kda_prefill_varlen: negative size");
+  if (norm) {
+    if ((norm->z_dtype != KDA_DTYPE_F32 && norm->z_dtype != KDA_DTYPE_BF16) ||
+        (norm->y_dtype != KDA_DTYPE_F32 && norm->y_dtype != KDA_DTYPE_BF16))
+      return fail(KDA_E_DTYPE, "kda_prefill_varlen: unknown norm z or y dtype");
+    if (!(norm->eps >= 0.0f) || !std::isfinite(norm->eps))
+      return fail(KDA_E_ARG, "kda_prefill_varlen: norm eps must be finite and >= 0");
+    if (t_tot > 0) KDA_TRY(check_ptrs("kda_prefill_varlen: norm z/weight/y", {norm->z, norm->weight, norm->y}));
+  }
   if (num_seqs == 0 && t_tot > 0) return fail(KDA_E_ARG, "kda_prefill_varlen: rows without sequences");
   KDA_TRY(check_opt_ptr("kda_prefill_varlen: slots", slots));
   if (raw) KDA_TRY(check_gate(raw->gate_mode, raw->lower_bound));
@@ -181,7 +189,17 @@ int kda_prefill_varlen(const kda_dims* d, int32_t num_seqs, int64_t t_tot, const
     L.raw_beta = raw->beta_logit; L.conv_w = raw->conv_weight; L.cs_in = raw->conv_state_in;
     L.cs_out = raw->conv_state_out;
   }
-  return hip_status(kda::launch_prefill(L, stream), "kda_prefill_varlen");
+  KDA_TRY(hip_status(kda::launch_prefill(L, stream), "kda_prefill_varlen"));
+  if (norm && t_tot > 0) {
+    kda::NormLaunch N{t_tot * d->num_heads, d->head_dim_v, norm->z_dtype, norm->y_dtype, o, norm->z, norm->weight,
+                      norm->eps, norm->y};
+    N.cu = cu_seqlens; N.slots = slots; N.num_seqs = num_seqs; N.H = d->num_heads;
+    const bool timed = g_nevents >= 6;
+    if (timed) KDA_TRY(hip_status(hipEventRecord(g_events[4], stream), "kda_prefill_varlen"));
+    KDA_TRY(hip_status(kda::launch_gated_rmsnorm(N, stream), "kda_prefill_varlen: norm"));
+    if (timed) KDA_TRY(hip_status(hipEventRecord(g_events[5], stream), "kda_prefill_varlen"));
+  }
+  return ok();
 }
 
 int kda_decode(const kda_dims* d, int32_t batch, const int32_t* slots, float* state, void* conv_state,

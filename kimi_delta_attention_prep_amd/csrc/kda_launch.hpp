@@ -34,6 +34,11 @@ struct NormLaunch {
   const float* w;
   float eps;
   void* y;
+  // optional (prompt epilogue): rows are [t_tot, H]; with slots given, the rows of a
+  // sequence whose slot is negative are left alone
+  const int32_t* cu = nullptr;
+  const int32_t* slots = nullptr;
+  int num_seqs = 0, H = 1;
 };
 hipError_t launch_gated_rmsnorm(const NormLaunch& L, hipStream_t s);
 

@@ -57,14 +57,15 @@ __device__ __forceinline__ void store8<uint16_t>(uint16_t* p, const float (&y)[8
 template <int DV, typename ZT, typename YT>
 __global__ __launch_bounds__(256) void gated_rmsnorm_kernel(int64_t rows, const float* __restrict__ o,
                                                             const ZT* __restrict__ z, const float* __restrict__ w,
-                                                            float eps, YT* __restrict__ y) {
+                                                            float eps, YT* __restrict__ y, const int32_t* cu,
+                                                            const int32_t* slots, int num_seqs, int H) {
   constexpr int LPR = DV / 8;  // lanes per row
   static_assert(LPR == 8 || LPR == 16, "8 or 16 lanes per row");
   const int t = threadIdx.x;
   const int64_t row = (int64_t)blockIdx.x * (256 / LPR) + t / LPR;
   const int c = 8 * (t % LPR);
   float ov[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, zv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  const bool live = row < rows;
+  bool live = row < rows;
   if (live) {
     load8<float>(o + row * DV + c, ov);
     load8<ZT>(z + row * DV + c, zv);
@@ -76,6 +77,15 @@ __global__ __launch_bounds__(256) void gated_rmsnorm_kernel(int64_t rows, const 
   ss += dpp_partner<0x4E>(ss);    // quad_perm [2,3,0,1]
   ss += dpp_partner<0x141>(ss);   // row_half_mirror: the 8-lane sum
   if constexpr (LPR == 16) ss += dpp_partner<0x140>(ss);  // row_mirror: the 16-lane sum
+  if (live && slots) {  // prompt epilogue with a slot map: the row's sequence n, largest with cu[n] <= token
+    const int64_t tok = row / H;
+    int lo = 0, hi = num_seqs;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (cu[mid] <= tok) lo = mid; else hi = mid;
+    }
+    live = slots[lo] >= 0;
+  }
   if (!live) return;
   const float inv = 1.0f / sqrtf(ss / (float)DV + eps);
   float wa[8], yv[8];
@@ -92,7 +102,8 @@ static hipError_t launch_norm_dv(const NormLaunch& L, hipStream_t s) {
   const bool zb = L.z_dtype == 1, yb = L.y_dtype == 1;
 #define KDA_NORM_CASE(ZT, YT)                                                                          \
   hipLaunchKernelGGL((gated_rmsnorm_kernel<DV, ZT, YT>), grid, dim3(256), 0, s, L.rows, L.o,           \
-                     static_cast<const ZT*>(L.z), L.w, L.eps, static_cast<YT*>(L.y))
+                     static_cast<const ZT*>(L.z), L.w, L.eps, static_cast<YT*>(L.y), L.cu, L.slots,    \
+                     L.num_seqs, L.H)
   if (zb && yb) KDA_NORM_CASE(uint16_t, uint16_t);
   else if (zb) KDA_NORM_CASE(uint16_t, float);
   else if (yb) KDA_NORM_CASE(float, uint16_t);

@@ -110,15 +110,27 @@ def test_prep_and_prefill_checks(lib):
     assert prep(2, 10, MIS) == K.KDA_E_ALIGN
     need = lib.kda_prefill_workspace_bytes(ctypes.byref(d), 2, 1000)
     assert need > 0
-    pf = lambda ws, nb: lib.kda_prefill_varlen(ctypes.byref(d), 2, 1000, A, None, A, A, A, A, A, None, A, A, ws, nb,
-                                               None)
+    pf = lambda ws, nb: lib.kda_prefill_varlen(ctypes.byref(d), 2, 1000, A, None, A, A, A, A, A, None, None, A, A,
+                                               ws, nb, None)
     assert pf(A, need - 1) == K.KDA_E_WORKSPACE
     assert pf(None, need) == K.KDA_E_WORKSPACE
     assert pf(ctypes.c_void_p(0x10010), need) == K.KDA_E_ALIGN
     # o is written with 16-byte stores: an element-aligned o is refused
-    assert lib.kda_prefill_varlen(ctypes.byref(d), 2, 1000, A, None, A, A, A, A, A, None, A, MIS4, A, need,
+    assert lib.kda_prefill_varlen(ctypes.byref(d), 2, 1000, A, None, A, A, A, A, A, None, None, A, MIS4, A, need,
                                   None) == K.KDA_E_ALIGN
     assert lib.kda_prefill_workspace_bytes(ctypes.byref(dims(dk=96)), 2, 1000) == 0
+    # the norm epilogue's arguments are checked with the rest, before any launch
+    def pn(z, zt, eps, y, yt):
+        nrm = K.KdaNormArgs(z, zt, 0x10000, eps, y, yt)
+        return lib.kda_prefill_varlen(ctypes.byref(d), 2, 1000, A, None, A, A, A, A, A, None, ctypes.byref(nrm), A,
+                                      A, A, need, None)
+    assert pn(0x10000, 7, 1e-6, 0x10000, K.DTYPE_F32) == K.KDA_E_DTYPE
+    assert pn(0x10000, K.DTYPE_BF16, 1e-6, 0x10000, 7) == K.KDA_E_DTYPE
+    assert pn(0x10000, K.DTYPE_F32, -1.0, 0x10000, K.DTYPE_F32) == K.KDA_E_ARG
+    assert pn(0x10000, K.DTYPE_F32, float("nan"), 0x10000, K.DTYPE_F32) == K.KDA_E_ARG
+    assert pn(0x10000, K.DTYPE_F32, 1e-6, 0x10008, K.DTYPE_BF16) == K.KDA_E_ALIGN  # y written 16 bytes at a time
+    assert pn(0x10004, K.DTYPE_F32, 1e-6, 0x10000, K.DTYPE_F32) == K.KDA_E_ALIGN
+    assert pn(None, K.DTYPE_F32, 1e-6, 0x10000, K.DTYPE_F32) == K.KDA_E_ARG
 
 
 def test_norm_checks(lib):

@@ -10,7 +10,7 @@ import kimi_delta_attention_prep_amd as K
 from kimi_delta_attention_prep_amd import inputs as I
 from oracle import oracle as O
 
-from helpers import (EPS, TOL_BF16, TOL_FP32, dims_for, gpu_decode_steps, gpu_layer_prefill, gpu_prep,
+from helpers import (EPS, TOL_BF16, TOL_FP32, dims_for, gpu_decode_steps, gpu_layer_prefill, gpu_prep, raw_rows,
                      oracle_layer, rel, tol_for)
 
 pytestmark = pytest.mark.gpu
@@ -332,6 +332,57 @@ def test_prefill_cut_at_chunk_multiple_is_bitwise(cut, precision):
     rb = gpu_layer_prefill(b, precision=precision)
     assert torch.equal(torch.cat([ra["o"], rb["o"]]), full["o"])
     assert torch.equal(rb["state"], full["state"])
+
+
+@pytest.mark.parametrize("fused,ydt", [(False, torch.float32), (True, torch.bfloat16), (True, torch.float32)])
+def test_prefill_norm_epilogue_is_bitwise_the_separate_norm(fused, ydt):
+    """kda_prefill_varlen with `norm`: o as without it, and y bit for bit what gated_rmsnorm_out gives on that o."""
+    w = small(torch.bfloat16, lens=(150, 3, 0, 64, 70), H=2, d=128, gate=I.GATE_SOFTPLUS, seed=91)
+    d = dims_for(w, K.PREC_FP16)
+    ref = gpu_layer_prefill(w, precision=K.PREC_FP16, y_dtype=ydt, fused=fused)
+    wd = w.to("cuda")
+    state = wd.state0.clone()
+    o = torch.empty(w.T, w.H, w.dv, device="cuda")
+    y = torch.empty(w.T, w.H, w.dv, device="cuda", dtype=ydt)
+    ws = torch.empty(K.kda_prefill_workspace_bytes(d, w.N, w.T), dtype=torch.uint8, device="cuda")
+    norm = dict(z=wd.z, weight=wd.norm_w, eps=EPS, y=y)
+    if fused:
+        K.kda_prefill_varlen(d, wd.cu_seqlens, None, None, None, None, None, state, o, ws,
+                             raw=raw_rows(wd, torch.empty_like(wd.conv_state0)), norm=norm)
+    else:
+        _, p = gpu_prep(w, d)
+        K.kda_prefill_varlen(d, wd.cu_seqlens, p["q_hat"], p["k_hat"], p["v"], p["g"], p["beta"], state, o, ws,
+                             norm=norm)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref["o"])
+    assert torch.equal(state, ref["state"])
+    assert torch.equal(y, ref["y"])
+
+
+def test_prefill_norm_epilogue_skips_negative_slots():
+    w = small(torch.bfloat16, lens=(90, 70, 40), H=2, d=64, seed=93)
+    d = dims_for(w)
+    wd, p = gpu_prep(w, d)
+    pool = torch.randn(4, w.H, w.dk, w.dv, device="cuda") * 0.02
+    pool[2] = wd.state0[0]
+    pool[0] = wd.state0[2]
+    slots = torch.tensor([2, -1, 0], dtype=torch.int32, device="cuda")
+    o = torch.full((w.T, w.H, w.dv), 7.0, device="cuda")
+    y = torch.full((w.T, w.H, w.dv), 5.0, device="cuda")
+    ws = torch.empty(K.kda_prefill_workspace_bytes(d, w.N, w.T), dtype=torch.uint8, device="cuda")
+    K.kda_prefill_varlen(d, wd.cu_seqlens, p["q_hat"], p["k_hat"], p["v"], p["g"], p["beta"], pool, o, ws,
+                         slots=slots, norm=dict(z=wd.z, weight=wd.norm_w, eps=EPS, y=y))
+    torch.cuda.synchronize()
+    cu = w.cu_seqlens.tolist()
+    assert torch.all(y[cu[1]:cu[2]] == 5.0)  # the skipped sequence: y untouched
+    y_sep = torch.empty_like(y)
+    K.gated_rmsnorm_out(o, wd.z, wd.norm_w, EPS, y_sep)
+    torch.cuda.synchronize()
+    for a, b in ((0, cu[1]), (cu[2], cu[3])):
+        assert torch.equal(y[a:b], y_sep[a:b])
+    ref = oracle_layer(w)
+    assert rel(y[:cu[1]], ref.y[:cu[1]]) < TOL_BF16
+    assert rel(y[cu[2]:], ref.y[cu[2]:]) < TOL_BF16
 
 
 def test_prefill_slots_and_negative_slot():
