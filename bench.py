@@ -16,7 +16,10 @@ the library's timing hook (kda_set_timing_events), around every kernel of the
 prompt call; the roofline object uses the dominant kernel's live average
 duration from that pass.  Its `traffic` comes from the
 rocprofv3 counter summary committed under profiles/, and is null when the
-kernel sources have changed since those counters were taken.
+kernel sources have changed since those counters were taken.  `rw_reference`
+is the rate this GPU sustains for a read-then-write pass (torch's in-place
+scale of 512 MiB, timed in the same run); the decode roofline and the whole
+pass also give their fraction of it.
 
 Modes besides the default run:
   --copy-calibration   also time a plain 1 GiB device copy (for counter runs:
@@ -365,9 +368,37 @@ def main():
                                       "traffic": committed_traffic("kda_rows (decode)", args.precision)},
                          "algorithmic_bytes_per_step": dbytes}
 
+    # ---------------- measured read-write reference ----------------
+    # the HBM rate this GPU sustains for the decode's access pattern (every byte read
+    # once, then written once): torch's in-place scale of a 512 MiB fp32 buffer, the
+    # size of the decode state pool
+    ref = measured_rw_reference(stream)
+    out["rw_reference"] = ref
+    out["whole_pass"]["rw_reference_frac"] = out["whole_pass"]["GB_per_s"] / ref["GB_per_s"]
+    if "decode" in out:
+        out["decode"]["roofline"]["rw_reference_frac"] = out["decode"]["roofline"]["achieved"] / ref["GB_per_s"]
+
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
+
+
+def measured_rw_reference(stream, mib=512, reps=20):
+    import torch
+    x = torch.ones(mib * (1 << 20) // 4, device="cuda")
+    for _ in range(3):
+        x.mul_(0.999999)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        x.mul_(0.999999)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del x
+    return {"kind": f"torch in-place scale of {mib} MiB fp32 (read then write every byte)",
+            "GB_per_s": 2 * mib * (1 << 20) / (ms * 1e-3) / 1e9, "ms": ms}
 
 
 if __name__ == "__main__":
