@@ -368,6 +368,10 @@ def main():
                                       "traffic": committed_traffic("kda_rows (decode)", args.precision)},
                          "algorithmic_bytes_per_step": dbytes}
 
+    # ---------------- small-batch decode: eager calls against one graph replay ----------------
+    if not args.no_decode:
+        out["decode_small_batch"] = small_batch_decode(stream, args.decode_steps)
+
     # ---------------- measured read-write reference ----------------
     # the HBM rate this GPU sustains for the decode's access pattern (every byte read
     # once, then written once): torch's in-place scale of a 512 MiB fp32 buffer, the
@@ -381,6 +385,54 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
+
+
+def small_batch_decode(stream, steps, B=1, H=32, d=128):
+    """Per-step time of B=1 decode issued call by call, and of the same steps
+    captured once in a HIP graph and replayed (launch overhead is what a small
+    batch pays)."""
+    import torch
+    import kimi_delta_attention_prep_amd as K
+    from kimi_delta_attention_prep_amd import inputs as I
+    w = I.decode(B=B, steps=steps, H=H, d=d, seed=3)
+    dd = K.Dims(H, d, d, w.dtype)
+    rows = {n: I.step_rows(w, n, steps).cuda() for n in ("q", "k", "v", "g", "beta")}
+    st, cs, cw = w.state0.cuda(), w.conv_state0.cuda(), w.conv_w.cuda()
+    o = torch.empty(steps, B, H, d, device="cuda")
+
+    def run():
+        for t in range(steps):
+            K.kda_decode(dd, st, cs, cw, rows["q"][t], rows["k"][t], rows["v"][t], rows["g"][t], rows["beta"][t],
+                         w.gate_mode, w.lower_bound, o[t])
+
+    run()
+    torch.cuda.synchronize()
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    e0, e1 = mk(), mk()
+    e0.record(stream)
+    run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    eager = e0.elapsed_time(e1) / steps
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = mk(), mk()
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    graph = e0.elapsed_time(e1) / steps
+    return {"workload": f"decode B={B} H={H} d={d}, {steps} steps", "eager_us_per_step": eager * 1e3,
+            "graph_us_per_step": graph * 1e3, "graph_tokens_per_s": B / (graph * 1e-3)}
 
 
 def measured_rw_reference(stream, mib=512, reps=20):
