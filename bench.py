@@ -368,6 +368,9 @@ def main():
                                       "traffic": committed_traffic("kda_rows (decode)", args.precision)},
                          "algorithmic_bytes_per_step": dbytes}
 
+    # ---------------- the scalar-decay layer on the same prompt workload ----------------
+    out["prefill_scalar_decay"] = scalar_decay_prefill(stream, w, prec, args.steps, args.warmup)
+
     # ---------------- small-batch decode: eager calls against one graph replay ----------------
     if not args.no_decode:
         out["decode_small_batch"] = small_batch_decode(stream, args.decode_steps)
@@ -385,6 +388,38 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
+
+
+def scalar_decay_prefill(stream, w, prec, steps, warmup):
+    """The prompt pass of the benchmark workload with one decay per head and row
+    (raw g rows [T, H], the scalar-decay layer), same call as the timed step."""
+    import torch
+    import kimi_delta_attention_prep_amd as K
+    T, H, dk, dv = w.T, w.H, w.dk, w.dv
+    d = K.Dims(H, dk, dv, w.dtype, precision=prec, decay_per_head=True)
+    wd = w.to("cuda")
+    gh = wd.g[:, :, 0].contiguous()
+    state, cs = wd.state0.clone(), wd.conv_state0.clone()
+    o = torch.empty(T, H, dv, device="cuda")
+    y = torch.empty(T, H, dv, device="cuda", dtype=torch.bfloat16)
+    ws = torch.empty(K.kda_prefill_workspace_bytes(d, w.N, T), dtype=torch.uint8, device="cuda")
+    raw = dict(q_raw=wd.q, k_raw=wd.k, v_raw=wd.v, g_raw=gh, beta_logit=wd.beta, conv_weight=wd.conv_w,
+               conv_state_in=cs, conv_state_out=cs, gate_mode=w.gate_mode, lower_bound=w.lower_bound)
+    norm = dict(z=wd.z, weight=wd.norm_w, eps=1e-6, y=y)
+    step = lambda: K.kda_prefill_varlen(d, wd.cu_seqlens, None, None, None, None, None, state, o, ws, raw=raw,
+                                        norm=norm)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"workload": f"prefill T={T} H={H} d={dk}, one decay per head and row (g rows [T, H])",
+            "value": T / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms}
 
 
 def small_batch_decode(stream, steps, B=1, H=32, d=128):

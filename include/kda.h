@@ -28,6 +28,7 @@
  *   - Streams: every call is enqueued on `stream` and returns without waiting.
  *   - Layouts: row-major, token-major packed rows.
  *       q, k, g rows      [T, H, d_k]      v, z, o rows   [T, H, d_v]
+ *       (raw g rows [T, H] when decay_shape is KDA_DECAY_PER_HEAD)
  *       beta logits       [T, H]
  *       state             [S_slots, H, d_k, d_v]  fp32, d_v contiguous
  *       conv channels     C = H*(2*d_k + d_v), ordered [q: H*d_k | k: H*d_k | v: H*d_v]
@@ -74,6 +75,12 @@ enum kda_status {
 enum kda_dtype { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 };
 enum kda_gate { KDA_GATE_SOFTPLUS = 0, KDA_GATE_SAFE = 1 };
 enum kda_act { KDA_ACT_NONE = 0, KDA_ACT_SILU = 1 };
+/* Shape of the decay: one log decay per key dim (the KDA layer), or one per head
+ * and row broadcast over the key dims (the scalar-decay gated delta rule); raw g
+ * rows are then [.., H] instead of [.., H, d_k].  The recurrence is the same
+ * with equal per-dim decays, and every entry point gives the bits it gives for
+ * the broadcast rows. */
+enum kda_decay { KDA_DECAY_PER_DIM = 0, KDA_DECAY_PER_HEAD = 1 };
 /* Arithmetic of the chunked prompt path's matrix products (all accumulate in fp32):
  *   FP32   fp32 matrix-core products;
  *   BF16X3 each fp32 operand split into bf16 hi + lo and the product formed as
@@ -92,6 +99,7 @@ typedef struct kda_dims {
   int32_t in_dtype;   /* kda_dtype of raw rows (q, k, v, g, beta logits) and of the conv state */
   int32_t conv_act;   /* kda_act applied after the conv */
   int32_t precision;  /* kda_precision of the prompt path's matrix products */
+  int32_t decay_shape; /* kda_decay of the raw g rows */
 } kda_dims;
 
 /* Log of a verify window: everything a later call needs to commit its rows.

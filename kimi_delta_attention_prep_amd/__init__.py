@@ -28,6 +28,7 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 GATE_SOFTPLUS, GATE_SAFE = 0, 1
 ACT_NONE, ACT_SILU = 0, 1
 PREC_FP32, PREC_BF16X3, PREC_FP16 = 0, 1, 2
+DECAY_PER_DIM, DECAY_PER_HEAD = 0, 1
 EXPORTS = ("kda_prep", "kda_prefill_workspace_bytes", "kda_prefill_varlen", "kda_decode", "kda_verify_window",
            "gated_rmsnorm_out", "kda_last_error", "kda_set_timing_events")
 
@@ -41,7 +42,7 @@ class KdaError(RuntimeError):
 class KdaDims(ctypes.Structure):
     _fields_ = [("num_heads", ctypes.c_int32), ("head_dim_k", ctypes.c_int32), ("head_dim_v", ctypes.c_int32),
                 ("conv_width", ctypes.c_int32), ("in_dtype", ctypes.c_int32), ("conv_act", ctypes.c_int32),
-                ("precision", ctypes.c_int32)]
+                ("precision", ctypes.c_int32), ("decay_shape", ctypes.c_int32)]
 
 
 class KdaRawRows(ctypes.Structure):
@@ -132,13 +133,18 @@ class Dims:
     in_dtype: torch.dtype = torch.bfloat16
     conv_act: int = ACT_SILU
     precision: int | None = None  # default: FP32 for fp32 rows, BF16X3 for bf16 rows
+    decay_per_head: bool = False  # raw g rows [.., H]: one decay per head (scalar-decay layer)
 
     def c(self) -> KdaDims:
         prec = self.precision
         if prec is None:
             prec = PREC_FP32 if self.in_dtype == torch.float32 else PREC_BF16X3
         return KdaDims(self.num_heads, self.head_dim_k, self.head_dim_v, 4, _dtype_code(self.in_dtype), self.conv_act,
-                       prec)
+                       prec, DECAY_PER_HEAD if self.decay_per_head else DECAY_PER_DIM)
+
+    def g_shape(self, *lead) -> tuple:
+        """Shape of raw g rows with leading dims `lead` (then H, and d_k unless the decay is per head)."""
+        return (*lead, self.num_heads) if self.decay_per_head else (*lead, self.num_heads, self.head_dim_k)
 
     @property
     def conv_channels(self) -> int:
@@ -153,7 +159,7 @@ def kda_prep(d: Dims, cu_seqlens, q_raw, k_raw, v_raw, conv_weight, conv_state_i
     H, dk, dv, dt = d.num_heads, d.head_dim_k, d.head_dim_v, d.in_dtype
     _need(cu_seqlens, "cu_seqlens", torch.int32)
     for name, t, shp in (("q_raw", q_raw, (T, H, dk)), ("k_raw", k_raw, (T, H, dk)), ("v_raw", v_raw, (T, H, dv)),
-                         ("g_raw", g_raw, (T, H, dk)), ("beta_logit", beta_logit, (T, H))):
+                         ("g_raw", g_raw, d.g_shape(T)), ("beta_logit", beta_logit, (T, H))):
         _need(t, name, dt, shp)
     _need(conv_weight, "conv_weight", torch.float32, (d.conv_channels, 4))
     _need(conv_state_in, "conv_state_in", dt)
@@ -193,7 +199,7 @@ def kda_prefill_varlen(d: Dims, cu_seqlens, q_hat, k_hat, v, g, beta, state, o, 
     else:
         T = raw["q_raw"].shape[0]
         dt = d.in_dtype
-        for name, shp in (("q_raw", (T, H, dk)), ("k_raw", (T, H, dk)), ("v_raw", (T, H, dv)), ("g_raw", (T, H, dk)),
+        for name, shp in (("q_raw", (T, H, dk)), ("k_raw", (T, H, dk)), ("v_raw", (T, H, dv)), ("g_raw", d.g_shape(T)),
                           ("beta_logit", (T, H))):
             _need(raw[name], name, dt, shp)
         _need(raw["conv_weight"], "conv_weight", torch.float32, (d.conv_channels, 4))
@@ -229,7 +235,7 @@ def kda_decode(d: Dims, state, conv_state, conv_weight, q_raw, k_raw, v_raw, g_r
     B = q_raw.shape[0]
     H, dk, dv, dt = d.num_heads, d.head_dim_k, d.head_dim_v, d.in_dtype
     for name, t, shp in (("q_raw", q_raw, (B, H, dk)), ("k_raw", k_raw, (B, H, dk)), ("v_raw", v_raw, (B, H, dv)),
-                         ("g_raw", g_raw, (B, H, dk)), ("beta_logit", beta_logit, (B, H))):
+                         ("g_raw", g_raw, d.g_shape(B)), ("beta_logit", beta_logit, (B, H))):
         _need(t, name, dt, shp)
     _need(state, "state", torch.float32)
     _need(conv_state, "conv_state", dt)
@@ -276,7 +282,7 @@ def kda_verify_window(d: Dims, state, conv_state, conv_weight, n_commit, log_in,
     B = batch if batch is not None else (q_raw.shape[0] if q_raw is not None else n_commit.numel())
     if W > 0:
         for name, t, shp in (("q_raw", q_raw, (B, W, H, dk)), ("k_raw", k_raw, (B, W, H, dk)),
-                             ("v_raw", v_raw, (B, W, H, dv)), ("g_raw", g_raw, (B, W, H, dk)),
+                             ("v_raw", v_raw, (B, W, H, dv)), ("g_raw", g_raw, d.g_shape(B, W)),
                              ("beta_logit", beta_logit, (B, W, H))):
             _need(t, name, dt, shp)
         _need(o, "o", torch.float32, (B, W, H, dv))

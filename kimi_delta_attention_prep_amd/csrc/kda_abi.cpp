@@ -47,6 +47,8 @@ int check_dims(const kda_dims* d) {
     return fail(KDA_E_DTYPE, "unknown conv_act %d", d->conv_act);
   if (d->precision != KDA_PREC_FP32 && d->precision != KDA_PREC_BF16X3 && d->precision != KDA_PREC_FP16)
     return fail(KDA_E_DTYPE, "unknown precision %d", d->precision);
+  if (d->decay_shape != KDA_DECAY_PER_DIM && d->decay_shape != KDA_DECAY_PER_HEAD)
+    return fail(KDA_E_GEOMETRY, "unknown decay shape %d", d->decay_shape);
   return KDA_OK;
 }
 
@@ -122,6 +124,7 @@ int kda_prep(const kda_dims* d, int32_t num_seqs, int64_t t_tot, const int32_t* 
   kda::PrepLaunch L{d->num_heads, d->head_dim_k, d->head_dim_v, d->in_dtype, d->conv_act, gate_mode, num_seqs, t_tot,
                     lower_bound, cu_seqlens, slots, q_raw, k_raw, v_raw, g_raw, beta_logit, conv_weight,
                     conv_state_in, conv_state_out, q_hat, k_hat, v_out, g_out, beta_out};
+  L.g_per_head = d->decay_shape == KDA_DECAY_PER_HEAD;
   return hip_status(kda::launch_prep(L, stream), "kda_prep");
 }
 
@@ -185,6 +188,7 @@ int kda_prefill_varlen(const kda_dims* d, int32_t num_seqs, int64_t t_tot, const
   L.events = g_events; L.nevents = g_nevents;
   if (raw) {
     L.fused = 1; L.gate_mode = raw->gate_mode; L.lb = raw->lower_bound;
+    L.g_per_head = d->decay_shape == KDA_DECAY_PER_HEAD;
     L.raw_q = raw->q_raw; L.raw_k = raw->k_raw; L.raw_v = raw->v_raw; L.raw_g = raw->g_raw;
     L.raw_beta = raw->beta_logit; L.conv_w = raw->conv_weight; L.cs_in = raw->conv_state_in;
     L.cs_out = raw->conv_state_out;
@@ -215,6 +219,7 @@ int kda_decode(const kda_dims* d, int32_t batch, const int32_t* slots, float* st
   KDA_TRY(check_ptrs("kda_decode: rows", {conv_state, q_raw, k_raw, v_raw, g_raw, beta_logit}, elem_bytes(d->in_dtype)));
   kda::RowsLaunch L{};
   L.H = d->num_heads; L.dk = d->head_dim_k; L.dv = d->head_dim_v; L.in_dtype = d->in_dtype; L.act = d->conv_act;
+  L.g_per_head = d->decay_shape == KDA_DECAY_PER_HEAD;
   L.gate_mode = gate_mode; L.batch = batch; L.window = 1; L.lb = lower_bound; L.slots = slots; L.state = state;
   L.conv_state = conv_state; L.conv_w = conv_weight; L.q = q_raw; L.k = k_raw; L.v = v_raw; L.g = g_raw;
   L.beta = beta_logit; L.o = o;
@@ -265,6 +270,7 @@ int kda_verify_window(const kda_dims* d, int32_t batch, int32_t window, const in
   if (!commit && window == 0) return ok();
   kda::RowsLaunch L{};
   L.H = d->num_heads; L.dk = d->head_dim_k; L.dv = d->head_dim_v; L.in_dtype = d->in_dtype; L.act = d->conv_act;
+  L.g_per_head = d->decay_shape == KDA_DECAY_PER_HEAD;
   L.gate_mode = gate_mode; L.batch = batch; L.window = window; L.lb = lower_bound; L.slots = slots; L.state = state;
   L.conv_state = conv_state; L.conv_w = conv_weight; L.q = q_raw; L.k = k_raw; L.v = v_raw; L.g = g_raw;
   L.beta = beta_logit; L.o = o;

@@ -23,6 +23,7 @@ struct RowsLaunch {
   int in_window;
   float *out_a, *out_k, *out_u;
   void* out_rows;
+  int g_per_head = 0;  // raw g rows [B, (window,) H]
 };
 hipError_t launch_rows(const RowsLaunch& L, bool verify, hipStream_t s);
 
@@ -52,6 +53,7 @@ struct PrepLaunch {
   const void* cs_in;
   void* cs_out;
   float *q_hat, *k_hat, *v_out, *g_out, *beta_out;
+  int g_per_head = 0;  // raw g rows [T, H]: one decay per head, broadcast over d_k
 };
 hipError_t launch_prep(const PrepLaunch& L, hipStream_t s);
 
@@ -74,6 +76,7 @@ struct PrefillLaunch {
   // measurement hook: events[2i], events[2i+1] around kernel i (2i+1 < nevents)
   hipEvent_t* events;
   int nevents;
+  int g_per_head = 0;  // raw g rows [T, H] (fused preamble)
 };
 size_t prefill_workspace_bytes(int H, int dk, int dv, int precision, int num_seqs, int64_t t_tot);
 hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t s);

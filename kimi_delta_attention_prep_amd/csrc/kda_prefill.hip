@@ -325,6 +325,7 @@ struct RawRowsArgs {
   int act, gate_mode;
   float lb;
   int esize;  // bytes per raw element; 0 without raw rows (nothing to carry)
+  int g_per_head;  // raw g rows [T, H]: one decay per head and row, broadcast over d_k
 };
 
 struct PrefillArgs {
@@ -646,6 +647,7 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
     // start together, so the first load of every CU meets the others' in HBM:
     // keeping that burst to the q rows gets q in sooner.
     uint4 xq[NSK], xk[NSK], xg[NGK];
+    RawT xgh[NGK];
 #pragma unroll
     for (int i = 0; i < NSK; ++i) xq[i] = load_staged(static_cast<const RawT*>(p.raw.q), DK, t + i * NT);
     // each stream's conv weights load right after its rows (a wait for them is then no
@@ -683,7 +685,13 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
 #pragma unroll
     for (int i = 0; i < NGK; ++i) {
       const int idx = t + i * NT, r = idx / (DK / VE), c0 = (idx % (DK / VE)) * VE;
-      xg[i] = *reinterpret_cast<const uint4*>(rg + (idx < L * (DK / VE) && r < len ? ((start + r) * H + h) * DK + c0 : 0));
+      // both loads are unconditional: with one decay per head, the 16-byte piece reads
+      // the q rows' first piece instead (g may hold fewer than 16 bytes) and the row's
+      // own decay comes from the scalar load, which otherwise reads g's first element
+      const bool ok = idx < L * (DK / VE) && r < len;
+      xg[i] = *reinterpret_cast<const uint4*>(p.raw.g_per_head ? static_cast<const RawT*>(p.raw.q)
+                                                               : rg + (ok ? ((start + r) * H + h) * DK + c0 : 0));
+      xgh[i] = rg[p.raw.g_per_head && ok ? (start + r) * H + h : 0];
     }
     const RawT braw = static_cast<const RawT*>(p.raw.beta)[t < len ? (start + t) * H + h : 0];
     if constexpr (kVStaged) {
@@ -701,7 +709,9 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
         float gv[VE];
 #pragma unroll
         for (int e = 0; e < VE; ++e)
-          gv[e] = r < len ? log_decay(piece_elem<RawT>(xg[i], e), p.raw.gate_mode, p.raw.lb) : 0.f;
+          gv[e] = r < len ? log_decay(p.raw.g_per_head ? to_f32(xgh[i]) : piece_elem<RawT>(xg[i], e),
+                                      p.raw.gate_mode, p.raw.lb)
+                          : 0.f;
 #pragma unroll
         for (int e = 0; e < VE; e += 4)
           *reinterpret_cast<float4*>(&sG[r * PK + c0 + e]) = make_float4(gv[e], gv[e + 1], gv[e + 2], gv[e + 3]);
@@ -1393,7 +1403,7 @@ static hipError_t launch_prefill_t(const PrefillLaunch& Lc, hipStream_t s) {
   p.H = Lc.H; p.num_seqs = Lc.num_seqs; p.cu = Lc.cu_seqlens; p.slots = Lc.slots;
   p.q = Lc.q_hat; p.k = Lc.k_hat; p.v = Lc.v; p.g = Lc.g; p.beta = Lc.beta; p.state = Lc.state; p.o = Lc.o;
   p.raw = {Lc.raw_q, Lc.raw_k, Lc.raw_v, Lc.raw_g, Lc.raw_beta, Lc.conv_w, Lc.cs_in, Lc.cs_out,
-           Lc.act, Lc.gate_mode, Lc.lb, FUSED ? (int)sizeof(RawT) : 0};
+           Lc.act, Lc.gate_mode, Lc.lb, FUSED ? (int)sizeof(RawT) : 0, Lc.g_per_head};
   p.sink = static_cast<float*>(Lc.workspace);
   p.recs = static_cast<uint8_t*>(Lc.workspace) + kSinkBytes;
   p.rec_bytes = rec_layout(DK, DV, Frag<POL>::BYTES).bytes;

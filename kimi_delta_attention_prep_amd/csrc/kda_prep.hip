@@ -27,6 +27,7 @@ struct PrepArgs {
   const RawT* cs_in;
   RawT* cs_out;
   float *q_hat, *k_hat, *v_out, *g_out, *beta_out;
+  int g_per_head;  // raw g rows [T, H]: one decay per head and row, broadcast over d_k
 };
 
 // sequence n such that cu[n] <= row < cu[n+1] (cu non-decreasing; zero-length
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<RawT> p) {
   for (int e = 0; e < EK; ++e) {
     p.q_hat[ok + e] = q[0][e];
     p.k_hat[ok + e] = k[0][e];
-    p.g_out[ok + e] = log_decay(to_f32(p.g[ok + e]), p.gate_mode, p.lb);
+    p.g_out[ok + e] = log_decay(to_f32(p.g[p.g_per_head ? pair : ok + e]), p.gate_mode, p.lb);
   }
 #pragma unroll
   for (int e = 0; e < EV; ++e) p.v_out[ov + e] = v[0][e];
@@ -120,6 +121,7 @@ static hipError_t launch_prep_t(const PrepLaunch& L, hipStream_t s) {
   p.cu = L.cu_seqlens; p.slots = L.slots;
   p.q = static_cast<const RawT*>(L.q); p.k = static_cast<const RawT*>(L.k); p.v = static_cast<const RawT*>(L.v);
   p.g = static_cast<const RawT*>(L.g); p.beta = static_cast<const RawT*>(L.beta); p.conv_w = L.conv_w;
+  p.g_per_head = L.g_per_head;
   p.cs_in = static_cast<const RawT*>(L.cs_in); p.cs_out = static_cast<RawT*>(L.cs_out);
   p.q_hat = L.q_hat; p.k_hat = L.k_hat; p.v_out = L.v_out; p.g_out = L.g_out; p.beta_out = L.beta_out;
   const int64_t waves = L.t_tot * L.H;

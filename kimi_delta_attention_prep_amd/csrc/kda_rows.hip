@@ -37,6 +37,7 @@ struct RowsShape {
 template <typename RawT>
 struct RowsArgs {
   int H, gate_mode, act, batch, window;
+  int g_per_head;  // raw g rows [B, (window,) H]: one decay per head and row, broadcast over d_k
   float lb;
   const int32_t* slots;
   float* state;
@@ -88,7 +89,7 @@ struct RowStep {
                      to_f32(ch.hk[2]), to_f32(raw_k), p.act);
       ch.hq[0] = ch.hq[1]; ch.hq[1] = ch.hq[2]; ch.hq[2] = raw_q;
       ch.hk[0] = ch.hk[1]; ch.hk[1] = ch.hk[2]; ch.hk[2] = raw_k;
-      s_a[t] = expf(log_decay(to_f32(p.g[row_hd_k + t]), p.gate_mode, p.lb));
+      s_a[t] = expf(log_decay(to_f32(p.g[p.g_per_head ? row_h : row_hd_k + t]), p.gate_mode, p.lb));
     } else if (t < DK + DV) {
       const int j = t - DK;
       raw_q = p.v[row_hd_v + j];
@@ -305,6 +306,7 @@ static hipError_t launch_rows_t(const RowsLaunch& L, hipStream_t s) {
   p.slots = L.slots; p.state = L.state; p.conv_state = static_cast<RawT*>(L.conv_state); p.conv_w = L.conv_w;
   p.q = static_cast<const RawT*>(L.q); p.k = static_cast<const RawT*>(L.k); p.v = static_cast<const RawT*>(L.v);
   p.g = static_cast<const RawT*>(L.g); p.beta = static_cast<const RawT*>(L.beta); p.o = L.o;
+  p.g_per_head = L.g_per_head;
   p.n_commit = L.n_commit; p.in_a = L.in_a; p.in_k = L.in_k; p.in_u = L.in_u;
   p.in_rows = static_cast<const RawT*>(L.in_rows); p.in_window = L.in_window;
   p.out_a = L.out_a; p.out_k = L.out_k; p.out_u = L.out_u; p.out_rows = static_cast<RawT*>(L.out_rows);

@@ -46,8 +46,8 @@ MIS = ctypes.c_void_p(0x10001)  # misaligned for every element type
 MIS4 = ctypes.c_void_p(0x10004)  # element-aligned, not 16-byte aligned
 
 
-def dims(H=2, dk=128, dv=128, W=4, dt=K.DTYPE_BF16, act=K.ACT_SILU, prec=K.PREC_BF16X3):
-    return K.KdaDims(H, dk, dv, W, dt, act, prec)
+def dims(H=2, dk=128, dv=128, W=4, dt=K.DTYPE_BF16, act=K.ACT_SILU, prec=K.PREC_BF16X3, decay=K.DECAY_PER_DIM):
+    return K.KdaDims(H, dk, dv, W, dt, act, prec, decay)
 
 
 def decode(lib, d, *, q=A, gate=K.GATE_SAFE, lb=-5.0, batch=4, slots=None, state=A):
@@ -57,7 +57,7 @@ def decode(lib, d, *, q=A, gate=K.GATE_SAFE, lb=-5.0, batch=4, slots=None, state
 @pytest.mark.parametrize("d,code", [
     (dims(dk=96), K.KDA_E_GEOMETRY), (dims(dv=32), K.KDA_E_GEOMETRY), (dims(W=3), K.KDA_E_GEOMETRY),
     (dims(dt=7), K.KDA_E_DTYPE), (dims(act=3), K.KDA_E_DTYPE), (dims(prec=5), K.KDA_E_DTYPE),
-    (dims(H=0), K.KDA_E_ARG),
+    (dims(H=0), K.KDA_E_ARG), (dims(decay=2), K.KDA_E_GEOMETRY), (dims(decay=-1), K.KDA_E_GEOMETRY),
 ])
 def test_geometry_and_dtype_rejected_before_launch(lib, d, code):
     assert decode(lib, d) == code
