@@ -374,6 +374,7 @@ def main():
     # ---------------- small-batch decode: eager calls against one graph replay ----------------
     if not args.no_decode:
         out["decode_small_batch"] = small_batch_decode(stream, args.decode_steps)
+        out["verify_window"] = verify_windows(stream, args.steps, args.warmup)
 
     # ---------------- measured read-write reference ----------------
     # the HBM rate this GPU sustains for the decode's access pattern (every byte read
@@ -420,6 +421,47 @@ def scalar_decay_prefill(stream, w, prec, steps, warmup):
     ms = e0.elapsed_time(e1) / steps
     return {"workload": f"prefill T={T} H={H} d={dk}, one decay per head and row (g rows [T, H])",
             "value": T / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms}
+
+
+def verify_windows(stream, steps, warmup, B=64, W=4, H=32, d=128):
+    """Speculative verify: each step commits the previous window's accepted rows
+    (seeded, within the rows each sequence ran) and runs a new window whose
+    length per sequence is seeded in 1..W, in one kda_verify_window call."""
+    import torch
+    import kimi_delta_attention_prep_amd as K
+    from kimi_delta_attention_prep_amd import inputs as I
+    w = I.generate("verify", lengths=[W] * B, H=H, dk=d, dv=d, dtype=torch.bfloat16, gate_mode=I.GATE_SAFE,
+                   state_std=0.02, conv_state_std=1.0, seed=5)
+    dd = K.Dims(H, d, d, w.dtype)
+    rows = {n: getattr(w, n).view(B, W, *getattr(w, n).shape[1:]).cuda() for n in ("q", "k", "v", "g", "beta")}
+    st, cs, cw = w.state0.cuda(), w.conv_state0.cuda(), w.conv_w.cuda()
+    gen = torch.Generator().manual_seed(6)
+    lens = torch.randint(1, W + 1, (B,), generator=gen, dtype=torch.int32)
+    keep = (torch.rand(B, generator=gen) * (lens.float() + 1)).floor().clamp(max=lens.float()).to(torch.int32)
+    lens, keep = lens.cuda(), keep.cuda()
+    logs = [K.VerifyLog.empty(dd, B, W), K.VerifyLog.empty(dd, B, W)]
+    o = torch.empty(B, W, H, d, device="cuda")
+    K.kda_verify_window(dd, st, cs, cw, None, None, logs[0], rows["q"], rows["k"], rows["v"], rows["g"],
+                        rows["beta"], w.gate_mode, w.lower_bound, o, window_lens=lens)
+
+    def step(i):
+        K.kda_verify_window(dd, st, cs, cw, keep, logs[i % 2], logs[(i + 1) % 2], rows["q"], rows["k"], rows["v"],
+                            rows["g"], rows["beta"], w.gate_mode, w.lower_bound, o, window_lens=lens)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        step(warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nrows = int(lens.sum())
+    return {"workload": f"verify B={B} window<={W} H={H} d={d}: commit + new window per call, lengths 1..{W} seeded",
+            "ms_per_call": ms, "draft_rows_per_call": nrows, "draft_rows_per_s": nrows / (ms * 1e-3),
+            "state_GB_per_s": 2 * B * H * d * d * 4 / (ms * 1e-3) / 1e9}
 
 
 def small_batch_decode(stream, steps, B=1, H=32, d=128):

@@ -204,11 +204,16 @@ int kda_decode(const kda_dims* d, int32_t batch, const int32_t* slots, float* st
  * committed state, writes their outputs o [batch, window, H, d_v] (same bits
  * as kda_decode on those rows) and their log to log_out.  The state and conv
  * state stay at the committed point.  window = 0 only commits.
+ *   window_lens  int32 [batch] device, or NULL: sequence b runs only its first
+ *             window_lens[b] rows of the window (clamped to [0, window]); its o
+ *             and log rows past those are left alone, and a later commit of
+ *             more rows than it ran is outside the preconditions
  *   n_commit  int32 [batch] device, or NULL when log_in is NULL (nothing to commit)
  *   rows      q_raw,k_raw,g_raw [batch,window,H,d_k], v_raw [batch,window,H,d_v],
  *             beta_logit [batch,window,H]  (in_dtype)
  *   log_out   buffers sized for `window`; must not overlap log_in. */
-int kda_verify_window(const kda_dims* d, int32_t batch, int32_t window, const int32_t* slots, float* state,
+int kda_verify_window(const kda_dims* d, int32_t batch, int32_t window, const int32_t* window_lens,
+                      const int32_t* slots, float* state,
                       void* conv_state, const float* conv_weight, const int32_t* n_commit, const kda_log* log_in,
                       const kda_log* log_out, const void* q_raw, const void* k_raw, const void* v_raw,
                       const void* g_raw, const void* beta_logit, int32_t gate_mode, float lower_bound, float* o,

@@ -81,7 +81,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.kda_prefill_varlen.argtypes = [D, i32, i64, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(KdaRawRows),
                                            ctypes.POINTER(KdaNormArgs), vp, vp, vp, ctypes.c_size_t, vp]
         lib.kda_decode.argtypes = [D, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp]
-        lib.kda_verify_window.argtypes = [D, i32, i32, vp, vp, vp, vp, vp, Lg, Lg, vp, vp, vp, vp, vp, i32, f32, vp, vp]
+        lib.kda_verify_window.argtypes = [D, i32, i32, vp, vp, vp, vp, vp, vp, Lg, Lg, vp, vp, vp, vp, vp, i32, f32, vp,
+                                          vp]
         lib.gated_rmsnorm_out.argtypes = [i64, i32, vp, vp, i32, vp, f32, vp, i32, vp]
         lib.kda_last_error.restype = ctypes.c_char_p
         lib.kda_set_timing_events.argtypes = [vp, i32]
@@ -275,7 +276,7 @@ class VerifyLog:
 
 
 def kda_verify_window(d: Dims, state, conv_state, conv_weight, n_commit, log_in, log_out, q_raw, k_raw, v_raw,
-                      g_raw, beta_logit, gate_mode, lower_bound, o, slots=None, batch=None):
+                      g_raw, beta_logit, gate_mode, lower_bound, o, slots=None, batch=None, window_lens=None):
     lib = load_library()
     H, dk, dv, dt = d.num_heads, d.head_dim_k, d.head_dim_v, d.in_dtype
     W = 0 if q_raw is None else q_raw.shape[1]
@@ -296,7 +297,10 @@ def kda_verify_window(d: Dims, state, conv_state, conv_weight, n_commit, log_in,
     dims = d.c()
     lin = log_in.c() if log_in is not None else None
     lout = log_out.c() if log_out is not None else None
-    _check(lib.kda_verify_window(ctypes.byref(dims), B, W, _ptr(slots), _ptr(state), _ptr(conv_state),
+    if window_lens is not None:
+        _need(window_lens, "window_lens", torch.int32, (B,))
+    _check(lib.kda_verify_window(ctypes.byref(dims), B, W, _ptr(window_lens), _ptr(slots), _ptr(state),
+                                 _ptr(conv_state),
                                  _ptr(conv_weight), _ptr(n_commit), ctypes.byref(lin) if lin else None,
                                  ctypes.byref(lout) if lout else None, _ptr(q_raw), _ptr(k_raw), _ptr(v_raw),
                                  _ptr(g_raw), _ptr(beta_logit), int(gate_mode), float(lower_bound), _ptr(o),

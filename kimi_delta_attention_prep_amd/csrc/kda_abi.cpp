@@ -226,7 +226,8 @@ int kda_decode(const kda_dims* d, int32_t batch, const int32_t* slots, float* st
   return hip_status(kda::launch_rows(L, false, stream), "kda_decode");
 }
 
-int kda_verify_window(const kda_dims* d, int32_t batch, int32_t window, const int32_t* slots, float* state,
+int kda_verify_window(const kda_dims* d, int32_t batch, int32_t window, const int32_t* window_lens,
+                      const int32_t* slots, float* state,
                       void* conv_state, const float* conv_weight, const int32_t* n_commit, const kda_log* log_in,
                       const kda_log* log_out, const void* q_raw, const void* k_raw, const void* v_raw,
                       const void* g_raw, const void* beta_logit, int32_t gate_mode, float lower_bound, float* o,
@@ -244,6 +245,7 @@ int kda_verify_window(const kda_dims* d, int32_t batch, int32_t window, const in
     return fail(KDA_E_GEOMETRY, "kda_verify_window: log_out sized for %d rows, window is %d", log_out->window, window);
   if (batch == 0) return ok();
   KDA_TRY(check_opt_ptr("kda_verify_window: slots", slots));
+  KDA_TRY(check_opt_ptr("kda_verify_window: window_lens", window_lens));
   const unsigned eb = elem_bytes(d->in_dtype);
   KDA_TRY(check_ptrs("kda_verify_window: state", {state}));
   KDA_TRY(check_ptrs("kda_verify_window: conv weight", {conv_weight}, 4));
@@ -274,7 +276,7 @@ int kda_verify_window(const kda_dims* d, int32_t batch, int32_t window, const in
   L.gate_mode = gate_mode; L.batch = batch; L.window = window; L.lb = lower_bound; L.slots = slots; L.state = state;
   L.conv_state = conv_state; L.conv_w = conv_weight; L.q = q_raw; L.k = k_raw; L.v = v_raw; L.g = g_raw;
   L.beta = beta_logit; L.o = o;
-  L.n_commit = n_commit;
+  L.n_commit = n_commit; L.window_lens = window > 0 ? window_lens : nullptr;
   if (commit) {
     L.in_a = log_in->a; L.in_k = log_in->k_hat; L.in_u = log_in->u; L.in_rows = log_in->conv_rows;
     L.in_window = log_in->window;

@@ -24,6 +24,7 @@ struct RowsLaunch {
   float *out_a, *out_k, *out_u;
   void* out_rows;
   int g_per_head = 0;  // raw g rows [B, (window,) H]
+  const int32_t* window_lens = nullptr;  // verify: rows per sequence, NULL = window
 };
 hipError_t launch_rows(const RowsLaunch& L, bool verify, hipStream_t s);
 

@@ -47,6 +47,7 @@ struct RowsArgs {
   float* o;                          // [B, window, H, d_v]
   // verify only
   const int32_t* n_commit;
+  const int32_t* wlen;  // rows of the window per sequence, or NULL (all `window`)
   const float *in_a, *in_k, *in_u;
   const RawT* in_rows;
   int in_window;
@@ -260,7 +261,12 @@ __global__ __launch_bounds__(256) void kda_rows_kernel(RowsArgs<RawT> p) {
         for (int r = 0; r < 3; ++r) cs[r * C + ck_ch] = ch.hk[r];
     }
     // 4. the window's own rows, on the register copy of the committed state
-    for (int r = 0; r < p.window; ++r) {
+    int nrow = p.window;  // uniform over the workgroup (one sequence)
+    if (p.wlen) {
+      const int wl = p.wlen[b];
+      nrow = wl < 0 ? 0 : (wl > p.window ? p.window : wl);
+    }
+    for (int r = 0; r < nrow; ++r) {
       const int64_t row_h = ((int64_t)b * p.window + r) * H + h;
       RawT raw_q{}, raw_k{};
       const float qk = rs.preamble(p, ch, row_h * DK, row_h * DV, row_h, raw_q, raw_k);
@@ -307,7 +313,7 @@ static hipError_t launch_rows_t(const RowsLaunch& L, hipStream_t s) {
   p.q = static_cast<const RawT*>(L.q); p.k = static_cast<const RawT*>(L.k); p.v = static_cast<const RawT*>(L.v);
   p.g = static_cast<const RawT*>(L.g); p.beta = static_cast<const RawT*>(L.beta); p.o = L.o;
   p.g_per_head = L.g_per_head;
-  p.n_commit = L.n_commit; p.in_a = L.in_a; p.in_k = L.in_k; p.in_u = L.in_u;
+  p.n_commit = L.n_commit; p.wlen = L.window_lens; p.in_a = L.in_a; p.in_k = L.in_k; p.in_u = L.in_u;
   p.in_rows = static_cast<const RawT*>(L.in_rows); p.in_window = L.in_window;
   p.out_a = L.out_a; p.out_k = L.out_k; p.out_u = L.out_u; p.out_rows = static_cast<RawT*>(L.out_rows);
   dim3 grid(L.H, L.batch);

@@ -90,8 +90,8 @@ def test_verify_window_checks(lib):
     d = dims()
     log = K.KdaLog(A.value, A.value, A.value, A.value, 4)
     bad = K.KdaLog(A.value, A.value, A.value, A.value, 3)
-    call = lambda W, nc, lin, lout: lib.kda_verify_window(ctypes.byref(d), 4, W, None, A, A, A, nc, lin, lout, MIS, A,
-                                                           A, A, A, K.GATE_SAFE, -5.0, A, None)
+    call = lambda W, nc, lin, lout, wl=None: lib.kda_verify_window(ctypes.byref(d), 4, W, wl, None, A, A, A, nc, lin,
+                                                                    lout, MIS, A, A, A, A, K.GATE_SAFE, -5.0, A, None)
     assert call(9, None, None, ctypes.byref(log)) == K.KDA_E_GEOMETRY
     assert call(-1, None, None, ctypes.byref(log)) == K.KDA_E_GEOMETRY
     assert call(4, None, None, None) == K.KDA_E_ARG              # rows without a log to write
@@ -99,6 +99,7 @@ def test_verify_window_checks(lib):
     assert call(4, A, None, ctypes.byref(log)) == K.KDA_E_ARG    # commit counts without a log
     assert call(4, A, ctypes.byref(log), ctypes.byref(log)) == K.KDA_E_ALIGN  # misaligned q row first
     assert call(0, None, None, None) == K.KDA_OK                 # nothing to commit, no rows
+    assert call(4, None, None, ctypes.byref(log), MIS) == K.KDA_E_ALIGN  # window lengths are int32
 
 
 def test_prep_and_prefill_checks(lib):

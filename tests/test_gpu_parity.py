@@ -138,6 +138,44 @@ def test_verify_window_replay_is_bitwise_serial_decode():
     assert rel(o_v.reshape(-1, w.H, w.dv), ref.o) < TOL_BF16
 
 
+def test_verify_window_with_per_sequence_lengths():
+    """Sequence b runs only its first lens[b] rows: those rows and their log equal the full window's, the rest of
+    o and the log keep their contents, and committing the kept rows gives the state of serial decode."""
+    B, W = 5, 4
+    w, rows = _verify_setup(B, W, seed=17)
+    d = dims_for(w)
+    lens = torch.tensor([0, 4, 1, 3, 2], dtype=torch.int32)
+    cw = w.conv_w.cuda()
+    full_log, full_o = K.VerifyLog.empty(d, B, W), torch.empty(B, W, w.H, w.dv, device="cuda")
+    st, cs = w.state0.cuda().clone(), w.conv_state0.cuda().clone()
+    K.kda_verify_window(d, st, cs, cw, None, None, full_log, rows["q"], rows["k"], rows["v"], rows["g"], rows["beta"],
+                        w.gate_mode, w.lower_bound, full_o)
+    log = K.VerifyLog.empty(d, B, W)
+    for t in (log.a, log.k_hat, log.u):
+        t.fill_(3.0)
+    log.conv_rows.fill_(0)
+    o = torch.full((B, W, w.H, w.dv), 7.0, device="cuda")
+    K.kda_verify_window(d, st, cs, cw, None, None, log, rows["q"], rows["k"], rows["v"], rows["g"], rows["beta"],
+                        w.gate_mode, w.lower_bound, o, window_lens=lens.cuda())
+    torch.cuda.synchronize()
+    for b in range(B):
+        n = int(lens[b])
+        assert torch.equal(o[b, :n], full_o[b, :n])
+        assert torch.all(o[b, n:] == 7.0)
+        for got, ref in ((log.a, full_log.a), (log.k_hat, full_log.k_hat), (log.u, full_log.u),
+                         (log.conv_rows, full_log.conv_rows)):
+            assert torch.equal(got[b, :n], ref[b, :n])
+        assert torch.all(log.a[b, n:] == 3.0) and torch.all(log.conv_rows[b, n:] == 0)
+    keep = torch.tensor([0, 3, 1, 2, 2], dtype=torch.int32)  # rows kept, at most the rows run
+    K.kda_verify_window(d, st, cs, cw, keep.cuda(), log, None, None, None, None, None, None, w.gate_mode,
+                        w.lower_bound, None, batch=B)
+    st_d, cs_d = w.state0.cuda().clone(), w.conv_state0.cuda().clone()
+    _decode_rows(w, rows, d, st_d, cs_d, range(W), lambda b, s: s < int(keep[b]))
+    torch.cuda.synchronize()
+    assert torch.equal(st, st_d)
+    assert torch.equal(cs, cs_d)
+
+
 def test_verify_commit_and_next_window_in_one_call():
     """Commit the previous window and run the next one in the same call; equals serial decode bitwise."""
     B, W = 4, 3
