@@ -360,7 +360,7 @@ __device__ __forceinline__ int slot_seq(const int32_t* cu, int num_seqs, int64_t
 // ---------------------------------------------------------------------------
 // intra-chunk kernel
 //
-// One workgroup (8 wavefronts) per (chunk, head).  Pivots: every 16-row block R
+// One workgroup (16 wavefronts) per (chunk, head).  Pivots: every 16-row block R
 // is anchored at its first row, gl_r = G_r - G_{16R} (a block-local prefix sum,
 // so exponents carry only the rounding of the decay they describe):
 //   diagonal block (R,R):  left  x_r e^{gl_r}            (<= |x_r|, x = k or q)
