@@ -196,6 +196,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the prompt pass and B=256 decode (for profiler runs: the extra lines launch the same "
+                         "kernels on other shapes)")
     ap.add_argument("--unfused", action="store_true", help="run kda_prep separately instead of inside the prompt pass")
     ap.add_argument("--precision", choices=("fp16", "bf16x3", "fp32"), default="fp16",
                     help="arithmetic of the prompt path's matrix products (see kda_precision)")
@@ -369,10 +372,11 @@ def main():
                          "algorithmic_bytes_per_step": dbytes}
 
     # ---------------- the scalar-decay layer on the same prompt workload ----------------
-    out["prefill_scalar_decay"] = scalar_decay_prefill(stream, w, prec, args.steps, args.warmup)
+    if not args.no_extras:
+        out["prefill_scalar_decay"] = scalar_decay_prefill(stream, w, prec, args.steps, args.warmup)
 
     # ---------------- small-batch decode: eager calls against one graph replay ----------------
-    if not args.no_decode:
+    if not args.no_decode and not args.no_extras:
         out["decode_small_batch"] = small_batch_decode(stream, args.decode_steps)
         out["verify_window"] = verify_windows(stream, args.steps, args.warmup)
 
@@ -380,11 +384,12 @@ def main():
     # the HBM rate this GPU sustains for the decode's access pattern (every byte read
     # once, then written once): torch's in-place scale of a 512 MiB fp32 buffer, the
     # size of the decode state pool
-    ref = measured_rw_reference(stream)
-    out["rw_reference"] = ref
-    out["whole_pass"]["rw_reference_frac"] = out["whole_pass"]["GB_per_s"] / ref["GB_per_s"]
-    if "decode" in out:
-        out["decode"]["roofline"]["rw_reference_frac"] = out["decode"]["roofline"]["achieved"] / ref["GB_per_s"]
+    if not args.no_extras:
+        ref = measured_rw_reference(stream)
+        out["rw_reference"] = ref
+        out["whole_pass"]["rw_reference_frac"] = out["whole_pass"]["GB_per_s"] / ref["GB_per_s"]
+        if "decode" in out:
+            out["decode"]["roofline"]["rw_reference_frac"] = out["decode"]["roofline"]["achieved"] / ref["GB_per_s"]
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
