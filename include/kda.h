@@ -10,7 +10,9 @@
  *   2. L2 normalisation of q and k over the key dimension;
  *   3. a per-key-dimension log-decay gate g (softplus: g = -softplus(x); safe:
  *      g = lower_bound * sigmoid(x), PR #2843 gate_activation='sigmoid' with
- *      gate_lower_bound), decay a = e^g, and a per-head beta = sigmoid(x_b);
+ *      gate_lower_bound), decay a = e^g, and a per-head beta = sigmoid(x_b)
+ *      (with KDA_DECAY_PER_HEAD, one decay per head and row: the scalar-decay
+ *      gated delta rule);
  *   4. the gated delta rule on one fp32 d_k x d_v state per (sequence, head):
  *        S_t = (I - beta_t k_t k_t^T) Diag(a_t) S_{t-1} + beta_t k_t v_t^T,
  *        o_t = S_t^T q_t;
@@ -40,13 +42,15 @@
  *   - Alignment: buffers the kernels move with 128-bit accesses must be 16-byte
  *     aligned: the state, the fp32 rows q_hat/k_hat/v/g of the prompt path, the
  *     raw q/k/v/g rows handed to kda_prefill_varlen in `raw`, the output o of
- *     every call, a log's u, and every buffer of gated_rmsnorm_out.  Every other pointer needs its element alignment.
+ *     every call, a log's u, the z, weight and y of the norm epilogue, and
+ *     every buffer of gated_rmsnorm_out.  Every other pointer needs its
+ *     element alignment.
  *   - Errors: each call returns KDA_OK or one KDA_E_* code.  All validation
  *     happens before the first launch; on error nothing is enqueued and no
  *     output is written.  kda_last_error() gives a message (thread-local).
  *   - Device-side contents (cu_seqlens monotone with cu[0]=0 and cu[N]=T, slots
- *     below the pool size, commit counts within the logged window) are
- *     preconditions the library does not read back.
+ *     below the pool size, commit counts within the rows each sequence logged)
+ *     are preconditions the library does not read back.
  */
 #ifndef KDA_H
 #define KDA_H
@@ -64,7 +68,7 @@ typedef struct ihipEvent_t* hipEvent_t;
 enum kda_status {
   KDA_OK = 0,
   KDA_E_ARG = 1,       /* null pointer or negative size */
-  KDA_E_GEOMETRY = 2,  /* d_k or d_v not in {64, 128}, conv width != 4, window not in [0, 8] */
+  KDA_E_GEOMETRY = 2,  /* d_k or d_v not in {64, 128}, conv width != 4, unknown decay shape, window not in [0, 8] */
   KDA_E_ALIGN = 3,     /* a pointer is not aligned as its access needs (see Alignment) */
   KDA_E_GATE = 4,      /* unknown gate mode, or safe mode with a lower bound that is not finite and < 0 */
   KDA_E_DTYPE = 5,     /* unknown dtype, activation or precision policy */
@@ -116,6 +120,7 @@ typedef struct kda_log {
  *   cu_seqlens      int32 [num_seqs+1] device, packed row offsets
  *   slots           int32 [num_seqs] device or NULL (conv_state row of each sequence)
  *   q_raw,k_raw     [t_tot, H, d_k] in_dtype;  v_raw [t_tot, H, d_v];  g_raw [t_tot, H, d_k]
+ *                   ([t_tot, H] with KDA_DECAY_PER_HEAD; g_out is then that decay repeated over d_k)
  *   beta_logit      [t_tot, H] in_dtype
  *   conv_weight     [C, 4] fp32
  *   conv_state_in   [slots, 3, C] in_dtype, read;  conv_state_out  same shape, written
