@@ -128,7 +128,10 @@ typedef struct kda_log {
  *   gate_mode       kda_gate;  lower_bound used in safe mode only (finite, < 0)
  *   outputs (fp32): q_hat, k_hat [t_tot,H,d_k]; v_out [t_tot,H,d_v]; g_out (log decay)
  *                   [t_tot,H,d_k]; beta_out [t_tot,H]
- * The outputs are what kda_prefill_varlen consumes. */
+ * The outputs are what kda_prefill_varlen consumes.  q_raw, k_raw, v_raw, g_raw
+ * and the four wide outputs move with 16-byte accesses and must be 16-byte
+ * aligned (else KDA_E_ALIGN); beta_logit, beta_out and the conv state need only
+ * element alignment. */
 int kda_prep(const kda_dims* d, int32_t num_seqs, int64_t t_tot, const int32_t* cu_seqlens, const int32_t* slots,
              const void* q_raw, const void* k_raw, const void* v_raw, const float* conv_weight,
              const void* conv_state_in, void* conv_state_out, const void* g_raw, const void* beta_logit,

@@ -118,8 +118,10 @@ int kda_prep(const kda_dims* d, int32_t num_seqs, int64_t t_tot, const int32_t* 
     KDA_TRY(check_ptrs("kda_prep: conv state", {conv_state_in, conv_state_out}, eb));
   }
   if (t_tot > 0) {
-    KDA_TRY(check_ptrs("kda_prep: rows", {q_raw, k_raw, v_raw, g_raw, beta_logit}, eb));
-    KDA_TRY(check_ptrs("kda_prep: outputs", {q_hat, k_hat, v_out, g_out, beta_out}, 4));
+    KDA_TRY(check_ptrs("kda_prep: q/k/v/g rows", {q_raw, k_raw, v_raw, g_raw}));
+    KDA_TRY(check_ptrs("kda_prep: beta logits", {beta_logit}, eb));
+    KDA_TRY(check_ptrs("kda_prep: outputs", {q_hat, k_hat, v_out, g_out}));
+    KDA_TRY(check_ptrs("kda_prep: beta out", {beta_out}, 4));
   }
   kda::PrepLaunch L{d->num_heads, d->head_dim_k, d->head_dim_v, d->in_dtype, d->conv_act, gate_mode, num_seqs, t_tot,
                     lower_bound, cu_seqlens, slots, q_raw, k_raw, v_raw, g_raw, beta_logit, conv_weight,

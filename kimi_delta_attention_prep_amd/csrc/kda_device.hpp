@@ -20,6 +20,26 @@ constexpr float kL2Eps = 1e-6f;  // inside the square root of the q/k L2 norms
 constexpr int kConvW = 4;        // conv taps; tap 3 multiplies the current row
 constexpr int kChunk = 64;       // prompt rows per chunk
 
+// ---------------------------------------------------------------------------
+// Record slots, with no table: chunk i of sequence n lives in slot
+// base(n) + i, base(n) = floor(cu[n] / 64) + n.  From one sequence to the next
+// base grows by floor(cu[n+1] / 64) - floor(cu[n] / 64) + 1 >= ceil(len_n / 64),
+// so no two chunks share a slot, and the last slot is below T / 64 + num_seqs.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int64_t slot_base(const int32_t* cu, int n) { return cu[n] / kChunk + n; }
+
+// the sequence whose slots include slot c: the largest n < num_seqs with base(n) <= c
+__device__ __forceinline__ int slot_seq(const int32_t* cu, int num_seqs, int64_t c) {
+  int lo = 0, hi = num_seqs;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (slot_base(cu, mid) <= c) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+inline int64_t max_chunks(int num_seqs, int64_t t_tot) { return t_tot / kChunk + num_seqs; }
+
 // raw rows arrive as fp32 or as bf16 bit patterns (uint16_t); widening is exact
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(uint16_t x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }

@@ -307,7 +307,6 @@ __host__ __device__ inline RecLayout rec_layout(int dk, int dv, int fb) {
   return r;
 }
 static inline int frag_bytes(int precision) { return precision == POL_FP16 ? 16 : 32; }
-static inline int64_t max_chunks(int num_seqs, int64_t t_tot) { return t_tot / kChunk + num_seqs; }
 // workspace: a 1 KiB sink that absorbs stores of rows past a sequence's end, then the records
 constexpr size_t kSinkBytes = 1024;
 
@@ -338,24 +337,6 @@ struct PrefillArgs {
   uint8_t* recs;       // [max_chunks][H][rec bytes]
   int64_t rec_bytes;
 };
-
-// ---------------------------------------------------------------------------
-// Record slots, with no table: chunk i of sequence n lives in slot
-// base(n) + i, base(n) = floor(cu[n] / 64) + n.  From one sequence to the next
-// base grows by floor(cu[n+1] / 64) - floor(cu[n] / 64) + 1 >= ceil(len_n / 64),
-// so no two chunks share a slot, and the last slot is below T / 64 + num_seqs.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ int64_t slot_base(const int32_t* cu, int n) { return cu[n] / kChunk + n; }
-
-// the sequence whose slots include slot c: the largest n < num_seqs with base(n) <= c
-__device__ __forceinline__ int slot_seq(const int32_t* cu, int num_seqs, int64_t c) {
-  int lo = 0, hi = num_seqs;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (slot_base(cu, mid) <= c) lo = mid; else hi = mid;
-  }
-  return lo;
-}
 
 // ---------------------------------------------------------------------------
 // intra-chunk kernel

@@ -7,10 +7,10 @@
 //         come from its carried conv state), then SiLU;
 //   q_hat = c_q / sqrt(|c_q|^2 + 1e-6), k_hat likewise, v = c_v;
 //   g = -softplus(x_g) or lb * sigmoid(x_g);  beta = sigmoid(x_b).
-// One wavefront per (row, head); each lane owns d/64 consecutive channels of q,
-// k, g and v, so every load and store is coalesced.  The carried conv state is
-// written by a second launch after every read of the old one, which lets the
-// caller pass the same buffer for input and output.
+// One workgroup per (64-row tile of a sequence, head, stream), its rows staged
+// in LDS with 16-byte loads; each lane owns d/64 consecutive channels of a row.
+// The carried conv state is written by a second launch after every read of the
+// old one, which lets the caller pass the same buffer for input and output.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -30,57 +30,121 @@ struct PrepArgs {
   int g_per_head;  // raw g rows [T, H]: one decay per head and row, broadcast over d_k
 };
 
-// sequence n such that cu[n] <= row < cu[n+1] (cu non-decreasing; zero-length
-// sequences are skipped by taking the last n with cu[n] <= row)
-__device__ __forceinline__ int find_seq(const int32_t* cu, int num_seqs, int64_t row) {
-  int lo = 0, hi = num_seqs;  // invariant: cu[lo] <= row < cu[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if ((int64_t)cu[mid] <= row) lo = mid; else hi = mid;
+// 8 consecutive raw values (16 or 32 bytes, aligned) as fp32
+__device__ __forceinline__ void load8_raw(const float* src, float (&x)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(src), b = *reinterpret_cast<const float4*>(src + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+__device__ __forceinline__ void load8_raw(const uint16_t* src, float (&x)[8]) {
+  const uint4 v = *reinterpret_cast<const uint4*>(src);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
   }
-  return lo;
 }
 
+// The conv of one stream (q, k or v: D channels per head) over one 64-row tile:
+// the tile's rows and the 3 rows before it are staged in LDS with 16-byte loads
+// (rows before the sequence's first row come from its carried conv state), then
+// each wavefront convolves 16 consecutive rows side by side from there and writes
+// a lane's D/64 channels of each row.  conv_rows computes each row on its own
+// whatever the number of rows, so the bits are those of the fused prompt kernel.
+template <int D, bool NORM, typename RawT>
+__device__ __forceinline__ void prep_stream(const PrepArgs<RawT>& p, RawT* st, const RawT* src, const RawT* cs,
+                                            int64_t C, int64_t ch0, float* dst, int h, int64_t t0, int64_t end,
+                                            int64_t start, int len) {
+  constexpr int L = kChunk, NT = 256, RW = L / (NT / 64);  // 16 rows per wavefront
+  constexpr int VE = 16 / sizeof(RawT);                   // raw elements per 16-byte piece
+  constexpr int PR = D / VE, NP = (L + 3) * PR;           // pieces per row, per staged tile
+  constexpr int NI = (NP + NT - 1) / NT;                  // ... per thread
+  constexpr int E = D / 64;                               // channels per lane
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, H = p.H;
+  const int64_t width = (int64_t)H * D, col0 = (int64_t)h * D;
+  // Loads are unconditional (clamped into the sequence) so that no branch makes a
+  // wait count fewer loads; rows before the sequence start are overwritten below.
+  uint4 x[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int idx = min(t + i * NT, NP - 1), sr = idx / PR;
+    int64_t pos = start - 3 + sr;
+    pos = pos < t0 ? t0 : (pos >= end ? end - 1 : pos);
+    x[i] = *reinterpret_cast<const uint4*>(src + pos * width + col0 + (idx % PR) * VE);
+  }
+  const ConvW<D> wt = load_conv_w<D>(p.conv_w + ch0 * 4);
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+    if (t + i * NT < NP) *reinterpret_cast<uint4*>(st + (t + i * NT) * VE) = x[i];
+  if (start == t0) {  // the sequence's first tile (uniform over the workgroup): the 3 carried rows
+    for (int idx = t; idx < 3 * PR; idx += NT) {
+      const int sr = idx / PR, c0 = (idx % PR) * VE;
+      const RawT* cr = cs + sr * C + ch0 + c0;  // the conv state is not 16-byte aligned per channel
+#pragma unroll
+      for (int e = 0; e < VE; ++e) st[idx * VE + e] = cr[e];
+    }
+  }
+  __syncthreads();
+  const int r0 = RW * wave;
+  float y[RW][E];
+  conv_rows<D, NORM, RW>([&](int rr, int j, int d) { return to_f32(st[(r0 + rr + j) * D + d]); }, wt, p.act, y);
+#pragma unroll
+  for (int rr = 0; rr < RW; ++rr) {
+    if (r0 + rr >= len) break;
+    float* o = dst + ((start + r0 + rr) * H + h) * D + E * lane;
+    if constexpr (E == 2) *reinterpret_cast<float2*>(o) = make_float2(y[rr][0], y[rr][1]);
+    else o[0] = y[rr][0];
+  }
+}
+
+// One workgroup (4 wavefronts) per (64-row tile of a sequence, head, stream),
+// the tiles anchored at each sequence's first row as the prompt kernels' chunks
+// are.  blockIdx.z picks the stream: 0 q, 1 k, 2 v (a staged conv each), 3 the
+// decay and beta (no conv: rows to outputs, 8 values per lane).  Splitting the
+// streams keeps each workgroup's LDS small, so several run per CU and one's
+// loads overlap another's stores.
 template <int DK, int DV, typename RawT>
-__global__ __launch_bounds__(256) void prep_kernel(PrepArgs<RawT> p) {
-  constexpr int EK = DK / 64, EV = DV / 64;  // channels per lane
-  const int lane = threadIdx.x & 63;
-  const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int H = p.H;
-  if (pair >= p.t_tot * H) return;
-  const int64_t row = pair / H;
-  const int h = (int)(pair - row * H);
-  const int n = find_seq(p.cu, p.num_seqs, row);
+__global__ __launch_bounds__(256) void prep_tile_kernel(PrepArgs<RawT> p) {
+  constexpr int L = kChunk, NT = 256;
+  extern __shared__ __align__(16) unsigned char prep_smem[];
+  RawT* st = reinterpret_cast<RawT*>(prep_smem);  // [67][D] staged rows of the workgroup's stream
+  const int t = threadIdx.x;
+  const int c = blockIdx.x, h = blockIdx.y, z = blockIdx.z, H = p.H;
+  const int n = slot_seq(p.cu, p.num_seqs, c);
+  const int64_t t0 = p.cu[n], end = p.cu[n + 1];
+  const int64_t start = t0 + (c - slot_base(p.cu, n)) * L;
+  if (start >= end) return;  // a tile past the sequence's last row
   const int slot = p.slots ? p.slots[n] : n;
   if (slot < 0) return;
-  const int64_t t0 = p.cu[n];
-  const int64_t rel = row - t0;
-  const int64_t C = (int64_t)H * (2 * DK + DV);
+  const int len = (int)min((int64_t)L, end - start);
+  const int64_t C = (int64_t)H * (2 * DK + DV), wk = (int64_t)H * DK;
   const RawT* cs = p.cs_in + (int64_t)slot * 3 * C;
-  const int64_t wk = (int64_t)H * DK, wv = (int64_t)H * DV;
-  // tap j of a channel: packed row t0+rel-3+j, or the carried conv state before the sequence start
-  auto tap_of = [&](const RawT* src, int64_t width, int64_t col0, int64_t ch0) {
-    return [=](int, int j, int d) {
-      const int64_t pos = rel - 3 + j;
-      return pos >= 0 ? to_f32(src[(t0 + pos) * width + col0 + d]) : to_f32(cs[(3 + pos) * C + ch0 + d]);
-    };
-  };
-  float q[1][EK], k[1][EK], v[1][EV];
-  conv_rows<DK, true, 1>(tap_of(p.q, wk, (int64_t)h * DK, (int64_t)h * DK), p.conv_w + (int64_t)h * DK * 4, p.act, q);
-  conv_rows<DK, true, 1>(tap_of(p.k, wk, (int64_t)h * DK, wk + (int64_t)h * DK),
-                         p.conv_w + (wk + (int64_t)h * DK) * 4, p.act, k);
-  conv_rows<DV, false, 1>(tap_of(p.v, wv, (int64_t)h * DV, 2 * wk + (int64_t)h * DV),
-                          p.conv_w + (2 * wk + (int64_t)h * DV) * 4, p.act, v);
-  const int64_t ok = pair * DK + EK * lane, ov = pair * DV + EV * lane;
+  if (z == 0) {
+    prep_stream<DK, true>(p, st, p.q, cs, C, (int64_t)h * DK, p.q_hat, h, t0, end, start, len);
+  } else if (z == 1) {
+    prep_stream<DK, true>(p, st, p.k, cs, C, wk + (int64_t)h * DK, p.k_hat, h, t0, end, start, len);
+  } else if (z == 2) {
+    prep_stream<DV, false>(p, st, p.v, cs, C, 2 * wk + (int64_t)h * DV, p.v_out, h, t0, end, start, len);
+  } else {
+    for (int idx = t; idx < L * (DK / 8); idx += NT) {
+      const int r = idx / (DK / 8), c8 = 8 * (idx % (DK / 8));
+      if (r >= len) break;  // rows ascend with idx
+      const int64_t pr = (start + r) * H + h;
+      float gv[8];
+      if (p.g_per_head) {
+        const float gh = log_decay(to_f32(p.g[pr]), p.gate_mode, p.lb);
 #pragma unroll
-  for (int e = 0; e < EK; ++e) {
-    p.q_hat[ok + e] = q[0][e];
-    p.k_hat[ok + e] = k[0][e];
-    p.g_out[ok + e] = log_decay(to_f32(p.g[p.g_per_head ? pair : ok + e]), p.gate_mode, p.lb);
+        for (int e = 0; e < 8; ++e) gv[e] = gh;
+      } else {
+        load8_raw(p.g + pr * DK + c8, gv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gv[e] = log_decay(gv[e], p.gate_mode, p.lb);
+      }
+      *reinterpret_cast<float4*>(p.g_out + pr * DK + c8) = make_float4(gv[0], gv[1], gv[2], gv[3]);
+      *reinterpret_cast<float4*>(p.g_out + pr * DK + c8 + 4) = make_float4(gv[4], gv[5], gv[6], gv[7]);
+    }
+    if (t < len) p.beta_out[(start + t) * H + h] = sigmoid(to_f32(p.beta[(start + t) * H + h]));
   }
-#pragma unroll
-  for (int e = 0; e < EV; ++e) p.v_out[ov + e] = v[0][e];
-  if (lane == 0) p.beta_out[pair] = sigmoid(to_f32(p.beta[pair]));
 }
 
 // conv_state_out[slot][r][c] = source row (len - 3 + r) of channel c, reaching
@@ -124,9 +188,17 @@ static hipError_t launch_prep_t(const PrepLaunch& L, hipStream_t s) {
   p.g_per_head = L.g_per_head;
   p.cs_in = static_cast<const RawT*>(L.cs_in); p.cs_out = static_cast<RawT*>(L.cs_out);
   p.q_hat = L.q_hat; p.k_hat = L.k_hat; p.v_out = L.v_out; p.g_out = L.g_out; p.beta_out = L.beta_out;
-  const int64_t waves = L.t_tot * L.H;
-  if (waves > 0) {
-    hipLaunchKernelGGL((prep_kernel<DK, DV, RawT>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, p);
+  const int64_t mc = max_chunks(L.num_seqs, L.t_tot);
+  if (L.t_tot > 0 && L.num_seqs > 0) {
+    constexpr size_t lds = (size_t)(kChunk + 3) * (DK > DV ? DK : DV) * sizeof(RawT);
+    static bool attr_set = false;
+    if (!attr_set) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_tile_kernel<DK, DV, RawT>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+    hipLaunchKernelGGL((prep_tile_kernel<DK, DV, RawT>), dim3((unsigned)mc, (unsigned)L.H, 4), dim3(256), lds, s, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

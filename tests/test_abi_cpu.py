@@ -109,6 +109,7 @@ def test_prep_and_prefill_checks(lib):
     assert prep(-1, 10, A) == K.KDA_E_ARG
     assert prep(0, 10, A) == K.KDA_E_ARG
     assert prep(2, 10, MIS) == K.KDA_E_ALIGN
+    assert prep(2, 10, MIS4) == K.KDA_E_ALIGN  # raw rows are read 16 bytes at a time
     need = lib.kda_prefill_workspace_bytes(ctypes.byref(d), 2, 1000)
     assert need > 0
     pf = lambda ws, nb: lib.kda_prefill_varlen(ctypes.byref(d), 2, 1000, A, None, A, A, A, A, A, None, None, A, A,
