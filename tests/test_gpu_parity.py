@@ -60,6 +60,45 @@ def test_prep_parity_and_conv_state_bytes(dtype, dk, dv, gate):
     assert np.array_equal(p["conv_state"].cpu().double().numpy(), ref.conv_state)
 
 
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float32, 64)])
+def test_prep_tile_edges_with_slots(dtype, d):
+    """The preamble's 64-row tiles at their edges: sequences shorter than the
+    three conv rows, tiles ending one row before, at and after 64, an empty
+    sequence, and a slot map that permutes the conv-state pool and skips one
+    sequence (whose rows and pool row stay untouched)."""
+    lens = [1, 2, 3, 63, 64, 65, 0, 67, 129, 4]
+    w = I.generate("prep_edges", lengths=lens, H=3, dk=d, dv=d, dtype=dtype, gate_mode=I.GATE_SAFE,
+                   state_std=0.02, conv_state_std=1.0, seed=11)
+    N, T, H = w.N, w.T, w.H
+    slots = [5, 0, 9, 2, 7, 1, 3, -1, 8, 4]  # sequence 7 (67 rows) is skipped
+    S = 10
+    dm = dims_for(w)
+    wd = w.to("cuda")
+    pool = torch.randn(S, 3, dm.conv_channels, generator=torch.Generator().manual_seed(2)).to(dtype).cuda()
+    for n, s_ in enumerate(slots):
+        if s_ >= 0:
+            pool[s_] = wd.conv_state0[n]
+    pool_in = pool.clone()
+    nan = lambda *sh: torch.full(sh, float("nan"), device="cuda")
+    out = dict(q_hat=nan(T, H, d), k_hat=nan(T, H, d), v=nan(T, H, d), g=nan(T, H, d), beta=nan(T, H))
+    K.kda_prep(dm, wd.cu_seqlens, wd.q, wd.k, wd.v, wd.conv_w, pool, pool, wd.g, wd.beta, w.gate_mode, w.lower_bound,
+               out["q_hat"], out["k_hat"], out["v"], out["g"], out["beta"],
+               slots=torch.tensor(slots, dtype=torch.int32, device="cuda"))
+    ref = O.prep(w.f64("q"), w.f64("k"), w.f64("v"), w.f64("conv_w"), w.f64("conv_state0"), w.f64("g"),
+                 w.f64("beta"), w.cu_seqlens.numpy(), gate_mode=w.gate_mode, lower_bound=w.lower_bound)
+    cu = w.cu_seqlens.tolist()
+    live = np.ones(T, dtype=bool)
+    live[cu[7]:cu[8]] = False
+    for name, r in (("q_hat", ref.q_hat), ("k_hat", ref.k_hat), ("v", ref.v), ("g", ref.g), ("beta", ref.beta)):
+        got = out[name].cpu()
+        assert torch.isnan(got[~torch.from_numpy(live)]).all(), name  # the skipped sequence's rows untouched
+        assert rel(got[torch.from_numpy(live)], r[live]) < 2e-6, name
+    for n, s_ in enumerate(slots):
+        if s_ >= 0:  # the carried conv state is a bit copy of raw rows, in the sequence's pool row
+            assert np.array_equal(pool[s_].cpu().double().numpy(), ref.conv_state[n]), n
+    assert torch.equal(pool[6], pool_in[6])  # a pool row no sequence maps to
+
+
 # ---------------------------------------------------------------------------
 # decode and verify windows
 # ---------------------------------------------------------------------------
