@@ -90,10 +90,11 @@ __device__ __forceinline__ void prep_stream(const PrepArgs<RawT>& p, RawT* st, c
   conv_rows<D, NORM, RW>([&](int rr, int j, int d) { return to_f32(st[(r0 + rr + j) * D + d]); }, wt, p.act, y);
 #pragma unroll
   for (int rr = 0; rr < RW; ++rr) {
-    if (r0 + rr >= len) break;
-    float* o = dst + ((start + r0 + rr) * H + h) * D + E * lane;
-    if constexpr (E == 2) *reinterpret_cast<float2*>(o) = make_float2(y[rr][0], y[rr][1]);
-    else o[0] = y[rr][0];
+    if (r0 + rr < len) {
+      float* o = dst + ((start + r0 + rr) * H + h) * D + E * lane;
+      if constexpr (E == 2) *reinterpret_cast<float2*>(o) = make_float2(y[rr][0], y[rr][1]);
+      else o[0] = y[rr][0];
+    }
   }
 }
 
