@@ -33,6 +33,8 @@ MUTANTS = [
      "double acc = S[d * dv + j];"),
     ("chunk_cumsum_dropped", "run += c->g[((c0 + r) * H + h) * dk + d];", "run = c->g[((c0 + r) * H + h) * dk + d];"),
     ("chunk_P_strict", "P[r * C + i] = (i <= r) ? sp : 0.0;", "P[r * C + i] = (i < r) ? sp : 0.0;"),
+    ("log_decay_is_g", "memcpy(c->log_a + (row * H + h) * dk, a,", "memcpy(c->log_a + (row * H + h) * dk, gt,"),
+    ("log_update_is_v", "memcpy(c->log_u + (row * H + h) * dv, u,", "memcpy(c->log_u + (row * H + h) * dv, vt,"),
     ("rms_sum_not_mean", "sqrt(ss / dv + eps)", "sqrt(ss + eps)"),
     ("out_gate_sign", "sigmoid(z[r * dv + j])", "sigmoid(-z[r * dv + j])"),
 ]

@@ -192,6 +192,34 @@ def test_p7_brute_force_products(oracle_mod, dk, dv, T):
             np.testing.assert_allclose(r.state[n, h], S_ref, rtol=1e-12, atol=1e-13)
 
 
+def test_p13_verify_log_against_products(oracle_mod):
+    """The per-row log a verify window keeps (decay a_t = e^{g_t}, key k_t, update u_t)
+    against the brute-force products: the state after each prefix of rows, S_t, is
+    built from the transition matrices, and since the step is S_t = Diag(a_t) S_{t-1}
+    + k_t u_t^T, the update is recovered as (S_t - Diag(a_t) S_{t-1})^T k_t / |k_t|^2.
+    Replaying the logged rows from the initial state then gives the final state."""
+    rng = np.random.default_rng(13)
+    lens = [5, 0, 6]
+    H, dk, dv = 2, 3, 2
+    cu, q, k, v, g, b, S0 = _rand_core(rng, lens, H, dk, dv, unit_keys=False)
+    r = O.recurrent(q, k, v, g, b, S0, cu, with_log=True)
+    np.testing.assert_allclose(r.log_a, np.exp(g), rtol=1e-15, atol=0)
+    assert np.array_equal(r.log_k, k)
+    for n in range(len(lens)):
+        for h in range(H):
+            S_prev, S_rep = S0[n, h], S0[n, h].copy()
+            for t in range(cu[n], cu[n + 1]):
+                sl = slice(cu[n], t + 1)
+                _, S_t = brute.states_by_products(q[sl, h], k[sl, h], v[sl, h], np.exp(g[sl, h]), b[sl, h],
+                                                  S0[n, h])
+                a_t, k_t = np.exp(g[t, h]), k[t, h]
+                u_ref = (S_t - a_t[:, None] * S_prev).T @ k_t / (k_t @ k_t)
+                np.testing.assert_allclose(r.log_u[t, h], u_ref, rtol=1e-10, atol=1e-12)
+                S_rep = r.log_a[t, h][:, None] * S_rep + np.outer(r.log_k[t, h], r.log_u[t, h])
+                S_prev = S_t
+            np.testing.assert_allclose(S_rep, r.state[n, h], rtol=1e-12, atol=1e-13)
+
+
 def test_p8_scalar_state_closed_form(oracle_mod):
     """d_k = d_v = 1: S_t = (1 - b k^2) a S_{t-1} + b k v, o_t = S_t q (keys not unit)."""
     rng = np.random.default_rng(8)
