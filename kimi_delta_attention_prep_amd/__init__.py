@@ -126,6 +126,59 @@ def _need(t, name, dtype=None, shape=None):
     return t
 
 
+# Debug mode: the device-side contents the library takes as preconditions
+# (cu_seqlens, slot maps, commit counts, window lengths) are copied to the host
+# and checked before the call.  Each check synchronises with the device, so it
+# is off by default; KDA_DEBUG=1 in the environment or set_debug(True) turns it on.
+_debug = os.environ.get("KDA_DEBUG", "0") not in ("", "0")
+
+
+def set_debug(on: bool) -> None:
+    global _debug
+    _debug = bool(on)
+
+
+def _host_ints(t) -> list:
+    return [int(x) for x in t.detach().to("cpu", torch.int64).tolist()]
+
+
+def _debug_cu(cu_seqlens, t_tot: int) -> None:
+    """cu_seqlens[0] = 0, non-decreasing, cu_seqlens[N] = t_tot."""
+    cu = _host_ints(cu_seqlens)
+    if not cu or cu[0] != 0 or cu[-1] != t_tot:
+        raise ValueError(f"cu_seqlens must start at 0 and end at {t_tot} (the row count), got {cu[:1]}..{cu[-1:]}")
+    bad = next((n for n in range(len(cu) - 1) if cu[n + 1] < cu[n]), None)
+    if bad is not None:
+        raise ValueError(f"cu_seqlens decreases at sequence {bad}: {cu[bad]} -> {cu[bad + 1]}")
+
+
+def _debug_slots(slots, pools) -> None:
+    """Every slot below each pool size (negative = skipped); no two sequences share a slot."""
+    sl = _host_ints(slots)
+    for name, size in pools:
+        over = [x for x in sl if x >= size]
+        if over:
+            raise ValueError(f"slot {over[0]} is outside the {name} pool of {size} slots")
+    live = [x for x in sl if x >= 0]
+    if len(set(live)) != len(live):
+        raise ValueError("two sequences map to the same slot (their state updates would race)")
+
+
+def _debug_range(t, name: str, lo: int, hi: int) -> None:
+    v = _host_ints(t)
+    bad = next((x for x in v if x < lo or x > hi), None)
+    if bad is not None:
+        raise ValueError(f"{name} holds {bad}, outside [{lo}, {hi}]")
+
+
+def _need_pool(n: int, slots, pools) -> None:
+    """Without a slot map, sequence i uses slot i: every pool needs n slots (shapes only, always checked)."""
+    if slots is None:
+        for name, size in pools:
+            if size < n:
+                raise ValueError(f"{name} has {size} slots for {n} sequences and no slot map")
+
+
 @dataclass(frozen=True)
 class Dims:
     num_heads: int
@@ -170,6 +223,12 @@ def kda_prep(d: Dims, cu_seqlens, q_raw, k_raw, v_raw, conv_weight, conv_state_i
         _need(t, name, torch.float32, shp)
     if slots is not None:
         _need(slots, "slots", torch.int32, (N,))
+    pools = (("conv_state", conv_state_in.shape[0]),)
+    _need_pool(N, slots, pools)
+    if _debug:
+        _debug_cu(cu_seqlens, T)
+        if slots is not None:
+            _debug_slots(slots, pools)
     dims = d.c()
     _check(lib.kda_prep(ctypes.byref(dims), N, T, _ptr(cu_seqlens), _ptr(slots), _ptr(q_raw), _ptr(k_raw),
                         _ptr(v_raw), _ptr(conv_weight), _ptr(conv_state_in), _ptr(conv_state_out), _ptr(g_raw),
@@ -223,6 +282,12 @@ def kda_prefill_varlen(d: Dims, cu_seqlens, q_hat, k_hat, v, g, beta, state, o, 
     _need(workspace, "workspace")
     if slots is not None:
         _need(slots, "slots", torch.int32, (N,))
+    pools = (("state", state.shape[0]),) + ((("conv_state", raw["conv_state_in"].shape[0]),) if raw else ())
+    _need_pool(N, slots, pools)
+    if _debug:
+        _debug_cu(cu_seqlens, T)
+        if slots is not None:
+            _debug_slots(slots, pools)
     dims = d.c()
     _check(lib.kda_prefill_varlen(ctypes.byref(dims), N, T, _ptr(cu_seqlens), _ptr(slots), _ptr(q_hat), _ptr(k_hat),
                                   _ptr(v), _ptr(g), _ptr(beta), ctypes.byref(rr) if rr is not None else None,
@@ -244,6 +309,10 @@ def kda_decode(d: Dims, state, conv_state, conv_weight, q_raw, k_raw, v_raw, g_r
     _need(o, "o", torch.float32, (B, H, dv))
     if slots is not None:
         _need(slots, "slots", torch.int32, (B,))
+    pools = (("state", state.shape[0]), ("conv_state", conv_state.shape[0]))
+    _need_pool(B, slots, pools)
+    if _debug and slots is not None:
+        _debug_slots(slots, pools)
     dims = d.c()
     _check(lib.kda_decode(ctypes.byref(dims), B, _ptr(slots), _ptr(state), _ptr(conv_state), _ptr(conv_weight),
                           _ptr(q_raw), _ptr(k_raw), _ptr(v_raw), _ptr(g_raw), _ptr(beta_logit), int(gate_mode),
@@ -299,6 +368,15 @@ def kda_verify_window(d: Dims, state, conv_state, conv_weight, n_commit, log_in,
     lout = log_out.c() if log_out is not None else None
     if window_lens is not None:
         _need(window_lens, "window_lens", torch.int32, (B,))
+    pools = (("state", state.shape[0]), ("conv_state", conv_state.shape[0]))
+    _need_pool(B, slots, pools)
+    if _debug:
+        if slots is not None:
+            _debug_slots(slots, pools)
+        if n_commit is not None:
+            _debug_range(n_commit, "n_commit", 0, log_in.window if log_in is not None else 0)
+        if window_lens is not None:
+            _debug_range(window_lens, "window_lens", 0, W)
     _check(lib.kda_verify_window(ctypes.byref(dims), B, W, _ptr(window_lens), _ptr(slots), _ptr(state),
                                  _ptr(conv_state),
                                  _ptr(conv_weight), _ptr(n_commit), ctypes.byref(lin) if lin else None,

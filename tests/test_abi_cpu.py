@@ -157,3 +157,31 @@ def test_timing_hook_checks(lib):
     assert lib.kda_set_timing_events(None, 2) == K.KDA_E_ARG
     assert lib.kda_set_timing_events(arr, 2) == K.KDA_OK
     assert lib.kda_set_timing_events(None, 0) == K.KDA_OK
+
+
+def test_debug_checks_of_device_contents():
+    """The debug-mode checks of what the library takes as preconditions, on host copies."""
+    import torch
+    i32 = lambda v: torch.tensor(v, dtype=torch.int32)
+    K._debug_cu(i32([0, 5, 5, 9]), 9)
+    for bad, t in (([1, 5, 9], 9), ([0, 5, 8], 9), ([0, 6, 5, 9], 9)):
+        with pytest.raises(ValueError):
+            K._debug_cu(i32(bad), t)
+    K._debug_slots(i32([3, -1, 0, 2]), (("state", 4),))
+    with pytest.raises(ValueError, match="outside"):
+        K._debug_slots(i32([3, 4]), (("state", 8), ("conv_state", 4)))
+    with pytest.raises(ValueError, match="same slot"):
+        K._debug_slots(i32([1, -1, 1]), (("state", 4),))
+    K._debug_range(i32([0, 4, 2]), "n_commit", 0, 4)
+    with pytest.raises(ValueError):
+        K._debug_range(i32([0, 5]), "n_commit", 0, 4)
+    with pytest.raises(ValueError):
+        K._debug_range(i32([-1]), "window_lens", 0, 4)
+
+
+def test_pool_size_without_slot_map():
+    """Without a slot map sequence i uses slot i: a pool smaller than the batch is refused (shapes only)."""
+    K._need_pool(3, None, (("state", 3), ("conv_state", 5)))
+    K._need_pool(3, object(), (("state", 1),))  # with a slot map only the device contents can tell
+    with pytest.raises(ValueError, match="no slot map"):
+        K._need_pool(4, None, (("state", 8), ("conv_state", 3)))
