@@ -164,6 +164,16 @@ __global__ __launch_bounds__(256) void conv_state_kernel(PrepArgs<RawT> p, int D
   const int64_t qk = (int64_t)p.H * DK;
   const RawT* in = p.cs_in + (int64_t)slot * 3 * C;
   RawT* out = p.cs_out + (int64_t)slot * 3 * C;
+  if (len >= 3) {  // (uniform over the workgroup) every row comes from the packed rows: three loads, then the stores
+    const RawT* src = c < qk ? p.q + c : (c < 2 * qk ? p.k + (c - qk) : p.v + (c - 2 * qk));
+    const int64_t width = c < 2 * qk ? qk : (int64_t)p.H * DV;
+    RawT x[3];
+#pragma unroll
+    for (int r = 0; r < 3; ++r) x[r] = src[(t0 + len - 3 + r) * width];
+#pragma unroll
+    for (int r = 0; r < 3; ++r) out[r * C + c] = x[r];
+    return;
+  }
   for (int r = 0; r < 3; ++r) {
     const int64_t pos = len - 3 + r;
     RawT x;
