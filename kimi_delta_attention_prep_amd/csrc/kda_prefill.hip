@@ -1191,6 +1191,18 @@ __device__ __forceinline__ void carry_rows(const PrefillArgs& p, int n, int slot
   const int64_t t0 = p.cu[n], len = (int64_t)p.cu[n + 1] - t0;
   const E* in = static_cast<const E*>(p.raw.cs_in) + (int64_t)slot * 3 * C;
   E* out = static_cast<E*>(p.raw.cs_out) + (int64_t)slot * 3 * C;
+  if (len >= 3) {  // (uniform over the sequence) every row comes from the packed rows: three loads, then the stores
+    const E* src = c < qk ? static_cast<const E*>(p.raw.q) + c
+                 : c < 2 * qk ? static_cast<const E*>(p.raw.k) + (c - qk)
+                              : static_cast<const E*>(p.raw.v) + (c - 2 * qk);
+    const int64_t width = c < 2 * qk ? qk : vw;
+    E x[3];
+#pragma unroll
+    for (int r = 0; r < 3; ++r) x[r] = src[(t0 + len - 3 + r) * width];
+#pragma unroll
+    for (int r = 0; r < 3; ++r) out[r * C + c] = x[r];
+    return;
+  }
   for (int r = 0; r < 3; ++r) {
     const int64_t pos = len - 3 + r;
     E x;
