@@ -374,6 +374,8 @@ def main():
     # ---------------- the scalar-decay layer on the same prompt workload ----------------
     if not args.no_extras:
         out["prefill_scalar_decay"] = scalar_decay_prefill(stream, w, prec, args.steps, args.warmup)
+        if not args.unfused:
+            out["prefill_two_call"] = two_call_prefill(stream, w, prec, args.steps, args.warmup)
 
     # ---------------- small-batch decode: eager calls against one graph replay ----------------
     if not args.no_decode and not args.no_extras:
@@ -426,6 +428,53 @@ def scalar_decay_prefill(stream, w, prec, steps, warmup):
     ms = e0.elapsed_time(e1) / steps
     return {"workload": f"prefill T={T} H={H} d={dk}, one decay per head and row (g rows [T, H])",
             "value": T / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms}
+
+
+def two_call_prefill(stream, w, prec, steps, warmup):
+    """The same prompt pass as two calls: kda_prep writes q_hat, k_hat, v, g and
+    beta in fp32, then kda_prefill_varlen (with the norm epilogue) reads them.
+    Reports the step and the preamble call on its own (HIP events)."""
+    import torch
+    import kimi_delta_attention_prep_amd as K
+    T, H, dk, dv = w.T, w.H, w.dk, w.dv
+    d = K.Dims(H, dk, dv, w.dtype, precision=prec)
+    wd = w.to("cuda")
+    f = lambda *s: torch.empty(*s, device="cuda", dtype=torch.float32)
+    qh, kh, vv, gg, bb = f(T, H, dk), f(T, H, dk), f(T, H, dv), f(T, H, dk), f(T, H)
+    state, cs = wd.state0.clone(), wd.conv_state0.clone()
+    o = f(T, H, dv)
+    y = torch.empty(T, H, dv, device="cuda", dtype=torch.bfloat16)
+    ws = torch.empty(K.kda_prefill_workspace_bytes(d, w.N, T), dtype=torch.uint8, device="cuda")
+    norm = dict(z=wd.z, weight=wd.norm_w, eps=1e-6, y=y)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+
+    def step(i=None):
+        if i is not None:
+            ev[2 * i].record(stream)
+        K.kda_prep(d, wd.cu_seqlens, wd.q, wd.k, wd.v, wd.conv_w, cs, cs, wd.g, wd.beta, w.gate_mode,
+                   w.lower_bound, qh, kh, vv, gg, bb)
+        if i is not None:
+            ev[2 * i + 1].record(stream)
+        K.kda_prefill_varlen(d, wd.cu_seqlens, qh, kh, vv, gg, bb, state, o, ws, norm=norm)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    prep_ms = sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps))[steps // 2]
+    prep_bytes = T * H * (w.q.element_size() * (3 * dk + dv + 1) + 4 * (3 * dk + dv + 1))
+    return {"workload": f"prefill T={T} H={H} d={dk} as kda_prep + kda_prefill_varlen (fp32 preamble outputs "
+                        "through HBM)", "value": T / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+            "kda_prep_ms": prep_ms, "kda_prep_GB_per_s": prep_bytes / (prep_ms * 1e-3) / 1e9}
 
 
 def verify_windows(stream, steps, warmup, B=64, W=4, H=32, d=128):
