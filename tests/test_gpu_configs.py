@@ -149,3 +149,14 @@ def test_verify_on_a_2048_row_prefilled_state():
     ref_o = ref.o.reshape(B, P + W, H, 128)
     assert rel(o_v, ref_o[:, P:]) < TOL_BF16
     assert rel(r["o"].reshape(B, P, H, 128), ref_o[:, :P]) < TOL_BF16
+
+
+def test_prefill_T4096_H16_fused_is_bitwise_the_two_call_path():
+    """At the benchmark's own size and policy, the fused prompt call (preamble inside the prompt
+    kernels) gives the bits of kda_prep followed by kda_prefill_varlen: o, final state, conv state."""
+    w = I.prefill()
+    a = gpu_layer_prefill(w, precision=K.PREC_FP16)
+    b = gpu_layer_prefill(w, precision=K.PREC_FP16, fused=True)
+    assert torch.equal(a["o"], b["o"])
+    assert torch.equal(a["state"], b["state"])
+    assert torch.equal(a["prep"]["conv_state"], b["prep"]["conv_state"])
