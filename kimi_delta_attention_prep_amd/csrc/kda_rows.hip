@@ -182,10 +182,14 @@ struct RowStep {
   }
 };
 
+constexpr int kRowsGridY = 65535;  // the largest y extent of a grid
+
 template <int DK, int DV, typename RawT, bool VERIFY>
 __global__ __launch_bounds__(256) void kda_rows_kernel(RowsArgs<RawT> p) {
   using SH = RowsShape<DK, DV>;
-  const int h = blockIdx.x, b = blockIdx.y;
+  // batches above the 65535 limit of a grid's y extent continue in z
+  const int h = blockIdx.x, b = (int)(blockIdx.z * kRowsGridY + blockIdx.y);
+  if (b >= p.batch) return;
   const int t = threadIdx.x;
   const int slot = p.slots ? p.slots[b] : b;
   if (slot < 0) return;
@@ -316,7 +320,8 @@ static hipError_t launch_rows_t(const RowsLaunch& L, hipStream_t s) {
   p.n_commit = L.n_commit; p.wlen = L.window_lens; p.in_a = L.in_a; p.in_k = L.in_k; p.in_u = L.in_u;
   p.in_rows = static_cast<const RawT*>(L.in_rows); p.in_window = L.in_window;
   p.out_a = L.out_a; p.out_k = L.out_k; p.out_u = L.out_u; p.out_rows = static_cast<RawT*>(L.out_rows);
-  dim3 grid(L.H, L.batch);
+  const int gy = L.batch < kRowsGridY ? L.batch : kRowsGridY;
+  dim3 grid(L.H, gy, (L.batch + kRowsGridY - 1) / kRowsGridY);
   hipLaunchKernelGGL((kda_rows_kernel<DK, DV, RawT, VERIFY>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }

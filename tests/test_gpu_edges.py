@@ -92,3 +92,30 @@ def test_long_sequence_next_to_a_short_one():
     rb = gpu_layer_prefill(b, precision=K.PREC_FP16, fused=True)
     assert torch.equal(torch.cat([ra["o"], rb["o"]]), r["o"][:n_long])
     assert torch.equal(rb["state"][0], r["state"][0])
+
+
+def test_decode_batch_beyond_one_grid_row():
+    """A decode batch larger than a grid's y extent (65535): sampled sequences on both sides of the
+    boundary, decoded again alone through a slot map, give the same bits (o, state, conv state)."""
+    B, H, d = 65540, 1, 64
+    dm = K.Dims(H, d, d, torch.bfloat16)
+    g = torch.Generator(device="cuda").manual_seed(9)
+    rn = lambda *s: torch.randn(*s, generator=g, device="cuda")
+    state0 = rn(B, H, d, d) * 0.02
+    cs0 = rn(B, 3, dm.conv_channels).to(torch.bfloat16)
+    cw = rn(dm.conv_channels, 4) * 0.5
+    rows = [rn(B, H, d).to(torch.bfloat16) for _ in range(4)]
+    beta = rn(B, H).to(torch.bfloat16)
+    st, cs = state0.clone(), cs0.clone()
+    o = torch.empty(B, H, d, device="cuda")
+    K.kda_decode(dm, st, cs, cw, *rows, beta, I.GATE_SAFE, -5.0, o)
+    idx = torch.tensor([0, 65534, 65535, 65539], device="cuda")
+    st2, cs2 = state0.clone(), cs0.clone()
+    o2 = torch.empty(4, H, d, device="cuda")
+    K.kda_decode(dm, st2, cs2, cw, *[r[idx].contiguous() for r in rows], beta[idx].contiguous(), I.GATE_SAFE,
+                 -5.0, o2, slots=idx.to(torch.int32))
+    torch.cuda.synchronize()
+    assert torch.equal(o[idx], o2)
+    assert torch.equal(st[idx], st2[idx])
+    assert torch.equal(cs[idx], cs2[idx])
+    assert not torch.equal(st[65539], state0[65539])  # the last sequence was decoded
