@@ -77,6 +77,31 @@ def kernel_algorithmic(name, T, H, dk, dv, N=1, chunk=64, in_bytes=2, y_bytes=2)
     return 0.0, 0.0
 
 
+def pass_bytes_per_token_head(dk, dv, in_bytes=2, y_bytes=2):
+    """Algorithmic HBM bytes of one prompt pass per token-head: the raw q, k, g (d_k each) and v, z (d_v each)
+    rows and the beta logit in, y out (1538 B at d = 128 with bf16 rows and bf16 y)."""
+    return in_bytes * (3 * dk + 2 * dv) + in_bytes + y_bytes * dv
+
+
+def prompt_roofline(per_kernel, T, H, dk, dv, N, precision):
+    """Roofline entry of a prompt pass for its dominant kernel: the pass's algorithmic bytes (per token-head
+    figure x T*H) over that kernel's average launch duration, against the HBM peak (the pass is HBM-bound by
+    its arithmetic intensity).  The kernel's own share of the bytes and FLOPs is reported beside it."""
+    dom = max(per_kernel, key=per_kernel.get)
+    dom_ms = per_kernel[dom]
+    per_unit = pass_bytes_per_token_head(dk, dv)
+    units = T * H
+    achieved = per_unit * units / (dom_ms * 1e-3) / 1e9
+    kf, kb = kernel_algorithmic(dom, T, H, dk, dv, N=N)
+    return {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": committed_traffic(dom, precision),
+            "basis": "whole-pass algorithmic bytes per token-head x token-heads / dominant kernel launch",
+            "bytes_per_token_head": per_unit, "token_heads": units, "ms_per_launch": dom_ms,
+            "kernel_share": {"algorithmic_bytes": kb, "algorithmic_flops": kf,
+                             "GB_per_s": kb / (dom_ms * 1e-3) / 1e9,
+                             "hbm_frac": kb / (dom_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}}
+
+
 def source_digest():
     """Digest of the sources the prompt and decode kernels are built from."""
     import hashlib
@@ -202,6 +227,9 @@ def main():
     ap.add_argument("--unfused", action="store_true", help="run kda_prep separately instead of inside the prompt pass")
     ap.add_argument("--precision", choices=("fp16", "bf16x3", "fp32"), default="fp16",
                     help="arithmetic of the prompt path's matrix products (see kda_precision)")
+    ap.add_argument("--workload", choices=("prefill", "varlen"), default="prefill",
+                    help="the timed prompt workload: T=4096 H=16 (the metric's), or the 8 packed sequences at H=32 "
+                         "(for profiler runs of that workload's kernels)")
     ap.add_argument("--copy-calibration", action="store_true", help="also run a plain 1 GiB device copy")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--pmc-command", default="", help="the counter command, stored in the summary")
@@ -226,41 +254,6 @@ def main():
     dev = "cuda"
     stream = torch.cuda.current_stream()
 
-    # ---------------- prompt workload ----------------
-    w = I.prefill()
-    T, H, dk, dv = w.T, w.H, w.dk, w.dv
-    prec = {"fp16": K.PREC_FP16, "bf16x3": K.PREC_BF16X3, "fp32": K.PREC_FP32}[args.precision]
-    d = K.Dims(H, dk, dv, w.dtype, precision=prec)
-    wd = w.to(dev)
-    f = lambda *s: torch.empty(*s, device=dev, dtype=torch.float32)
-    qh, kh, vv, gg, bb = f(T, H, dk), f(T, H, dk), f(T, H, dv), f(T, H, dk), f(T, H)
-    state = wd.state0.clone()
-    cs = wd.conv_state0.clone()
-    o = f(T, H, dv)
-    y = torch.empty(T, H, dv, device=dev, dtype=torch.bfloat16)
-    ws = torch.empty(K.kda_prefill_workspace_bytes(d, w.N, T), dtype=torch.uint8, device=dev)
-    raw = dict(q_raw=wd.q, k_raw=wd.k, v_raw=wd.v, g_raw=wd.g, beta_logit=wd.beta, conv_weight=wd.conv_w,
-               conv_state_in=cs, conv_state_out=cs, gate_mode=w.gate_mode, lower_bound=w.lower_bound)
-    norm = dict(z=wd.z, weight=wd.norm_w, eps=1e-6, y=y)
-    names = ("kda_prep", "kda_prefill_varlen") if args.unfused else ("kda_prefill_varlen",)
-
-    def step(ev=None):
-        i = 0
-        if ev is not None:
-            ev[i].record(stream)
-        if args.unfused:
-            K.kda_prep(d, wd.cu_seqlens, wd.q, wd.k, wd.v, wd.conv_w, cs, cs, wd.g, wd.beta, w.gate_mode,
-                       w.lower_bound, qh, kh, vv, gg, bb)
-            i += 1
-            if ev is not None:
-                ev[i].record(stream)
-            K.kda_prefill_varlen(d, wd.cu_seqlens, qh, kh, vv, gg, bb, state, o, ws, norm=norm)
-        else:
-            K.kda_prefill_varlen(d, wd.cu_seqlens, None, None, None, None, None, state, o, ws, raw=raw, norm=norm)
-        i += 1
-        if ev is not None:
-            ev[i].record(stream)
-
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -269,67 +262,31 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    mk = lambda: torch.cuda.Event(enable_timing=True)
-    # 1) the timed region: exactly K steps, only a start and an end event
-    t_start, t_end = mk(), mk()
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for _ in range(args.steps):
-        step()
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms = t_start.elapsed_time(t_end) / args.steps
-    # 2) a second timed pass of K steps with events around every entry point and,
-    #    through the library's timing hook, around every kernel of the prompt call
-    #    (recording events between kernels adds gaps, so the throughput comes from 1)
-    evs = [[mk() for _ in range(len(names) + 1)] for _ in range(args.steps)]
-    kev = [[mk() for _ in range(2 * len(K.PREFILL_KERNELS))] for _ in range(args.steps)]
-    for e in (x for row in kev for x in row):
-        e.record(stream)  # creates the HIP events the hook records into
-    torch.cuda.synchronize()
-    for s in range(args.steps):
-        K.kda_set_timing_events(kev[s])
-        step(evs[s])
-    torch.cuda.synchronize()
-    K.kda_set_timing_events(None)
-    per_entry = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i, n in enumerate(names)}
-    per_kernel = {}
-    for i, n in enumerate(K.PREFILL_KERNELS):
-        per_kernel[n] = sum(e[2 * i].elapsed_time(e[2 * i + 1]) for e in kev) / args.steps
+    # ---------------- prompt workload ----------------
+    w = I.prefill() if args.workload == "prefill" else I.varlen()
+    T, H, dk, dv = w.T, w.H, w.dk, w.dv
+    prec = PRECISIONS[args.precision](K)
+    pp = time_prompt_pass(stream, w, prec, args.steps, args.warmup, unfused=args.unfused)
+    ms = pp["ms_per_step"]
     tokens_per_s = T / (ms * 1e-3)
-
     flops, bytes_ = prefill_algorithmic(T, H, dk, dv, y_bytes=2)
-    dom = max(per_kernel, key=per_kernel.get)
-    dom_ms = per_kernel[dom]
-    kf, kb = kernel_algorithmic(dom, T, H, dk, dv, N=w.N)
-    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    if kb > 0 and kf / kb < ridge:
-        roof = {"kernel": dom, "bound": "hbm", "achieved": kb / (dom_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s"}
-    else:
-        roof = {"kernel": dom, "bound": "mfma", "achieved": kf / (dom_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = committed_traffic(dom, args.precision)
-    roof["ms_per_launch"] = dom_ms
-    roof["algorithmic_bytes_per_launch"] = kb
-    roof["algorithmic_flops_per_launch"] = kf
+    roof = prompt_roofline(pp["kernels_ms"], T, H, dk, dv, w.N, args.precision)
     out = {
         "metric": "KDA tokens/s: prefill (T=4096,H=16) and decode (B=256); % MFMA/HBM peak",
         "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": {"fp16": "fp16", "bf16x3": "bf16", "fp32": "f32"}[args.precision],
+        "dtype": DTYPE_NAMES[args.precision],
         "data": "synthetic",
-        "config": {"workload": "prefill T=4096 H=16 d_k=d_v=128 bf16 rows, fp32 state, safe gate lb=-5, chunk 64",
+        "config": {"workload": ("prefill T=4096 H=16 d_k=d_v=128 bf16 rows, fp32 state, safe gate lb=-5, chunk 64"
+                                if args.workload == "prefill" else
+                                f"varlen {w.N} packed sequences, {T} rows, H={H} d_k=d_v=128 bf16 rows, fp32 state, "
+                                "softplus gate, chunk 64"),
                    "matrix_products": args.precision, "preamble": "separate" if args.unfused else "fused",
                    "output_norm": "epilogue",
-                   "global_batch": 1, "seq_len": T, "parallelism": "none"},
+                   "global_batch": w.N, "seq_len": T, "parallelism": "none"},
         "roofline": roof,
-        "entry_points_ms": per_entry,
-        "kernels_ms": per_kernel,
+        "entry_points_ms": pp["entry_points_ms"],
+        "kernels_ms": pp["kernels_ms"],
         "whole_pass": {"algorithmic_GB": bytes_ / 1e9, "algorithmic_GFLOP": flops / 1e9,
                        "GB_per_s": bytes_ / (ms * 1e-3) / 1e9, "hbm_frac": bytes_ / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                        "TFLOP_per_s": flops / (ms * 1e-3) / 1e12,
@@ -338,7 +295,6 @@ def main():
 
     # ---------------- decode workload ----------------
     if not args.no_decode:
-        del qh, kh, vv, gg, bb, o, y, ws
         wdec = I.decode(steps=args.decode_steps)
         B, Hd = wdec.N, wdec.H
         dd = K.Dims(Hd, wdec.dk, wdec.dv, wdec.dtype)
@@ -371,6 +327,16 @@ def main():
                                       "traffic": committed_traffic("kda_rows (decode)", args.precision)},
                          "algorithmic_bytes_per_step": dbytes}
 
+    # ---------------- the same pass under the other bf16-row policy; the varlen workload ----------------
+    if not args.no_extras:
+        other = "bf16x3" if args.precision != "bf16x3" else "fp16"
+        out[f"prefill_{other}"] = prompt_line(stream, w, other, args.steps, args.warmup, K)
+        if args.workload == "prefill":
+            wv = I.varlen()
+            out["prefill_varlen"] = prompt_line(stream, wv, args.precision, max(3, args.steps // 4),
+                                                max(1, args.warmup // 2), K)
+            del wv
+
     # ---------------- the scalar-decay layer on the same prompt workload ----------------
     if not args.no_extras:
         out["prefill_scalar_decay"] = scalar_decay_prefill(stream, w, prec, args.steps, args.warmup)
@@ -396,6 +362,92 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
+
+
+PRECISIONS = {"fp16": lambda K: K.PREC_FP16, "bf16x3": lambda K: K.PREC_BF16X3, "fp32": lambda K: K.PREC_FP32}
+DTYPE_NAMES = {"fp16": "fp16", "bf16x3": "bf16", "fp32": "f32"}
+
+
+def time_prompt_pass(stream, w, prec, steps, warmup, unfused=False):
+    """Times prompt passes over workload w (bf16 rows): each pass is one kda_prefill_varlen call with the
+    preamble fused and the norm epilogue to bf16 y (or kda_prep, then that call, when unfused), carrying state
+    and conv state from pass to pass.  W warmup passes, then exactly K passes between two events (the
+    throughput), then K more with events around every entry point and, through the library's timing hook,
+    around every kernel of the prompt call (recording events between kernels adds gaps, so the throughput
+    comes from the first K)."""
+    import torch
+    import kimi_delta_attention_prep_amd as K
+    T, H, dk, dv = w.T, w.H, w.dk, w.dv
+    d = K.Dims(H, dk, dv, w.dtype, precision=prec)
+    wd = w.to("cuda")
+    f = lambda *s: torch.empty(*s, device="cuda", dtype=torch.float32)
+    pre = (f(T, H, dk), f(T, H, dk), f(T, H, dv), f(T, H, dk), f(T, H)) if unfused else None
+    state = wd.state0.clone()
+    cs = wd.conv_state0.clone()
+    o = f(T, H, dv)
+    y = torch.empty(T, H, dv, device="cuda", dtype=torch.bfloat16)
+    ws = torch.empty(K.kda_prefill_workspace_bytes(d, w.N, T), dtype=torch.uint8, device="cuda")
+    raw = dict(q_raw=wd.q, k_raw=wd.k, v_raw=wd.v, g_raw=wd.g, beta_logit=wd.beta, conv_weight=wd.conv_w,
+               conv_state_in=cs, conv_state_out=cs, gate_mode=w.gate_mode, lower_bound=w.lower_bound)
+    norm = dict(z=wd.z, weight=wd.norm_w, eps=1e-6, y=y)
+    names = ("kda_prep", "kda_prefill_varlen") if unfused else ("kda_prefill_varlen",)
+
+    def step(ev=None):
+        i = 0
+        if ev is not None:
+            ev[i].record(stream)
+        if unfused:
+            K.kda_prep(d, wd.cu_seqlens, wd.q, wd.k, wd.v, wd.conv_w, cs, cs, wd.g, wd.beta, w.gate_mode,
+                       w.lower_bound, *pre)
+            i += 1
+            if ev is not None:
+                ev[i].record(stream)
+            K.kda_prefill_varlen(d, wd.cu_seqlens, *pre, state, o, ws, norm=norm)
+        else:
+            K.kda_prefill_varlen(d, wd.cu_seqlens, None, None, None, None, None, state, o, ws, raw=raw, norm=norm)
+        i += 1
+        if ev is not None:
+            ev[i].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    t_start, t_end = mk(), mk()
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for _ in range(steps):
+        step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_end) / steps
+    evs = [[mk() for _ in range(len(names) + 1)] for _ in range(steps)]
+    kev = [[mk() for _ in range(2 * len(K.PREFILL_KERNELS))] for _ in range(steps)]
+    for e in (x for row in kev for x in row):
+        e.record(stream)  # creates the HIP events the hook records into
+    torch.cuda.synchronize()
+    for i in range(steps):
+        K.kda_set_timing_events(kev[i])
+        step(evs[i])
+    torch.cuda.synchronize()
+    K.kda_set_timing_events(None)
+    per_entry = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / steps for i, n in enumerate(names)}
+    per_kernel = {n: sum(e[2 * i].elapsed_time(e[2 * i + 1]) for e in kev) / steps
+                  for i, n in enumerate(K.PREFILL_KERNELS)}
+    return {"ms_per_step": ms, "entry_points_ms": per_entry, "kernels_ms": per_kernel}
+
+
+def prompt_line(stream, w, precision, steps, warmup, K):
+    """One extra line: the fused prompt pass over workload w under `precision`, with its kernel times and
+    its roofline entry."""
+    T, H = w.T, w.H
+    pp = time_prompt_pass(stream, w, PRECISIONS[precision](K), steps, warmup)
+    lens = (w.cu_seqlens[1:] - w.cu_seqlens[:-1]).tolist()
+    return {"workload": f"{w.name}: {w.N} sequence(s), {T} rows (lengths {lens}), H={H}, d={w.dk}, bf16 rows, "
+                        f"{'softplus' if w.gate_mode == 0 else 'safe'} gate",
+            "matrix_products": precision, "value": T / (pp["ms_per_step"] * 1e-3), "unit": "tokens/s",
+            "ms_per_step": pp["ms_per_step"], "steps": steps, "kernels_ms": pp["kernels_ms"],
+            "roofline": prompt_roofline(pp["kernels_ms"], T, H, w.dk, w.dv, w.N, precision)}
 
 
 def scalar_decay_prefill(stream, w, prec, steps, warmup):

@@ -67,8 +67,9 @@ typedef struct ihipEvent_t* hipEvent_t;
 
 enum kda_status {
   KDA_OK = 0,
-  KDA_E_ARG = 1,       /* null pointer or negative size */
-  KDA_E_GEOMETRY = 2,  /* d_k or d_v not in {64, 128}, conv width != 4, unknown decay shape, window not in [0, 8] */
+  KDA_E_ARG = 1,       /* null pointer, negative size, or more rows than cu_seqlens (int32) or a launch grid addresses */
+  KDA_E_GEOMETRY = 2,  /* d_k or d_v not in {64, 128}, num_heads > 65535, conv width != 4, unknown decay shape,
+                          window not in [0, 8] */
   KDA_E_ALIGN = 3,     /* a pointer is not aligned as its access needs (see Alignment) */
   KDA_E_GATE = 4,      /* unknown gate mode, or safe mode with a lower bound that is not finite and < 0 */
   KDA_E_DTYPE = 5,     /* unknown dtype, activation or precision policy */
@@ -89,14 +90,21 @@ enum kda_decay { KDA_DECAY_PER_DIM = 0, KDA_DECAY_PER_HEAD = 1 };
  *   FP32   fp32 matrix-core products;
  *   BF16X3 each fp32 operand split into bf16 hi + lo and the product formed as
  *          hi*hi + hi*lo + lo*hi (relative error about 2^-16 per product);
+ *          the fp32 range throughout;
  *   FP16   in the inter-chunk pass, the per-chunk operands (each entry bounded
  *          by 1) rounded once to fp16 and the state / update operands split
  *          into fp16 hi + lo (relative error about 2^-12 per product); the
- *          intra-chunk products as in BF16X3. */
+ *          intra-chunk products as in BF16X3.
+ *          Domain: each state and update entry x must satisfy |x| < 65504 (the
+ *          largest finite fp16 value); the pair hi + lo then holds x to within
+ *          max(2^-22 |x|, 2^-25), so entries much smaller than 2^-12 lose
+ *          relative precision.  Outside the domain the split overflows and the
+ *          call's o, y and state are not finite (never finite and wrong).  Use
+ *          BF16X3 or FP32 for states or value rows that may leave it. */
 enum kda_precision { KDA_PREC_FP32 = 0, KDA_PREC_BF16X3 = 1, KDA_PREC_FP16 = 2 };
 
 typedef struct kda_dims {
-  int32_t num_heads;  /* H >= 1 */
+  int32_t num_heads;  /* 1 <= H <= 65535 */
   int32_t head_dim_k; /* d_k in {64, 128} */
   int32_t head_dim_v; /* d_v in {64, 128} */
   int32_t conv_width; /* must be 4 */

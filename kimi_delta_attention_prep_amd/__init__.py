@@ -114,15 +114,31 @@ def _dtype_code(dt: torch.dtype) -> int:
     raise TypeError(f"unsupported dtype {dt}")
 
 
+def _shape_ok(t, shape) -> bool:
+    """`shape` entries are sizes, or None for any size (a pool's slot count)."""
+    return t.dim() == len(shape) and all(want is None or have == want for have, want in zip(t.shape, shape))
+
+
+def _validate(specs, device=True):
+    """Check every (name, tensor, dtype or None, shape or None) entry: first the type, dtype and shape of all of
+    them, then (unless device is False) that each is a contiguous device tensor.  The library receives bare
+    pointers and cannot check a buffer's size, so this is the guard against reads and writes past an allocation;
+    it runs before any launch."""
+    for name, t, dtype, shape in specs:
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a tensor")
+        if dtype is not None and t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+        if shape is not None and not _shape_ok(t, shape):
+            want = tuple("*" if x is None else x for x in shape)
+            raise ValueError(f"{name} must have shape {want}, got {tuple(t.shape)}")
+    for name, t, _, _ in specs if device else ():
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+
+
 def _need(t, name, dtype=None, shape=None):
-    if not isinstance(t, torch.Tensor):
-        raise TypeError(f"{name} must be a tensor")
-    if not t.is_cuda or not t.is_contiguous():
-        raise ValueError(f"{name} must be a contiguous device tensor")
-    if dtype is not None and t.dtype != dtype:
-        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if shape is not None and tuple(t.shape) != tuple(shape):
-        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    _validate([(name, t, dtype, shape)])
     return t
 
 
@@ -208,21 +224,21 @@ class Dims:
 def kda_prep(d: Dims, cu_seqlens, q_raw, k_raw, v_raw, conv_weight, conv_state_in, conv_state_out, g_raw,
              beta_logit, gate_mode, lower_bound, q_hat, k_hat, v_out, g_out, beta_out, slots=None):
     lib = load_library()
+    H, dk, dv, dt = d.num_heads, d.head_dim_k, d.head_dim_v, d.in_dtype
+    _validate([("cu_seqlens", cu_seqlens, torch.int32, (None,)), ("q_raw", q_raw, dt, (None, H, dk))], device=False)
     T = q_raw.shape[0]
     N = cu_seqlens.numel() - 1
-    H, dk, dv, dt = d.num_heads, d.head_dim_k, d.head_dim_v, d.in_dtype
-    _need(cu_seqlens, "cu_seqlens", torch.int32)
-    for name, t, shp in (("q_raw", q_raw, (T, H, dk)), ("k_raw", k_raw, (T, H, dk)), ("v_raw", v_raw, (T, H, dv)),
-                         ("g_raw", g_raw, d.g_shape(T)), ("beta_logit", beta_logit, (T, H))):
-        _need(t, name, dt, shp)
-    _need(conv_weight, "conv_weight", torch.float32, (d.conv_channels, 4))
-    _need(conv_state_in, "conv_state_in", dt)
-    _need(conv_state_out, "conv_state_out", dt, conv_state_in.shape)
-    for name, t, shp in (("q_hat", q_hat, (T, H, dk)), ("k_hat", k_hat, (T, H, dk)), ("v_out", v_out, (T, H, dv)),
-                         ("g_out", g_out, (T, H, dk)), ("beta_out", beta_out, (T, H))):
-        _need(t, name, torch.float32, shp)
+    C = d.conv_channels
+    specs = [("cu_seqlens", cu_seqlens, None, None), ("q_raw", q_raw, None, None), ("k_raw", k_raw, dt, (T, H, dk)), ("v_raw", v_raw, dt, (T, H, dv)), ("g_raw", g_raw, dt, d.g_shape(T)),
+             ("beta_logit", beta_logit, dt, (T, H)), ("conv_weight", conv_weight, torch.float32, (C, 4)),
+             ("conv_state_in", conv_state_in, dt, (None, 3, C)),
+             ("conv_state_out", conv_state_out, dt, tuple(conv_state_in.shape)),
+             ("q_hat", q_hat, torch.float32, (T, H, dk)), ("k_hat", k_hat, torch.float32, (T, H, dk)),
+             ("v_out", v_out, torch.float32, (T, H, dv)), ("g_out", g_out, torch.float32, (T, H, dk)),
+             ("beta_out", beta_out, torch.float32, (T, H))]
     if slots is not None:
-        _need(slots, "slots", torch.int32, (N,))
+        specs.append(("slots", slots, torch.int32, (N,)))
+    _validate(specs)
     pools = (("conv_state", conv_state_in.shape[0]),)
     _need_pool(N, slots, pools)
     if _debug:
@@ -247,41 +263,41 @@ def kda_prefill_varlen(d: Dims, cu_seqlens, q_hat, k_hat, v, g, beta, state, o, 
     conv_state_out, gate_mode, lower_bound) the preamble runs inside the prompt kernels and q_hat..beta may be None.
     With norm=dict(z, weight, eps, y) the gated output norm runs as the call's epilogue (y as gated_rmsnorm_out)."""
     lib = load_library()
-    N = cu_seqlens.numel() - 1
     H, dk, dv = d.num_heads, d.head_dim_k, d.head_dim_v
-    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    _validate([("cu_seqlens", cu_seqlens, torch.int32, (None,))], device=False)
+    N = cu_seqlens.numel() - 1
     rr = None
     if raw is None:
+        _validate([("q_hat", q_hat, torch.float32, (None, H, dk))], device=False)
         T = q_hat.shape[0]
-        for name, t, shp in (("q_hat", q_hat, (T, H, dk)), ("k_hat", k_hat, (T, H, dk)), ("v", v, (T, H, dv)),
-                             ("g", g, (T, H, dk)), ("beta", beta, (T, H))):
-            _need(t, name, torch.float32, shp)
+        specs = [("q_hat", q_hat, None, None), ("k_hat", k_hat, torch.float32, (T, H, dk)), ("v", v, torch.float32, (T, H, dv)),
+                 ("g", g, torch.float32, (T, H, dk)), ("beta", beta, torch.float32, (T, H))]
     else:
-        T = raw["q_raw"].shape[0]
         dt = d.in_dtype
-        for name, shp in (("q_raw", (T, H, dk)), ("k_raw", (T, H, dk)), ("v_raw", (T, H, dv)), ("g_raw", d.g_shape(T)),
-                          ("beta_logit", (T, H))):
-            _need(raw[name], name, dt, shp)
-        _need(raw["conv_weight"], "conv_weight", torch.float32, (d.conv_channels, 4))
-        _need(raw["conv_state_in"], "conv_state_in", dt)
-        _need(raw["conv_state_out"], "conv_state_out", dt, raw["conv_state_in"].shape)
+        _validate([("q_raw", raw["q_raw"], dt, (None, H, dk))], device=False)
+        T = raw["q_raw"].shape[0]
+        specs = [("q_raw", raw["q_raw"], None, None)]
+        specs += [(name, raw[name], dt, shp) for name, shp in
+                 (("k_raw", (T, H, dk)), ("v_raw", (T, H, dv)), ("g_raw", d.g_shape(T)), ("beta_logit", (T, H)))]
+        specs += [("conv_weight", raw["conv_weight"], torch.float32, (d.conv_channels, 4)),
+                  ("conv_state_in", raw["conv_state_in"], dt, (None, 3, d.conv_channels))]
+        specs.append(("conv_state_out", raw["conv_state_out"], dt, tuple(raw["conv_state_in"].shape)))
+    specs += [("cu_seqlens", cu_seqlens, None, None), ("o", o, torch.float32, (T, H, dv)),
+              ("state", state, torch.float32, (None, H, dk, dv)), ("workspace", workspace, None, None)]
+    if norm is not None:
+        specs += [("z", norm["z"], None, (T, H, dv)), ("weight", norm["weight"], torch.float32, (dv,)),
+                  ("y", norm["y"], None, (T, H, dv))]
+    if slots is not None:
+        specs.append(("slots", slots, torch.int32, (N,)))
+    _validate(specs)
+    if raw is not None:
         rr = KdaRawRows(*(raw[n].data_ptr() for n in ("q_raw", "k_raw", "v_raw", "g_raw", "beta_logit", "conv_weight",
                                                       "conv_state_in", "conv_state_out")),
                         int(raw["gate_mode"]), float(raw["lower_bound"]))
-    _need(o, "o", torch.float32, (T, H, dv))
     nn = None
     if norm is not None:
-        _need(norm["z"], "z", shape=(T, H, dv))
-        _need(norm["weight"], "weight", torch.float32, (dv,))
-        _need(norm["y"], "y", shape=(T, H, dv))
         nn = KdaNormArgs(norm["z"].data_ptr(), _dtype_code(norm["z"].dtype), norm["weight"].data_ptr(),
                          float(norm["eps"]), norm["y"].data_ptr(), _dtype_code(norm["y"].dtype))
-    _need(state, "state", torch.float32)
-    if state.dim() != 4 or tuple(state.shape[1:]) != (H, dk, dv):
-        raise ValueError(f"state must be [slots, {H}, {dk}, {dv}]")
-    _need(workspace, "workspace")
-    if slots is not None:
-        _need(slots, "slots", torch.int32, (N,))
     pools = (("state", state.shape[0]),) + ((("conv_state", raw["conv_state_in"].shape[0]),) if raw else ())
     _need_pool(N, slots, pools)
     if _debug:
@@ -291,24 +307,23 @@ def kda_prefill_varlen(d: Dims, cu_seqlens, q_hat, k_hat, v, g, beta, state, o, 
     dims = d.c()
     _check(lib.kda_prefill_varlen(ctypes.byref(dims), N, T, _ptr(cu_seqlens), _ptr(slots), _ptr(q_hat), _ptr(k_hat),
                                   _ptr(v), _ptr(g), _ptr(beta), ctypes.byref(rr) if rr is not None else None,
-                                  ctypes.byref(nn) if nn is not None else None, _ptr(state), _ptr(o), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                  _stream()))
+                                  ctypes.byref(nn) if nn is not None else None, _ptr(state), _ptr(o), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream()))
 
 
 def kda_decode(d: Dims, state, conv_state, conv_weight, q_raw, k_raw, v_raw, g_raw, beta_logit, gate_mode,
                lower_bound, o, slots=None):
     lib = load_library()
-    B = q_raw.shape[0]
     H, dk, dv, dt = d.num_heads, d.head_dim_k, d.head_dim_v, d.in_dtype
-    for name, t, shp in (("q_raw", q_raw, (B, H, dk)), ("k_raw", k_raw, (B, H, dk)), ("v_raw", v_raw, (B, H, dv)),
-                         ("g_raw", g_raw, d.g_shape(B)), ("beta_logit", beta_logit, (B, H))):
-        _need(t, name, dt, shp)
-    _need(state, "state", torch.float32)
-    _need(conv_state, "conv_state", dt)
-    _need(conv_weight, "conv_weight", torch.float32, (d.conv_channels, 4))
-    _need(o, "o", torch.float32, (B, H, dv))
+    _validate([("q_raw", q_raw, dt, (None, H, dk))], device=False)
+    B = q_raw.shape[0]
+    specs = [("q_raw", q_raw, None, None), ("k_raw", k_raw, dt, (B, H, dk)), ("v_raw", v_raw, dt, (B, H, dv)), ("g_raw", g_raw, dt, d.g_shape(B)),
+             ("beta_logit", beta_logit, dt, (B, H)), ("state", state, torch.float32, (None, H, dk, dv)),
+             ("conv_state", conv_state, dt, (None, 3, d.conv_channels)),
+             ("conv_weight", conv_weight, torch.float32, (d.conv_channels, 4)), ("o", o, torch.float32, (B, H, dv))]
     if slots is not None:
-        _need(slots, "slots", torch.int32, (B,))
+        specs.append(("slots", slots, torch.int32, (B,)))
+    _validate(specs)
     pools = (("state", state.shape[0]), ("conv_state", conv_state.shape[0]))
     _need_pool(B, slots, pools)
     if _debug and slots is not None:
@@ -343,31 +358,46 @@ class VerifyLog:
         return KdaLog(self.a.data_ptr(), self.k_hat.data_ptr(), self.u.data_ptr(), self.conv_rows.data_ptr(),
                       self.window)
 
+    def specs(self, d: Dims, batch: int, window: int, tag: str) -> list:
+        """Validation entries of every field for a log of `batch` sequences and `window` rows."""
+        H, dk, dv = d.num_heads, d.head_dim_k, d.head_dim_v
+        return [(f"{tag}.a", self.a, torch.float32, (batch, window, H, dk)),
+                (f"{tag}.k_hat", self.k_hat, torch.float32, (batch, window, H, dk)),
+                (f"{tag}.u", self.u, torch.float32, (batch, window, H, dv)),
+                (f"{tag}.conv_rows", self.conv_rows, d.in_dtype, (batch, window, d.conv_channels))]
+
 
 def kda_verify_window(d: Dims, state, conv_state, conv_weight, n_commit, log_in, log_out, q_raw, k_raw, v_raw,
                       g_raw, beta_logit, gate_mode, lower_bound, o, slots=None, batch=None, window_lens=None):
     lib = load_library()
     H, dk, dv, dt = d.num_heads, d.head_dim_k, d.head_dim_v, d.in_dtype
+    if q_raw is not None:
+        _validate([("q_raw", q_raw, dt, (None, None, H, dk))], device=False)
     W = 0 if q_raw is None else q_raw.shape[1]
     B = batch if batch is not None else (q_raw.shape[0] if q_raw is not None else n_commit.numel())
+    specs = [("state", state, torch.float32, (None, H, dk, dv)),
+             ("conv_state", conv_state, dt, (None, 3, d.conv_channels)),
+             ("conv_weight", conv_weight, torch.float32, (d.conv_channels, 4))]
     if W > 0:
-        for name, t, shp in (("q_raw", q_raw, (B, W, H, dk)), ("k_raw", k_raw, (B, W, H, dk)),
-                             ("v_raw", v_raw, (B, W, H, dv)), ("g_raw", g_raw, d.g_shape(B, W)),
-                             ("beta_logit", beta_logit, (B, W, H))):
-            _need(t, name, dt, shp)
-        _need(o, "o", torch.float32, (B, W, H, dv))
-    _need(state, "state", torch.float32)
-    _need(conv_state, "conv_state", dt)
-    _need(conv_weight, "conv_weight", torch.float32, (d.conv_channels, 4))
+        specs += [("q_raw", q_raw, dt, (B, W, H, dk)), ("k_raw", k_raw, dt, (B, W, H, dk)),
+                  ("v_raw", v_raw, dt, (B, W, H, dv)), ("g_raw", g_raw, dt, d.g_shape(B, W)),
+                  ("beta_logit", beta_logit, dt, (B, W, H)), ("o", o, torch.float32, (B, W, H, dv))]
+        if log_out is None:
+            raise ValueError("a window with rows needs log_out")
+        specs += log_out.specs(d, B, W, "log_out")
     if n_commit is not None:
-        _need(n_commit, "n_commit", torch.int32, (B,))
+        if log_in is None:
+            raise ValueError("n_commit needs the log it commits from (log_in)")
+        specs.append(("n_commit", n_commit, torch.int32, (B,)))
+        specs += log_in.specs(d, B, log_in.window, "log_in")
     if slots is not None:
-        _need(slots, "slots", torch.int32, (B,))
+        specs.append(("slots", slots, torch.int32, (B,)))
+    if window_lens is not None:
+        specs.append(("window_lens", window_lens, torch.int32, (B,)))
+    _validate(specs)
     dims = d.c()
     lin = log_in.c() if log_in is not None else None
     lout = log_out.c() if log_out is not None else None
-    if window_lens is not None:
-        _need(window_lens, "window_lens", torch.int32, (B,))
     pools = (("state", state.shape[0]), ("conv_state", conv_state.shape[0]))
     _need_pool(B, slots, pools)
     if _debug:
@@ -387,12 +417,13 @@ def kda_verify_window(d: Dims, state, conv_state, conv_weight, n_commit, log_in,
 
 def gated_rmsnorm_out(o, z, w, eps, y):
     lib = load_library()
+    _validate([("o", o, torch.float32, None)], device=False)
+    if o.dim() < 1:
+        raise ValueError("o must have at least one dimension (the d_v values of a row)")
     dv = o.shape[-1]
-    rows = o.numel() // dv
-    _need(o, "o", torch.float32)
-    _need(z, "z", shape=o.shape)
-    _need(w, "w", torch.float32, (dv,))
-    _need(y, "y", shape=o.shape)
+    rows = o.numel() // dv if dv else 0
+    _validate([("o", o, torch.float32, None), ("z", z, None, tuple(o.shape)), ("w", w, torch.float32, (dv,)),
+               ("y", y, None, tuple(o.shape))])
     _check(lib.gated_rmsnorm_out(rows, dv, _ptr(o), _ptr(z), _dtype_code(z.dtype), _ptr(w), float(eps), _ptr(y),
                                  _dtype_code(y.dtype), _stream()))
 

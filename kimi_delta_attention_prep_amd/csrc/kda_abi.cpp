@@ -8,6 +8,9 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "kda.h"
 #include "kda_launch.hpp"
@@ -31,12 +34,29 @@ int ok() {
   return KDA_OK;
 }
 
+// Limits that keep every launch within a grid's extents: heads go on a grid axis of
+// at most 65535, and the prompt path's workgroup counts (one per (record slot, head),
+// one per 16 rows of the norm) on an axis of at most 2^31 - 1.
+constexpr int kMaxHeads = 65535;
+constexpr int64_t kMaxGridX = 2147483647;
+
+int check_rows(const char* what, const kda_dims* d, int32_t num_seqs, int64_t t_tot) {
+  if (t_tot > 2147483647) return fail(KDA_E_ARG, "%s: %lld rows exceed the int32 range of cu_seqlens", what,
+                                      (long long)t_tot);
+  const int64_t records = t_tot / 64 + num_seqs;  // record slots of the prompt path
+  if (records * d->num_heads > kMaxGridX || (t_tot * d->num_heads) / 16 > kMaxGridX)
+    return fail(KDA_E_ARG, "%s: %lld rows x %d heads exceed the launch grid", what, (long long)t_tot, d->num_heads);
+  return KDA_OK;
+}
+
 bool aligned(const void* p, unsigned a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1u)) == 0; }
 unsigned elem_bytes(int32_t dtype) { return dtype == KDA_DTYPE_BF16 ? 2u : 4u; }
 
 int check_dims(const kda_dims* d) {
   if (!d) return fail(KDA_E_ARG, "dims is NULL");
   if (d->num_heads < 1) return fail(KDA_E_ARG, "num_heads must be >= 1 (got %d)", d->num_heads);
+  if (d->num_heads > kMaxHeads)
+    return fail(KDA_E_GEOMETRY, "num_heads %d unsupported: at most %d", d->num_heads, kMaxHeads);
   if (!((d->head_dim_k == 64 || d->head_dim_k == 128) && (d->head_dim_v == 64 || d->head_dim_v == 128)))
     return fail(KDA_E_GEOMETRY, "head dims (%d, %d) unsupported: d_k and d_v must be 64 or 128", d->head_dim_k,
                 d->head_dim_v);
@@ -90,6 +110,24 @@ int hip_status(hipError_t e, const char* what) {
 
 }  // namespace
 
+namespace kda {
+
+hipError_t ensure_dynamic_lds(const void* kernel, size_t bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, size_t> set_to;  // (kernel, device) -> bytes allowed
+  std::lock_guard<std::mutex> lock(mu);
+  size_t& have = set_to[std::make_pair(kernel, dev)];
+  if (have >= bytes) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) have = bytes;
+  return e;
+}
+
+}  // namespace kda
+
 extern "C" {
 
 const char* kda_last_error(void) { return g_err; }
@@ -111,6 +149,7 @@ int kda_prep(const kda_dims* d, int32_t num_seqs, int64_t t_tot, const int32_t* 
   KDA_TRY(check_gate(gate_mode, lower_bound));
   if (num_seqs < 0 || t_tot < 0) return fail(KDA_E_ARG, "kda_prep: negative size");
   if (num_seqs == 0 && t_tot > 0) return fail(KDA_E_ARG, "kda_prep: rows without sequences");
+  KDA_TRY(check_rows("kda_prep", d, num_seqs, t_tot));
   KDA_TRY(check_opt_ptr("kda_prep: slots", slots));
   const unsigned eb = elem_bytes(d->in_dtype);
   if (num_seqs > 0) {
@@ -141,6 +180,7 @@ int kda_prefill_varlen(const kda_dims* d, int32_t num_seqs, int64_t t_tot, const
                        float* state, float* o, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   KDA_TRY(check_dims(d));
   if (num_seqs < 0 || t_tot < 0) return fail(KDA_E_ARG, "kda_prefill_varlen: negative size");
+  KDA_TRY(check_rows("kda_prefill_varlen", d, num_seqs, t_tot));
   if (norm) {
     if ((norm->z_dtype != KDA_DTYPE_F32 && norm->z_dtype != KDA_DTYPE_BF16) ||
         (norm->y_dtype != KDA_DTYPE_F32 && norm->y_dtype != KDA_DTYPE_BF16))
@@ -292,6 +332,7 @@ int kda_verify_window(const kda_dims* d, int32_t batch, int32_t window, const in
 int gated_rmsnorm_out(int64_t rows, int32_t d_v, const float* o, const void* z, int32_t z_dtype, const float* w,
                       float eps, void* y, int32_t y_dtype, hipStream_t stream) {
   if (rows < 0) return fail(KDA_E_ARG, "gated_rmsnorm_out: negative rows");
+  if (rows / 16 > kMaxGridX) return fail(KDA_E_ARG, "gated_rmsnorm_out: %lld rows exceed the launch grid", (long long)rows);
   if (d_v != 64 && d_v != 128) return fail(KDA_E_GEOMETRY, "gated_rmsnorm_out: d_v %d not in {64, 128}", d_v);
   if ((z_dtype != KDA_DTYPE_F32 && z_dtype != KDA_DTYPE_BF16) || (y_dtype != KDA_DTYPE_F32 && y_dtype != KDA_DTYPE_BF16))
     return fail(KDA_E_DTYPE, "gated_rmsnorm_out: unknown dtype");

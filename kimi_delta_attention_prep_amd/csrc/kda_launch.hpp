@@ -8,6 +8,12 @@
 
 namespace kda {
 
+// Raises `kernel`'s dynamic-LDS limit to at least `bytes` on the calling thread's
+// current device.  The attribute is set once per (kernel, device) for the life of
+// the process, under a lock, so host threads that make their first calls at the
+// same time, or calls on several devices, each find it set before they launch.
+hipError_t ensure_dynamic_lds(const void* kernel, size_t bytes);
+
 struct RowsLaunch {
   int H, dk, dv, in_dtype, act, gate_mode, batch, window;
   float lb;

@@ -376,9 +376,7 @@ struct IntraSmem {
   static constexpr int TA = T2 + L * PK;      // A                                   [L][PL]
   static constexpr int TP = TA + L * PL;      // P, then X                           [L][PL]
   static constexpr int TB = TP + L * PL;      // beta                                [L]
-  static constexpr int TGF = TB + L;          // G_{16R} from the chunk start         [4][DK]
-  static constexpr int TX = TGF + 4 * DK;     // G_last - G_{16I}                     [4][DK]
-  static constexpr int TD = TX + 4 * DK;      // e^{G_{16R} - G_{16I+16}}, I + 1 < R  [6][DK]
+  static constexpr int TD = TB + L;           // e^{G_{16R} - G_{16I+16}}, I + 1 < R  [6][DK]
   static constexpr int TG0 = TD + 6 * DK;     // g at each block's first row          [4][DK]
   static constexpr int TY = TG0 + 4 * DK;     // solve scratch, one per wavefront    [3][16][17]
   static constexpr int TFLAG = TY + 3 * 16 * 17;
@@ -538,8 +536,6 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
   float* sA = smem + SM::TA;
   float* sP = smem + SM::TP;
   float* sBeta = smem + SM::TB;
-  float* sGF = smem + SM::TGF;
-  float* sX = smem + SM::TX;
   float* sD = smem + SM::TD;
   float* sG0 = smem + SM::TG0;
   float* sGFe = smem + SM::TGFE;
@@ -739,11 +735,11 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
   }
   __syncthreads();
 
-  // 3. per key dim, from block-local sums: T_R = G_{16R+16} - G_{16R}, G_{16R}, G_last - G_{16I},
-  //    e^{G_{16R} - G_{16I+16}} for the off-diagonal block pairs, and gamma_L; for the
-  //    pivoted path also e^{G_{16R}}, e^{G_last - G_{16I+16}} (I < 3) or e^{G_last - G_48},
-  //    and e^{T_I}.  Both sets are written: which path the chunk takes is known after
-  //    the barrier.  One thread per (block R, key dim d); every sum runs over J in order.
+  // 3. per key dim, from block-local sums: T_R = G_{16R+16} - G_{16R}, and the exponentials of the
+  //    pivoted path: e^{G_{16R}}, e^{G_last - G_{16I+16}} (I < 3) or e^{G_last - G_48},
+  //    e^{G_{16R} - G_{16I+16}} for the off-diagonal block pairs, e^{T_I}, and gamma_L (which
+  //    the exact path rewrites from its own sums: which path the chunk takes is known after
+  //    the barrier).  One thread per (block R, key dim d); every sum runs over J in order.
   if (t < 4 * DK) {
     const int R = t / DK, d = t % DK;
     float T[3];
@@ -754,14 +750,12 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
     const float g0 = sG0[d];
     float gf = g0;  // G_{16R}
     for (int J = 0; J < R; ++J) gf += T[J];
-    sGF[R * DK + d] = gf;
     sGFe[R * DK + d] = pexp<POL>(gf);
     float x = 0.f;  // G_last - G_{16R}: blocks past the last row hold only zero rows
     if (R <= Rl) {
       x = glL;
       for (int J = R; J < Rl; ++J) x += T[J];
     }
-    sX[R * DK + d] = x;
     sXe[R * DK + d] = pexp<POL>(R < 3 ? x - T[R] : x);
     for (int I = 0; I + 1 < R; ++I) {
       float dd = 0.f;
@@ -780,14 +774,59 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
   __syncthreads();
   const bool exact = sFlag[0] != 0;
 
-  // 4. exact path: operand fragments of Q^gamma = e^{G_r} q_r and K_<^T (e^{G_last - G_i} k_i),
-  //    one exponential per element (the pivoted path forms them from its factors in step 5)
+  // 4. exact path.  Its exponents are differences G_r - G_i of prefix sums over the chunk,
+  //    G_r = g_0 + ... + g_r, which grow to thousands under steep decay; a prefix sum
+  //    rounded to fp32 would carry that magnitude's rounding into every difference.  So
+  //    each G_r is kept as an unevaluated sum hi + lo of two fp32 numbers, accumulated
+  //    with Knuth's two-sum (the rounding error of every addition goes into lo), and a
+  //    difference is (hi_r - hi_i) + (lo_r - lo_i), exact up to its own last rounding.
+  //    The log decays are read again from their source and recomputed by the same
+  //    function as in step 1, so they are the same values.  hi replaces gl in T2, lo
+  //    lives over the A and P tiles until the pair products are stored.  Then the
+  //    operand fragments of Q^gamma = e^{G_r} q_r and K_<^T (e^{G_last - G_i} k_i) and
+  //    gamma_L, one exponential per element (the pivoted path forms them from its
+  //    factors in step 5).
+  float* sGlo = sA;  // [L][PK] over the A and P tiles (exact path only)
+  static_assert(L * PK <= 2 * L * PL, "the low parts fit over the A and P tiles");
+  const int last = len - 1;
   if (exact) {
+    for (int idx = t; idx < L * DK; idx += NT) {
+      const int r = idx / DK, d = idx % DK;
+      float gr = 0.f;
+      if (r < len) {
+        if constexpr (FUSED) {
+          const RawT* rg = static_cast<const RawT*>(p.raw.g);
+          gr = log_decay(to_f32(p.raw.g_per_head ? rg[(start + r) * H + h] : rg[((start + r) * H + h) * DK + d]),
+                         p.raw.gate_mode, p.raw.lb);
+        } else {
+          gr = p.g[((start + r) * H + h) * DK + d];
+        }
+      }
+      sG[r * PK + d] = gr;
+    }
+    __syncthreads();
+    if (t < DK) {  // one key dim per thread, rows in order
+      float hi = 0.f, lo = 0.f;
+      for (int r = 0; r < L; ++r) {
+        const float gr = sG[r * PK + t];
+        const float sum = hi + gr, bv = sum - hi;
+        lo += (hi - (sum - bv)) + (gr - bv);
+        hi = sum;
+        sG[r * PK + t] = hi;
+        sGlo[r * PK + t] = lo;
+      }
+    }
+    __syncthreads();
+    if (t >= 3 * DK && t < 4 * DK) {  // the thread that wrote gamma_L in step 3
+      const int d = t - 3 * DK;
+      reinterpret_cast<float*>(rec + rl.gL)[d] = pexp<POL>(sG[last * PK + d] + sGlo[last * PK + d]);
+    }
     write_afrags<POL, NT>(rec + rl.Qf, 4, DK / 32, [&](int r, int d) {
-      return sQ[r * PK + d] * pexp<POL>(sGF[(r / 16) * DK + d] + sG[r * PK + d]);
+      return sQ[r * PK + d] * pexp<POL>(sG[r * PK + d] + sGlo[r * PK + d]);
     });
     write_afrags<POL, NT>(rec + rl.Kf, DK / 16, 2, [&](int d, int r) {
-      return sK[r * PK + d] * pexp<POL>(sX[(r / 16) * DK + d] - sG[r * PK + d]);
+      return sK[r * PK + d] *
+             pexp<POL>((sG[last * PK + d] - sG[r * PK + d]) + (sGlo[last * PK + d] - sGlo[r * PK + d]));
     });
     __syncthreads();
   }
@@ -809,7 +848,7 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
   //                           = e^{G_last - G_48} (k_i e^{-gl_i})             (I = 3)
   //    (every factor at most 1, or within the span guard for the last block),
   //    with the per-(block, key dim) exponentials of step 3 in place of G_{16R}
-  //    and G_last - G_{16I} (read raw only on the exact path), and
+  //    and G_last - G_{16I}, and
   //    k e^{T_I - gl} = (k e^{-gl}) e^{T_I}, one product.
   if (!exact) {
     float* sRk = sA;  // [48][PK] k e^{T_I - gl}, over the A and P tiles until the products are done
@@ -883,21 +922,32 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
       if ((ii >> 4) > (rr >> 4)) { sA[rr * PL + ii] = 0.f; sP[rr * PL + ii] = 0.f; }
     }
   } else {
-    // exact path: every pair (r, i <= r) with one exponential of G_r - G_i per key dim
-    for (int pr = t; pr < L * L; pr += NT) {
-      const int r = pr / L, i = pr % L;
-      float sa = 0.f, sp = 0.f;
-      if (i <= r) {
-        const int R = r / 16, I = i / 16;
+    // exact path: every pair (r, i <= r) with one exponential of G_r - G_i per key dim, the
+    // difference taken from the two-sum prefixes of step 4; the sums are kept in registers
+    // until every thread is done reading the low parts over the A and P tiles
+    constexpr int NPR = (L * L + NT - 1) / NT;
+    float sa[NPR], sp[NPR];
+#pragma unroll
+    for (int j = 0; j < NPR; ++j) {
+      const int pr = t + j * NT, r = pr / L, i = pr % L;
+      sa[j] = sp[j] = 0.f;
+      if (pr < L * L && i <= r) {
         for (int d = 0; d < DK; ++d) {
-          const float dg = (sGF[R * DK + d] - sGF[I * DK + d]) + (sG[r * PK + d] - sG[i * PK + d]);
+          const float dg = (sG[r * PK + d] - sG[i * PK + d]) + (sGlo[r * PK + d] - sGlo[i * PK + d]);
           const float e = expf(dg);
-          sa = fmaf(sK[r * PK + d] * sK[i * PK + d], e, sa);
-          sp = fmaf(sQ[r * PK + d] * sK[i * PK + d], e, sp);
+          sa[j] = fmaf(sK[r * PK + d] * sK[i * PK + d], e, sa[j]);
+          sp[j] = fmaf(sQ[r * PK + d] * sK[i * PK + d], e, sp[j]);
         }
       }
-      sA[r * PL + i] = (i < r) ? sBeta[r] * sa : 0.f;
-      sP[r * PL + i] = (i <= r) ? sp : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NPR; ++j) {
+      const int pr = t + j * NT, r = pr / L, i = pr % L;
+      if (pr < L * L) {
+        sA[r * PL + i] = (i < r) ? sBeta[r] * sa[j] : 0.f;
+        sP[r * PL + i] = (i <= r) ? sp[j] : 0.f;
+      }
     }
   }
   __syncthreads();
@@ -960,7 +1010,7 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
   //    b_r e^{G_r} k_r into T2, b_r v_r into T0 (through T1).  A fragment item is
   //    (column tile c, 32-row block kb, lane): 8 rows of one column.  e^{G_r} k_r
   //    is e^{G_{16R}} (k_r e^{gl_r}) from the factors of step 5, or formed
-  //    directly from gl on the exact path.
+  //    directly from the chunk prefix G_r on the exact path.
   using FI = Frag<IP>;
   using FB = typename FI::B;
   constexpr int NFK = (DK / 16) * 2 * 64, PFK = (NFK + NT - 1) / NT;
@@ -977,9 +1027,9 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int r = 32 * kb + FI::kof(g, e);
-          const float gf = (exact ? sGF : sGFe)[(r / 16) * DK + d];  // G_{16R}, or e^{G_{16R}} off the exact path
-          if (exact) x[e] = sBeta[r] * (sK[r * PK + d] * pexp<POL>(gf + sG[r * PK + d]));
-          else x[e] = sBeta[r] * (FT::load1(sK, r, d) * gf);
+          // exact path: T2 holds the chunk prefix G_r (its high part); else e^{G_{16R}} times the factor k e^{gl}
+          if (exact) x[e] = sBeta[r] * (sK[r * PK + d] * pexp<POL>(sG[r * PK + d]));
+          else x[e] = sBeta[r] * (FT::load1(sK, r, d) * sGFe[(r / 16) * DK + d]);
         }
         fk[i] = FI::make_b(x);
       }
@@ -1411,13 +1461,8 @@ static hipError_t launch_prefill_t(const PrefillLaunch& Lc, hipStream_t s) {
   const int64_t mc = max_chunks(Lc.num_seqs, Lc.t_tot);
   constexpr size_t intra_bytes = IntraSmem<DK, DV>::BYTES;
   constexpr size_t scan_bytes = ScanSmem<DK, POL>::BYTES;
-  static bool attr_set = false;
-  if (!attr_set) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_intra_kernel<DK, DV, POL, RawT, FUSED>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)intra_bytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  e = ensure_dynamic_lds(reinterpret_cast<const void*>(&chunk_intra_kernel<DK, DV, POL, RawT, FUSED>), intra_bytes);
+  if (e != hipSuccess) return e;
   e = mark(0, 0);
   if (e != hipSuccess) return e;
   if (mc > 0 && Lc.t_tot > 0 && Lc.num_seqs > 0) {

@@ -152,9 +152,12 @@ __global__ __launch_bounds__(256) void prep_tile_kernel(PrepArgs<RawT> p) {
 // back into conv_state_in for short sequences.  Rows are written in order
 // r = 0, 1, 2 by the thread that reads them; with in == out, row r reads old
 // row r + len >= r, so nothing is overwritten before it is read.
+constexpr int kSeqGridY = 65535;  // the largest y extent of a grid: sequences beyond it continue in z
+
 template <typename RawT>
 __global__ __launch_bounds__(256) void conv_state_kernel(PrepArgs<RawT> p, int DK, int DV) {
-  const int n = blockIdx.y;
+  const int n = (int)(blockIdx.z * kSeqGridY + blockIdx.y);
+  if (n >= p.num_seqs) return;
   const int64_t C = (int64_t)p.H * (2 * DK + DV);
   const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (c >= C) return;
@@ -202,21 +205,18 @@ static hipError_t launch_prep_t(const PrepLaunch& L, hipStream_t s) {
   const int64_t mc = max_chunks(L.num_seqs, L.t_tot);
   if (L.t_tot > 0 && L.num_seqs > 0) {
     constexpr size_t lds = (size_t)(kChunk + 3) * (DK > DV ? DK : DV) * sizeof(RawT);
-    static bool attr_set = false;
-    if (!attr_set) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_tile_kernel<DK, DV, RawT>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
+    const hipError_t ea = ensure_dynamic_lds(reinterpret_cast<const void*>(&prep_tile_kernel<DK, DV, RawT>), lds);
+    if (ea != hipSuccess) return ea;
     hipLaunchKernelGGL((prep_tile_kernel<DK, DV, RawT>), dim3((unsigned)mc, (unsigned)L.H, 4), dim3(256), lds, s, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const int64_t C = (int64_t)L.H * (2 * DK + DV);
   if (L.num_seqs > 0) {
-    hipLaunchKernelGGL((conv_state_kernel<RawT>), dim3((unsigned)((C + 255) / 256), (unsigned)L.num_seqs), dim3(256),
-                       0, s, p, DK, DV);
+    const unsigned gy = (unsigned)(L.num_seqs < kSeqGridY ? L.num_seqs : kSeqGridY);
+    const unsigned gz = (unsigned)((L.num_seqs + kSeqGridY - 1) / kSeqGridY);
+    hipLaunchKernelGGL((conv_state_kernel<RawT>), dim3((unsigned)((C + 255) / 256), gy, gz), dim3(256), 0, s, p, DK,
+                       DV);
   }
   return hipGetLastError();
 }

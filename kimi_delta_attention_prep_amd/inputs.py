@@ -3,7 +3,8 @@
 This module only draws random numbers; it holds none of the layer's arithmetic.
 Both the GPU path and the fp64 CPU oracle take their inputs from here.
 
-Draw order (fixed, one CPU generator per workload, seed 0 unless given):
+Draw order (fixed, one generator per workload -- the CPU's unless the workload
+says otherwise -- seed 0 unless given):
 lengths, q_raw, k_raw, v_raw, g_raw, beta_logit, z, conv_w, norm_w, state0,
 conv_state0.  Values are drawn in float32, then rounded to bfloat16 (round to
 nearest even, torch's conversion) where the workload is bf16.  The oracle
@@ -18,6 +19,8 @@ Workloads (sizes as in the pages' serving context: 128-wide KDA heads):
             state0 ~ N(0, 0.02^2), conv_state0 ~ N(0,1)
   verify    B=64, window 4 on top of a carried state, H=32, d=128, bf16,
             safe gate lb=-5, accept length j ~ U{0..3}
+  verify_prefilled  the same window on the state a 2048-row prompt per
+            sequence leaves (zero initial carries)
 Common: q/k/v/gate/beta-logit/z ~ N(0,1); conv_w ~ U(-1/2, 1/2) (bound
 1/sqrt(W) for W=4 taps); norm_w ~ U(0.5, 1.5).
 """
@@ -75,13 +78,18 @@ class Workload:
               for f in self.__dataclass_fields__}
         return Workload(**kw)
 
+    def head_channels(self, heads) -> torch.Tensor:
+        """Conv-channel indices of a subset of heads, in conv channel order (q, then k, then v)."""
+        H, dk, dv = self.H, self.dk, self.dv
+        return torch.tensor([h * dk + i for h in heads for i in range(dk)] +
+                            [H * dk + h * dk + i for h in heads for i in range(dk)] +
+                            [2 * H * dk + h * dv + i for h in heads for i in range(dv)])
+
     def select_heads(self, heads) -> "Workload":
         """The same workload restricted to a subset of heads (conv channels picked per stream)."""
         heads = list(heads)
-        H, dk, dv = self.H, self.dk, self.dv
-        ch = torch.tensor([h * dk + i for h in heads for i in range(dk)] +
-                          [H * dk + h * dk + i for h in heads for i in range(dk)] +
-                          [2 * H * dk + h * dv + i for h in heads for i in range(dv)])
+        dk, dv = self.dk, self.dv
+        ch = self.head_channels(heads)
         hs = torch.tensor(heads)
         pick = (lambda t: t[:, hs].contiguous())
         return Workload(self.name, len(heads), dk, dv, self.cu_seqlens, pick(self.q), pick(self.k), pick(self.v),
@@ -95,12 +103,16 @@ class Workload:
 
 
 def _normal(gen, shape, std=1.0):
-    return torch.randn(shape, generator=gen, dtype=torch.float32) * std
+    x = torch.randn(shape, generator=gen, dtype=torch.float32, device=gen.device)
+    return x if std == 1.0 else x * std
 
 
 def generate(name: str, *, lengths, H, dk, dv, dtype, gate_mode, lower_bound=-5.0, state_std=0.0,
-             conv_state_std=0.0, seed=0, meta=None) -> Workload:
-    gen = torch.Generator("cpu").manual_seed(seed)
+             conv_state_std=0.0, seed=0, meta=None, device="cpu") -> Workload:
+    """device: where the generator draws and the tensors live (cu_seqlens always on the host).  The CPU
+    generator is the default; a workload too large to draw on the host in reasonable time draws on the
+    GPU's generator instead (other values for the same seed, used by both sides alike)."""
+    gen = torch.Generator(device).manual_seed(seed)
     if callable(lengths):
         lengths = lengths(gen)
     lengths = [int(x) for x in lengths]
@@ -115,11 +127,12 @@ def generate(name: str, *, lengths, H, dk, dv, dtype, gate_mode, lower_bound=-5.
     g = _normal(gen, (T, H, dk))
     beta = _normal(gen, (T, H))
     z = _normal(gen, (T, H, dv))
-    conv_w = torch.rand((C, CONV_W), generator=gen, dtype=torch.float32) - 0.5
-    norm_w = torch.rand((dv,), generator=gen, dtype=torch.float32) + 0.5
-    state0 = _normal(gen, (N, H, dk, dv), state_std) if state_std > 0 else torch.zeros((N, H, dk, dv))
+    conv_w = torch.rand((C, CONV_W), generator=gen, dtype=torch.float32, device=device) - 0.5
+    norm_w = torch.rand((dv,), generator=gen, dtype=torch.float32, device=device) + 0.5
+    state0 = (_normal(gen, (N, H, dk, dv), state_std) if state_std > 0
+              else torch.zeros((N, H, dk, dv), device=device))
     conv_state0 = (_normal(gen, (N, CONV_W - 1, C), conv_state_std) if conv_state_std > 0
-                   else torch.zeros((N, CONV_W - 1, C)))
+                   else torch.zeros((N, CONV_W - 1, C), device=device))
     cast = (lambda t: t.to(dtype))
     return Workload(name, H, dk, dv, cu, cast(q), cast(k), cast(v), cast(g), cast(beta), cast(z), conv_w, norm_w,
                     state0, cast(conv_state0), gate_mode, float(lower_bound), dict(meta or {}))
@@ -136,7 +149,7 @@ def prefill(seed=0, T=4096, H=16, d=128) -> Workload:
 
 
 def varlen(seed=0, N=8, lo=512, hi=8192, H=32, d=128) -> Workload:
-    lens = (lambda gen: torch.randint(lo, hi + 1, (N,), generator=gen).tolist())
+    lens = (lambda gen: torch.randint(lo, hi + 1, (N,), generator=gen, device=gen.device).tolist())
     return generate("varlen", lengths=lens, H=H, dk=d, dv=d, dtype=torch.bfloat16, gate_mode=GATE_SOFTPLUS,
                     state_std=0.02, conv_state_std=1.0, seed=seed)
 
@@ -152,6 +165,19 @@ def verify(seed=0, B=64, window=4, H=32, d=128) -> Workload:
     (rows 0..j of each window are kept)."""
     w = generate("verify", lengths=[window] * B, H=H, dk=d, dv=d, dtype=torch.bfloat16, gate_mode=GATE_SAFE,
                  lower_bound=-5.0, state_std=0.02, conv_state_std=1.0, seed=seed, meta={"window": window})
+    gen = torch.Generator("cpu").manual_seed(seed + 1)
+    w.meta["accept"] = torch.randint(0, window, (B,), generator=gen, dtype=torch.int32)
+    return w
+
+
+def verify_prefilled(seed=0, B=64, prompt=2048, window=4, H=32, d=128, device="cuda") -> Workload:
+    """B sequences of prompt + window rows each: the first `prompt` rows of a sequence build its state through
+    the chunked prompt path, the last `window` rows are its draft window.  Zero initial carries; safe gate
+    lb=-5; meta['accept'] = j ~ U{0..window-1} (rows 0..j of each window are kept).  At the full size (2.7 G
+    values) it draws on the GPU's generator by default."""
+    w = generate("verify_prefilled", lengths=[prompt + window] * B, H=H, dk=d, dv=d, dtype=torch.bfloat16,
+                 gate_mode=GATE_SAFE, lower_bound=-5.0, seed=seed, meta={"prompt": prompt, "window": window},
+                 device=device)
     gen = torch.Generator("cpu").manual_seed(seed + 1)
     w.meta["accept"] = torch.randint(0, window, (B,), generator=gen, dtype=torch.int32)
     return w

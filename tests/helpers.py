@@ -97,3 +97,20 @@ def gpu_decode_steps(w: Workload, steps: int, dev="cuda"):
     K.gated_rmsnorm_out(o, rows["z"], wd.norm_w, EPS, y)
     torch.cuda.synchronize()
     return dict(o=o, y=y, state=state, conv_state=cs)
+
+
+def oracle_pieces(w: Workload, pieces, seqs=None, heads=None, state0=None, conv_state0=None, with_log=False):
+    """The oracle over sequences made of chosen packed rows of w: sequence b runs rows pieces[b] (indices into w's
+    rows, in order) from the initial state and conv state of w's sequence seqs[b] (default b), or from the given
+    state0 [len(pieces), H, dk, dv] / conv_state0 [len(pieces), 3, C] (float64).  heads restricts every tensor to
+    those heads (conv channels picked per stream)."""
+    ww = w.select_heads(heads) if heads is not None else w
+    seqs = list(range(len(pieces))) if seqs is None else list(seqs)
+    idx = np.concatenate([np.asarray(p, dtype=np.int64) for p in pieces]) if len(pieces) else np.zeros(0, np.int64)
+    cu = np.zeros(len(pieces) + 1, dtype=np.int64)
+    cu[1:] = np.cumsum([len(p) for p in pieces])
+    take = lambda name: ww.f64(name)[idx]
+    st0 = ww.f64("state0")[seqs] if state0 is None else state0
+    cs0 = ww.f64("conv_state0")[seqs] if conv_state0 is None else conv_state0
+    return O.layer(take("q"), take("k"), take("v"), ww.f64("conv_w"), cs0, take("g"), take("beta"), take("z"),
+                   ww.f64("norm_w"), st0, cu, gate_mode=w.gate_mode, lower_bound=w.lower_bound, with_log=with_log)

@@ -185,3 +185,89 @@ def test_pool_size_without_slot_map():
     K._need_pool(3, object(), (("state", 1),))  # with a slot map only the device contents can tell
     with pytest.raises(ValueError, match="no slot map"):
         K._need_pool(4, None, (("state", 8), ("conv_state", 3)))
+
+
+def test_head_count_and_grid_limits(lib):
+    """Heads go on a grid axis of at most 65535, and the prompt path's workgroup counts must fit a grid."""
+    assert decode(lib, dims(H=65536)) == K.KDA_E_GEOMETRY
+    d = dims()
+    big = 1 << 31  # more rows than cu_seqlens (int32) can address
+    assert lib.kda_prep(ctypes.byref(d), 2, big, A, None, A, A, A, A, A, A, A, A, K.GATE_SAFE, -5.0, A, A, A, A, A,
+                        None) == K.KDA_E_ARG
+    wide = dims(H=65535)
+    rows = (1 << 31) - 1  # (rows / 64) record slots x 65535 heads overflow the grid
+    assert lib.kda_prefill_varlen(ctypes.byref(wide), 1, rows, A, None, A, A, A, A, A, None, None, A, A, A, 1 << 40,
+                                  None) == K.KDA_E_ARG
+
+
+def _cpu_call_args(H=2, dk=128, dv=128, T=70, B=3, W=4):
+    """Host tensors of the right dtypes and shapes for every binding call (the binding validates shapes before it
+    requires device tensors, so a wrong shape is reported on the host with no launch)."""
+    import torch
+    d = K.Dims(H, dk, dv, torch.bfloat16)
+    C = d.conv_channels
+    bf = lambda *s: torch.zeros(*s, dtype=torch.bfloat16)
+    f = lambda *s: torch.zeros(*s, dtype=torch.float32)
+    return d, C, bf, f
+
+
+def test_binding_rejects_wrong_shapes_before_any_launch(lib):
+    import torch
+    d, C, bf, f = _cpu_call_args()
+    H, dk, dv, B, W = 2, 128, 128, 3, 4
+    cw = f(C, 4)
+    rows = lambda lead: (bf(*lead, H, dk), bf(*lead, H, dk), bf(*lead, H, dv), bf(*lead, H, dk), bf(*lead, H))
+
+    def decode_call(state=None, conv_state=None, o=None):
+        q, k, v, g, b = rows((B,))
+        K.kda_decode(d, f(B, H, dk, dv) if state is None else state, bf(B, 3, C) if conv_state is None else conv_state,
+                     cw, q, k, v, g, b, K.GATE_SAFE, -5.0, f(B, H, dv) if o is None else o)
+
+    with pytest.raises(ValueError, match="state must have shape"):
+        decode_call(state=f(B, H, 64, 64))  # a pool for d = 64 under d = 128 dims
+    with pytest.raises(ValueError, match="conv_state must have shape"):
+        decode_call(conv_state=bf(B, 3, C - 8))
+    with pytest.raises(TypeError, match="conv_state must be"):
+        decode_call(conv_state=f(B, 3, C))  # the conv state holds raw-row dtype
+    with pytest.raises(ValueError, match="o must have shape"):
+        decode_call(o=f(B + 1, H, dv))
+    with pytest.raises(ValueError, match="contiguous device tensor"):
+        decode_call()  # right shapes: the call still needs device tensors
+
+    def verify_call(log_in=None, log_out=None, n_commit=None):
+        q, k, v, g, b = (x.view(B, 1, *x.shape[1:]).expand(B, W, *x.shape[1:]).contiguous() for x in rows((B,)))
+        lo = K.VerifyLog(f(B, W, H, dk), f(B, W, H, dk), f(B, W, H, dv), bf(B, W, C)) if log_out is None else log_out
+        K.kda_verify_window(d, f(B, H, dk, dv), bf(B, 3, C), cw, n_commit, log_in, lo, q, k, v, g, b, K.GATE_SAFE,
+                            -5.0, f(B, W, H, dv))
+
+    with pytest.raises(ValueError, match="log_out.u must have shape"):
+        verify_call(log_out=K.VerifyLog(f(B, W, H, dk), f(B, W, H, dk), f(B, W, H, dv - 1), bf(B, W, C)))
+    with pytest.raises(ValueError, match="log_out.a must have shape"):
+        verify_call(log_out=K.VerifyLog(f(B + 1, W, H, dk), f(B, W, H, dk), f(B, W, H, dv), bf(B, W, C)))
+    with pytest.raises(TypeError, match="log_out.conv_rows must be"):
+        verify_call(log_out=K.VerifyLog(f(B, W, H, dk), f(B, W, H, dk), f(B, W, H, dv), f(B, W, C)))
+    short = K.VerifyLog(f(B, 2, H, dk), f(B, 2, H, dk), f(B, 2, H, dv), bf(B, 3, C))  # conv rows of another window
+    with pytest.raises(ValueError, match="log_in.conv_rows must have shape"):
+        verify_call(log_in=short, n_commit=torch.zeros(B, dtype=torch.int32))
+    with pytest.raises(ValueError, match="log_in"):
+        verify_call(n_commit=torch.zeros(B, dtype=torch.int32))  # commit counts without their log
+
+    T, N = 70, 2
+    q, k, v, g, b = rows((T,))
+    cu = torch.tensor([0, 30, T], dtype=torch.int32)
+    with pytest.raises(ValueError, match="conv_state_in must have shape"):
+        K.kda_prep(d, cu, q, k, v, cw, bf(N, 2, C), bf(N, 2, C), g, b, K.GATE_SAFE, -5.0, f(T, H, dk), f(T, H, dk),
+                   f(T, H, dv), f(T, H, dk), f(T, H))
+    with pytest.raises(ValueError, match="g_out must have shape"):
+        K.kda_prep(d, cu, q, k, v, cw, bf(N, 3, C), bf(N, 3, C), g, b, K.GATE_SAFE, -5.0, f(T, H, dk), f(T, H, dk),
+                   f(T, H, dv), f(T, H), f(T, H))
+    with pytest.raises(ValueError, match="state must have shape"):
+        K.kda_prefill_varlen(d, cu, f(T, H, dk), f(T, H, dk), f(T, H, dv), f(T, H, dk), f(T, H), f(N, H, dk),
+                             f(T, H, dv), torch.zeros(16, dtype=torch.uint8))
+    raw = dict(q_raw=q, k_raw=k, v_raw=v, g_raw=g, beta_logit=b, conv_weight=cw, conv_state_in=bf(N, 3, C),
+               conv_state_out=bf(N + 1, 3, C), gate_mode=K.GATE_SAFE, lower_bound=-5.0)
+    with pytest.raises(ValueError, match="conv_state_out must have shape"):
+        K.kda_prefill_varlen(d, cu, None, None, None, None, None, f(N, H, dk, dv), f(T, H, dv),
+                             torch.zeros(16, dtype=torch.uint8), raw=raw)
+    with pytest.raises(ValueError, match="y must have shape"):
+        K.gated_rmsnorm_out(f(T, dv), bf(T, dv), f(dv), 1e-6, f(T, dv + 1))

@@ -119,3 +119,29 @@ def test_decode_batch_beyond_one_grid_row():
     assert torch.equal(st[idx], st2[idx])
     assert torch.equal(cs[idx], cs2[idx])
     assert not torch.equal(st[65539], state0[65539])  # the last sequence was decoded
+
+
+def test_prep_sequences_beyond_one_grid_row():
+    """kda_prep over more sequences than a grid's y extent (65535): the conv-state carry of the last
+    sequences (past the boundary) is the bit copy of their raw rows the oracle gives, and every
+    preamble output matches the oracle."""
+    from oracle import oracle as O
+    N, H, d = 65540, 1, 64
+    lens = [2 if n % 3 else 5 for n in range(N)]  # sequences shorter and longer than the 3 carried rows
+    w = I.generate("many_seqs", lengths=lens, H=H, dk=d, dv=d, dtype=torch.bfloat16, gate_mode=I.GATE_SAFE,
+                   conv_state_std=1.0, seed=13)
+    print(f"prep over N={w.N} sequences, T={w.T}", flush=True)
+    dm = K.Dims(H, d, d, torch.bfloat16)
+    wd = w.to("cuda")
+    T = w.T
+    f = lambda *s: torch.empty(*s, device="cuda")
+    out = dict(q_hat=f(T, H, d), k_hat=f(T, H, d), v=f(T, H, d), g=f(T, H, d), beta=f(T, H))
+    cs = torch.empty_like(wd.conv_state0)
+    K.kda_prep(dm, wd.cu_seqlens, wd.q, wd.k, wd.v, wd.conv_w, wd.conv_state0, cs, wd.g, wd.beta, w.gate_mode,
+               w.lower_bound, out["q_hat"], out["k_hat"], out["v"], out["g"], out["beta"])
+    torch.cuda.synchronize()
+    ref = O.prep(w.f64("q"), w.f64("k"), w.f64("v"), w.f64("conv_w"), w.f64("conv_state0"), w.f64("g"),
+                 w.f64("beta"), w.cu_seqlens.numpy(), gate_mode=w.gate_mode, lower_bound=w.lower_bound)
+    assert np.array_equal(cs.cpu().double().numpy(), ref.conv_state)
+    for name, r in (("q_hat", ref.q_hat), ("k_hat", ref.k_hat), ("v", ref.v), ("g", ref.g), ("beta", ref.beta)):
+        assert rel(out[name], r) < 2e-6, name

@@ -2,14 +2,16 @@
 on the caller's stream (no allocation, no host synchronisation, no memset), so a
 captured decode step, verify window or prompt pass replays with the bits of the
 eager call.  Each graph is replayed several times, with eager work of the
-library on other buffers between the replays, and every replay is checked."""
+library on other buffers between the replays, and every replay is checked bit
+for bit against the eager call and against the fp64 oracle."""
+import numpy as np
 import pytest
 import torch
 
 import kimi_delta_attention_prep_amd as K
 from kimi_delta_attention_prep_amd import inputs as I
 
-from helpers import EPS, dims_for, raw_rows
+from helpers import EPS, TOL_BF16, dims_for, oracle_layer, oracle_pieces, raw_rows, rel
 
 pytestmark = pytest.mark.gpu
 
@@ -67,6 +69,7 @@ def test_decode_steps_replay_from_a_graph(B):
     st_g, cs_g = st0.clone(), cs0.clone()
     o_g = torch.empty_like(o_e)
     g = _capture(lambda: run(st_g, cs_g, o_g))
+    ref = oracle_layer(w)  # row s of every sequence at step s
     for r in range(REPLAYS):
         st_g.copy_(st0)
         cs_g.copy_(cs0)
@@ -77,6 +80,9 @@ def test_decode_steps_replay_from_a_graph(B):
         assert torch.equal(o_g, o_e), f"replay {r}: o"
         assert torch.equal(st_g, st_e), f"replay {r}: state"
         assert torch.equal(cs_g, cs_e), f"replay {r}: conv state"
+        assert rel(o_g.transpose(0, 1).reshape(w.T, H, w.dv), ref.o) < TOL_BF16, f"replay {r}: o vs oracle"
+        assert rel(st_g, ref.state) < TOL_BF16, f"replay {r}: state vs oracle"
+        assert np.array_equal(cs_g.cpu().double().numpy(), ref.prep.conv_state), f"replay {r}: conv state vs oracle"
 
 
 def test_verify_window_and_commit_replay_from_a_graph():
@@ -101,6 +107,8 @@ def test_verify_window_and_commit_replay_from_a_graph():
     st_g, cs_g, log_g = st0.clone(), cs0.clone(), K.VerifyLog.empty(d, B, W)
     o_g = torch.empty_like(o_e)
     g = _capture(lambda: run(st_g, cs_g, log_g, o_g))
+    ref = oracle_layer(w, with_log=True)  # the whole window of every sequence from S0
+    kept = oracle_pieces(w, [range(b * W, b * W + int(n_commit[b])) for b in range(B)])
     for r in range(REPLAYS):
         st_g.copy_(st0)
         cs_g.copy_(cs0)
@@ -112,6 +120,11 @@ def test_verify_window_and_commit_replay_from_a_graph():
         assert torch.equal(st_g, st_e) and torch.equal(cs_g, cs_e), f"replay {r}: committed state"
         for n in ("a", "k_hat", "u", "conv_rows"):
             assert torch.equal(getattr(log_g, n), getattr(log_e, n)), f"replay {r}: log {n}"
+        assert rel(o_g.reshape(w.T, H, w.dv), ref.o) < TOL_BF16, f"replay {r}: o vs oracle"
+        assert rel(log_g.u.reshape(w.T, H, w.dv), ref.log_u) < TOL_BF16, f"replay {r}: logged update vs oracle"
+        assert rel(log_g.a.reshape(w.T, H, w.dk), ref.log_a) < 1e-6, f"replay {r}: logged decay vs oracle"
+        assert rel(st_g, kept.state) < TOL_BF16, f"replay {r}: committed state vs oracle"
+        assert np.array_equal(cs_g.cpu().double().numpy(), kept.prep.conv_state), f"replay {r}: conv state vs oracle"
 
 
 def test_prompt_pass_replays_from_a_graph():
@@ -131,6 +144,7 @@ def test_prompt_pass_replays_from_a_graph():
     run(*e)
     gbuf = mk()
     g = _capture(lambda: run(*gbuf))
+    ref = oracle_layer(w)
     for r in range(REPLAYS):
         gbuf[0].copy_(wd.state0)
         gbuf[2].fill_(float("nan"))
@@ -139,3 +153,6 @@ def test_prompt_pass_replays_from_a_graph():
         torch.cuda.synchronize()
         for a, b, n in zip(gbuf, e, ("state", "conv state", "o", "y")):
             assert torch.equal(a, b), f"replay {r}: {n}"
+        errs = {"state": rel(gbuf[0], ref.state), "o": rel(gbuf[2], ref.o), "y": rel(gbuf[3].float(), ref.y)}
+        assert all(x < TOL_BF16 for x in errs.values()), f"replay {r}: {errs}"
+        assert np.array_equal(gbuf[1].cpu().double().numpy(), ref.prep.conv_state), f"replay {r}: conv state"

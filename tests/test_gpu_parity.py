@@ -11,7 +11,7 @@ from kimi_delta_attention_prep_amd import inputs as I
 from oracle import oracle as O
 
 from helpers import (EPS, TOL_BF16, TOL_FP32, dims_for, gpu_decode_steps, gpu_layer_prefill, gpu_prep, raw_rows,
-                     oracle_layer, rel, tol_for)
+                     oracle_layer, oracle_pieces, rel, tol_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -43,7 +43,9 @@ def test_gated_rmsnorm(dv, zdt, ydt):
     y = torch.empty(rows, dv, dtype=ydt, device="cuda")
     K.gated_rmsnorm_out(o.cuda(), z.cuda(), w.cuda(), EPS, y)
     ref = O.gated_rmsnorm(o.double().numpy(), z.double().numpy(), w.double().numpy(), EPS)
-    assert rel(y, ref) < (4e-3 if ydt == torch.bfloat16 else 2e-6)
+    # a bf16 y carries its own rounding, at most 2^-9 of each value (round to nearest even with 8
+    # significant bits), so its relative L2 error is at most 2^-9 plus that of the fp32 arithmetic
+    assert rel(y, ref) < (2.0 ** -9 + 2e-6 if ydt == torch.bfloat16 else 2e-6)
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
@@ -213,6 +215,18 @@ def test_verify_window_with_per_sequence_lengths():
     torch.cuda.synchronize()
     assert torch.equal(st, st_d)
     assert torch.equal(cs, cs_d)
+    # the fp64 oracle: sequence b's rows are the first lens[b] rows of its window run from S0, and the
+    # committed state is the oracle's after the first keep[b] rows
+    ref = oracle_layer(w, with_log=True)
+    ran = [b * W + r for b in range(B) for r in range(int(lens[b]))]
+    got = lambda t: torch.cat([t[b, :int(lens[b])] for b in range(B)])
+    assert rel(got(o), ref.o[ran]) < TOL_BF16
+    assert rel(got(log.a), ref.log_a[ran]) < 1e-6
+    assert rel(got(log.k_hat), ref.log_k[ran]) < 1e-5
+    assert rel(got(log.u), ref.log_u[ran]) < TOL_BF16
+    kept = oracle_pieces(w, [range(b * W, b * W + int(keep[b])) for b in range(B)])
+    assert rel(st, kept.state) < TOL_BF16
+    assert np.array_equal(cs.cpu().double().numpy(), kept.prep.conv_state)
 
 
 def test_verify_commit_and_next_window_in_one_call():
@@ -298,8 +312,11 @@ def test_prefill_many_ragged_sequences(dk, dv, precision, fused):
     assert np.array_equal(r["prep"]["conv_state"].cpu().double().numpy(), ref.prep.conv_state)
     # every sequence on its own, including the ones that start with an empty prompt
     st = r["state"].cpu().double().numpy()
+    per_seq = [rel(st[n], ref.state[n]) for n in range(w.N)]
+    worst = int(np.argmax(per_seq))
+    print(f"worst per-sequence state rel-L2 {per_seq[worst]:.2e} (sequence {worst}, length {lens[worst]})", flush=True)
     for n in range(w.N):
-        assert rel(st[n], ref.state[n]) < 4 * TOL_BF16, f"sequence {n} (length {lens[n]})"
+        assert per_seq[n] < TOL_BF16, f"sequence {n} (length {lens[n]})"
 
 
 @pytest.mark.parametrize("precision", [K.PREC_FP32, K.PREC_BF16X3, K.PREC_FP16])
@@ -357,8 +374,9 @@ def test_prefill_steep_decay_takes_exact_path():
     r = gpu_layer_prefill(w)
     ref = oracle_layer(w)
     assert np.all(np.isfinite(r["o"].cpu().numpy()))
-    assert rel(r["o"], ref.o) < 1e-4
-    assert rel(r["state"], ref.state) < 1e-4
+    errs = {"o": rel(r["o"], ref.o), "state": rel(r["state"], ref.state)}
+    print("steep decay, exact path:", errs, flush=True)
+    assert all(e < TOL_FP32 for e in errs.values()), errs
 
 
 @pytest.mark.parametrize("boundary", [20.0, 10.0])
@@ -376,8 +394,9 @@ def test_prefill_steep_gate_on_block_first_rows(boundary):
     r = gpu_layer_prefill(w)
     ref = oracle_layer(w)
     assert np.all(np.isfinite(r["o"].cpu().numpy()))
-    assert rel(r["o"], ref.o) < 1e-4
-    assert rel(r["state"], ref.state) < 1e-4
+    errs = {"o": rel(r["o"], ref.o), "state": rel(r["state"], ref.state)}
+    print(errs, flush=True)
+    assert all(e < TOL_FP32 for e in errs.values()), errs
 
 
 @pytest.mark.parametrize("precision", [K.PREC_BF16X3, K.PREC_FP16])
