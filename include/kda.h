@@ -203,6 +203,28 @@ int kda_prefill_varlen(const kda_dims* d, int32_t num_seqs, int64_t t_tot, const
                        const float* g, const float* beta, const kda_raw_rows* raw, const kda_norm_args* norm,
                        float* state, float* o, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* kda_prefill_varlen_noalloc -- for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same call as kda_prefill_varlen (same arguments, kernels,
+ * bits and errors) without the workspace argument: the sink and the chunk
+ * records go to a scratch array the library holds in each device's memory,
+ * KDA_NOALLOC_SCRATCH_BYTES (160 MiB; T=4096 rows at H=16, d=128 fit under
+ * every precision policy), from the first use of the library on that device
+ * until the process ends.  The call itself allocates nothing.
+ *   Errors: KDA_E_WORKSPACE when kda_prefill_workspace_bytes() for the call's
+ *   geometry exceeds KDA_NOALLOC_SCRATCH_BYTES (nothing is enqueued);
+ *   KDA_E_HIP if the scratch's device address cannot be resolved (the first
+ *   call on each device resolves it, before any launch).
+ *   Sharing: every call on a device uses that device's one scratch, which keeps
+ *   the last call's contents (nothing in it has to start at zero).  Calls that
+ *   overlap on one device -- on two streams, or from two host threads without
+ *   ordering between their streams -- race on it; the caller orders them. */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)160 << 20)
+int kda_prefill_varlen_noalloc(const kda_dims* d, int32_t num_seqs, int64_t t_tot, const int32_t* cu_seqlens,
+                               const int32_t* slots, const float* q_hat, const float* k_hat, const float* v,
+                               const float* g, const float* beta, const kda_raw_rows* raw, const kda_norm_args* norm,
+                               float* state, float* o, hipStream_t stream);
+
 /* kda_decode -- one row per sequence (parts 1-4 fused): conv step on the conv
  * state, gates, norms, state step, readout.
  *   q_raw,k_raw,g_raw [batch,H,d_k], v_raw [batch,H,d_v], beta_logit [batch,H]  (in_dtype)

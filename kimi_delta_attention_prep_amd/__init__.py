@@ -29,8 +29,9 @@ GATE_SOFTPLUS, GATE_SAFE = 0, 1
 ACT_NONE, ACT_SILU = 0, 1
 PREC_FP32, PREC_BF16X3, PREC_FP16 = 0, 1, 2
 DECAY_PER_DIM, DECAY_PER_HEAD = 0, 1
-EXPORTS = ("kda_prep", "kda_prefill_workspace_bytes", "kda_prefill_varlen", "kda_decode", "kda_verify_window",
-           "gated_rmsnorm_out", "kda_last_error", "kda_set_timing_events")
+EXPORTS = ("kda_prep", "kda_prefill_workspace_bytes", "kda_prefill_varlen", "kda_prefill_varlen_noalloc",
+           "kda_decode", "kda_verify_window", "gated_rmsnorm_out", "kda_last_error", "kda_set_timing_events")
+NOALLOC_SCRATCH_BYTES = 160 << 20  # KDA_NOALLOC_SCRATCH_BYTES
 
 
 class KdaError(RuntimeError):
@@ -80,14 +81,17 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.kda_prefill_workspace_bytes.restype = ctypes.c_size_t
         lib.kda_prefill_varlen.argtypes = [D, i32, i64, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(KdaRawRows),
                                            ctypes.POINTER(KdaNormArgs), vp, vp, vp, ctypes.c_size_t, vp]
+        lib.kda_prefill_varlen_noalloc.argtypes = [D, i32, i64, vp, vp, vp, vp, vp, vp, vp,
+                                                   ctypes.POINTER(KdaRawRows), ctypes.POINTER(KdaNormArgs), vp, vp,
+                                                   vp]
         lib.kda_decode.argtypes = [D, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp]
         lib.kda_verify_window.argtypes = [D, i32, i32, vp, vp, vp, vp, vp, vp, Lg, Lg, vp, vp, vp, vp, vp, i32, f32, vp,
                                           vp]
         lib.gated_rmsnorm_out.argtypes = [i64, i32, vp, vp, i32, vp, f32, vp, i32, vp]
         lib.kda_last_error.restype = ctypes.c_char_p
         lib.kda_set_timing_events.argtypes = [vp, i32]
-        for f in ("kda_prep", "kda_prefill_varlen", "kda_decode", "kda_verify_window", "gated_rmsnorm_out",
-                  "kda_set_timing_events"):
+        for f in ("kda_prep", "kda_prefill_varlen", "kda_prefill_varlen_noalloc", "kda_decode", "kda_verify_window",
+                  "gated_rmsnorm_out", "kda_set_timing_events"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -257,11 +261,20 @@ def kda_prefill_workspace_bytes(d: Dims, num_seqs: int, t_tot: int) -> int:
     return int(load_library().kda_prefill_workspace_bytes(ctypes.byref(dims), int(num_seqs), int(t_tot)))
 
 
+def kda_prefill_varlen_noalloc(d: Dims, cu_seqlens, q_hat, k_hat, v, g, beta, state, o, slots=None, raw=None,
+                               norm=None):
+    """kda_prefill_varlen without a workspace: the chunk records go to the library's per-device scratch
+    (NOALLOC_SCRATCH_BYTES), for callers that cannot allocate device memory.  Calls that overlap on one device
+    race on that scratch."""
+    kda_prefill_varlen(d, cu_seqlens, q_hat, k_hat, v, g, beta, state, o, None, slots=slots, raw=raw, norm=norm)
+
+
 def kda_prefill_varlen(d: Dims, cu_seqlens, q_hat, k_hat, v, g, beta, state, o, workspace, slots=None, raw=None,
                        norm=None):
     """Chunked prompt pass.  With raw=dict(q_raw, k_raw, v_raw, g_raw, beta_logit, conv_weight, conv_state_in,
     conv_state_out, gate_mode, lower_bound) the preamble runs inside the prompt kernels and q_hat..beta may be None.
-    With norm=dict(z, weight, eps, y) the gated output norm runs as the call's epilogue (y as gated_rmsnorm_out)."""
+    With norm=dict(z, weight, eps, y) the gated output norm runs as the call's epilogue (y as gated_rmsnorm_out).
+    workspace=None calls kda_prefill_varlen_noalloc instead."""
     lib = load_library()
     H, dk, dv = d.num_heads, d.head_dim_k, d.head_dim_v
     _validate([("cu_seqlens", cu_seqlens, torch.int32, (None,))], device=False)
@@ -283,7 +296,9 @@ def kda_prefill_varlen(d: Dims, cu_seqlens, q_hat, k_hat, v, g, beta, state, o, 
                   ("conv_state_in", raw["conv_state_in"], dt, (None, 3, d.conv_channels))]
         specs.append(("conv_state_out", raw["conv_state_out"], dt, tuple(raw["conv_state_in"].shape)))
     specs += [("cu_seqlens", cu_seqlens, None, None), ("o", o, torch.float32, (T, H, dv)),
-              ("state", state, torch.float32, (None, H, dk, dv)), ("workspace", workspace, None, None)]
+              ("state", state, torch.float32, (None, H, dk, dv))]
+    if workspace is not None:
+        specs.append(("workspace", workspace, None, None))
     if norm is not None:
         specs += [("z", norm["z"], None, (T, H, dv)), ("weight", norm["weight"], torch.float32, (dv,)),
                   ("y", norm["y"], None, (T, H, dv))]
@@ -305,10 +320,14 @@ def kda_prefill_varlen(d: Dims, cu_seqlens, q_hat, k_hat, v, g, beta, state, o, 
         if slots is not None:
             _debug_slots(slots, pools)
     dims = d.c()
-    _check(lib.kda_prefill_varlen(ctypes.byref(dims), N, T, _ptr(cu_seqlens), _ptr(slots), _ptr(q_hat), _ptr(k_hat),
-                                  _ptr(v), _ptr(g), _ptr(beta), ctypes.byref(rr) if rr is not None else None,
-                                  ctypes.byref(nn) if nn is not None else None, _ptr(state), _ptr(o), _ptr(workspace),
-                                  workspace.numel() * workspace.element_size(), _stream()))
+    common = (ctypes.byref(dims), N, T, _ptr(cu_seqlens), _ptr(slots), _ptr(q_hat), _ptr(k_hat), _ptr(v), _ptr(g),
+              _ptr(beta), ctypes.byref(rr) if rr is not None else None, ctypes.byref(nn) if nn is not None else None,
+              _ptr(state), _ptr(o))
+    if workspace is None:
+        _check(lib.kda_prefill_varlen_noalloc(*common, _stream()))
+    else:
+        _check(lib.kda_prefill_varlen(*common, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream()))
 
 
 def kda_decode(d: Dims, state, conv_state, conv_weight, q_raw, k_raw, v_raw, g_raw, beta_logit, gate_mode,

@@ -126,6 +126,8 @@ hipError_t ensure_dynamic_lds(const void* kernel, size_t bytes) {
   return e;
 }
 
+static_assert(kNoAllocScratchBytes == KDA_NOALLOC_SCRATCH_BYTES, "scratch size as the header states it");
+
 }  // namespace kda
 
 extern "C" {
@@ -174,51 +176,61 @@ size_t kda_prefill_workspace_bytes(const kda_dims* d, int32_t num_seqs, int64_t 
   return kda::prefill_workspace_bytes(d->num_heads, d->head_dim_k, d->head_dim_v, d->precision, num_seqs, t_tot);
 }
 
-int kda_prefill_varlen(const kda_dims* d, int32_t num_seqs, int64_t t_tot, const int32_t* cu_seqlens,
-                       const int32_t* slots, const float* q_hat, const float* k_hat, const float* v,
-                       const float* g, const float* beta, const kda_raw_rows* raw, const kda_norm_args* norm,
-                       float* state, float* o, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// kda_prefill_varlen and its allocation-free variant: the same validation and launches; the
+// variant takes the chunk records' scratch from the library's per-device array instead of the
+// caller's workspace (noalloc, with workspace NULL on entry).
+static int prefill_call(const char* fn, const kda_dims* d, int32_t num_seqs, int64_t t_tot, const int32_t* cu_seqlens,
+                        const int32_t* slots, const float* q_hat, const float* k_hat, const float* v, const float* g,
+                        const float* beta, const kda_raw_rows* raw, const kda_norm_args* norm, float* state, float* o,
+                        void* workspace, size_t workspace_bytes, bool noalloc, hipStream_t stream) {
   KDA_TRY(check_dims(d));
-  if (num_seqs < 0 || t_tot < 0) return fail(KDA_E_ARG, "kda_prefill_varlen: negative size");
-  KDA_TRY(check_rows("kda_prefill_varlen", d, num_seqs, t_tot));
+  if (num_seqs < 0 || t_tot < 0) return fail(KDA_E_ARG, "%s: negative size", fn);
+  KDA_TRY(check_rows(fn, d, num_seqs, t_tot));
   if (norm) {
     if ((norm->z_dtype != KDA_DTYPE_F32 && norm->z_dtype != KDA_DTYPE_BF16) ||
         (norm->y_dtype != KDA_DTYPE_F32 && norm->y_dtype != KDA_DTYPE_BF16))
-      return fail(KDA_E_DTYPE, "kda_prefill_varlen: unknown norm z or y dtype");
+      return fail(KDA_E_DTYPE, "%s: unknown norm z or y dtype", fn);
     if (!(norm->eps >= 0.0f) || !std::isfinite(norm->eps))
-      return fail(KDA_E_ARG, "kda_prefill_varlen: norm eps must be finite and >= 0");
-    if (t_tot > 0) KDA_TRY(check_ptrs("kda_prefill_varlen: norm z/weight/y", {norm->z, norm->weight, norm->y}));
+      return fail(KDA_E_ARG, "%s: norm eps must be finite and >= 0", fn);
+    if (t_tot > 0) KDA_TRY(check_ptrs("prompt call: norm z/weight/y", {norm->z, norm->weight, norm->y}));
   }
-  if (num_seqs == 0 && t_tot > 0) return fail(KDA_E_ARG, "kda_prefill_varlen: rows without sequences");
-  KDA_TRY(check_opt_ptr("kda_prefill_varlen: slots", slots));
+  if (num_seqs == 0 && t_tot > 0) return fail(KDA_E_ARG, "%s: rows without sequences", fn);
+  KDA_TRY(check_opt_ptr("prompt call: slots", slots));
   if (raw) KDA_TRY(check_gate(raw->gate_mode, raw->lower_bound));
   const unsigned eb = elem_bytes(d->in_dtype);
   if (num_seqs > 0) {
-    KDA_TRY(check_ptrs("kda_prefill_varlen: cu_seqlens", {cu_seqlens}, 4));
-    KDA_TRY(check_ptrs("kda_prefill_varlen: state", {state}));
+    KDA_TRY(check_ptrs("prompt call: cu_seqlens", {cu_seqlens}, 4));
+    KDA_TRY(check_ptrs("prompt call: state", {state}));
     if (raw) {
-      KDA_TRY(check_ptrs("kda_prefill_varlen: raw conv weight", {raw->conv_weight}, 4));
-      KDA_TRY(check_ptrs("kda_prefill_varlen: raw conv state", {raw->conv_state_in, raw->conv_state_out}, eb));
+      KDA_TRY(check_ptrs("prompt call: raw conv weight", {raw->conv_weight}, 4));
+      KDA_TRY(check_ptrs("prompt call: raw conv state", {raw->conv_state_in, raw->conv_state_out}, eb));
     }
   }
   if (t_tot > 0) {
     if (raw) {
-      KDA_TRY(check_ptrs("kda_prefill_varlen: raw q/k/v/g rows", {raw->q_raw, raw->k_raw, raw->v_raw, raw->g_raw}));
-      KDA_TRY(check_ptrs("kda_prefill_varlen: raw beta logits", {raw->beta_logit}, eb));
+      KDA_TRY(check_ptrs("prompt call: raw q/k/v/g rows", {raw->q_raw, raw->k_raw, raw->v_raw, raw->g_raw}));
+      KDA_TRY(check_ptrs("prompt call: raw beta logits", {raw->beta_logit}, eb));
     } else {
-      KDA_TRY(check_ptrs("kda_prefill_varlen", {q_hat, k_hat, v, g}));
-      KDA_TRY(check_ptrs("kda_prefill_varlen", {beta}, 4));
+      KDA_TRY(check_ptrs("prompt call", {q_hat, k_hat, v, g}));
+      KDA_TRY(check_ptrs("prompt call", {beta}, 4));
     }
-    KDA_TRY(check_ptrs("kda_prefill_varlen: o", {o}));
+    KDA_TRY(check_ptrs("prompt call: o", {o}));
   }
   const size_t need =
       kda::prefill_workspace_bytes(d->num_heads, d->head_dim_k, d->head_dim_v, d->precision, num_seqs, t_tot);
+  if (num_seqs > 0 && noalloc) {
+    if (need > kda::kNoAllocScratchBytes)
+      return fail(KDA_E_WORKSPACE, "%s: this call needs %zu bytes of scratch, more than the %zu the library holds "
+                  "per device; use kda_prefill_varlen with a workspace", fn, need, kda::kNoAllocScratchBytes);
+    KDA_TRY(hip_status(kda::noalloc_scratch(&workspace), fn));
+    workspace_bytes = kda::kNoAllocScratchBytes;
+  }
   if (num_seqs > 0) {
     if (!workspace || workspace_bytes < need)
-      return fail(KDA_E_WORKSPACE, "kda_prefill_varlen: workspace of %zu bytes needed, %zu given", need,
+      return fail(KDA_E_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                   workspace ? workspace_bytes : (size_t)0);
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-      return fail(KDA_E_ALIGN, "kda_prefill_varlen: workspace must be 256-byte aligned");
+      return fail(KDA_E_ALIGN, "%s: workspace must be 256-byte aligned", fn);
   }
   if (num_seqs == 0) return ok();
   kda::PrefillLaunch L{};
@@ -235,17 +247,33 @@ int kda_prefill_varlen(const kda_dims* d, int32_t num_seqs, int64_t t_tot, const
     L.raw_beta = raw->beta_logit; L.conv_w = raw->conv_weight; L.cs_in = raw->conv_state_in;
     L.cs_out = raw->conv_state_out;
   }
-  KDA_TRY(hip_status(kda::launch_prefill(L, stream), "kda_prefill_varlen"));
+  KDA_TRY(hip_status(kda::launch_prefill(L, stream), fn));
   if (norm && t_tot > 0) {
     kda::NormLaunch N{t_tot * d->num_heads, d->head_dim_v, norm->z_dtype, norm->y_dtype, o, norm->z, norm->weight,
                       norm->eps, norm->y};
     N.cu = cu_seqlens; N.slots = slots; N.num_seqs = num_seqs; N.H = d->num_heads;
     const bool timed = g_nevents >= 6;
-    if (timed) KDA_TRY(hip_status(hipEventRecord(g_events[4], stream), "kda_prefill_varlen"));
-    KDA_TRY(hip_status(kda::launch_gated_rmsnorm(N, stream), "kda_prefill_varlen: norm"));
-    if (timed) KDA_TRY(hip_status(hipEventRecord(g_events[5], stream), "kda_prefill_varlen"));
+    if (timed) KDA_TRY(hip_status(hipEventRecord(g_events[4], stream), fn));
+    KDA_TRY(hip_status(kda::launch_gated_rmsnorm(N, stream), fn));
+    if (timed) KDA_TRY(hip_status(hipEventRecord(g_events[5], stream), fn));
   }
   return ok();
+}
+
+int kda_prefill_varlen(const kda_dims* d, int32_t num_seqs, int64_t t_tot, const int32_t* cu_seqlens,
+                       const int32_t* slots, const float* q_hat, const float* k_hat, const float* v,
+                       const float* g, const float* beta, const kda_raw_rows* raw, const kda_norm_args* norm,
+                       float* state, float* o, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return prefill_call("kda_prefill_varlen", d, num_seqs, t_tot, cu_seqlens, slots, q_hat, k_hat, v, g, beta, raw,
+                      norm, state, o, workspace, workspace_bytes, false, stream);
+}
+
+int kda_prefill_varlen_noalloc(const kda_dims* d, int32_t num_seqs, int64_t t_tot, const int32_t* cu_seqlens,
+                               const int32_t* slots, const float* q_hat, const float* k_hat, const float* v,
+                               const float* g, const float* beta, const kda_raw_rows* raw, const kda_norm_args* norm,
+                               float* state, float* o, hipStream_t stream) {
+  return prefill_call("kda_prefill_varlen_noalloc", d, num_seqs, t_tot, cu_seqlens, slots, q_hat, k_hat, v, g, beta,
+                      raw, norm, state, o, nullptr, 0, true, stream);
 }
 
 int kda_decode(const kda_dims* d, int32_t batch, const int32_t* slots, float* state, void* conv_state,

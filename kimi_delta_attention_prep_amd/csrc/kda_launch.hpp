@@ -88,4 +88,10 @@ struct PrefillLaunch {
 size_t prefill_workspace_bytes(int H, int dk, int dv, int precision, int num_seqs, int64_t t_tot);
 hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t s);
 
+// Scratch of the allocation-free prompt call: a device array of this many bytes, one per
+// device; noalloc_scratch gives its address on the calling thread's current device
+// (resolved on the first call on each device and kept for the life of the process).
+constexpr size_t kNoAllocScratchBytes = (size_t)160 << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace kda

@@ -35,6 +35,8 @@
 //   BF16X3  operands split into bf16 hi + lo, hi*hi + hi*lo + lo*hi
 //   FP16    A operands (W, Q^gamma, P, K_<^T: every entry bounded by 1) rounded
 //           once to fp16; B operands (state, U) split into fp16 hi + lo
+#include <mutex>
+
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -313,6 +315,33 @@ constexpr size_t kSinkBytes = 1024;
 size_t prefill_workspace_bytes(int H, int dk, int dv, int precision, int num_seqs, int64_t t_tot) {
   const RecLayout rl = rec_layout(dk, dv, frag_bytes(precision));
   return kSinkBytes + (size_t)max_chunks(num_seqs, t_tot) * H * (size_t)rl.bytes;
+}
+
+// The allocation-free prompt call's workspace: the sink and the chunk records live here instead of in
+// a caller buffer.  Nothing in it has to start at zero (every record the scan reads is written by the
+// intra-chunk kernel of the same call, and the sink is never read), so no call clears it.  Host code
+// never passes this array's name to a kernel: its host-side symbol is not the device address.  Each
+// device's address comes from hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 // raw rows and preamble parameters when the preamble runs inside the prompt kernels

@@ -271,3 +271,17 @@ def test_binding_rejects_wrong_shapes_before_any_launch(lib):
                              torch.zeros(16, dtype=torch.uint8), raw=raw)
     with pytest.raises(ValueError, match="y must have shape"):
         K.gated_rmsnorm_out(f(T, dv), bf(T, dv), f(dv), 1e-6, f(T, dv + 1))
+
+
+def test_noalloc_prompt_call_checks(lib):
+    """The allocation-free prompt call validates like kda_prefill_varlen, and refuses a geometry whose records
+    exceed the library's scratch before resolving or touching it."""
+    d = dims()
+    call = lambda N, T, o=A: lib.kda_prefill_varlen_noalloc(ctypes.byref(d), N, T, A, None, A, A, A, A, A, None, None,
+                                                            A, o, None)
+    assert lib.kda_prefill_workspace_bytes(ctypes.byref(d), 8, 40000) > K.NOALLOC_SCRATCH_BYTES
+    assert call(8, 40000) == K.KDA_E_WORKSPACE
+    assert b"scratch" in lib.kda_last_error()
+    assert call(2, 1000, MIS4) == K.KDA_E_ALIGN  # o is written with 16-byte stores
+    assert call(-1, 10) == K.KDA_E_ARG
+    assert call(0, 0) == K.KDA_OK  # nothing to do, nothing launched
