@@ -1383,12 +1383,15 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillArgs p, int grou
       typename F::B bs[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) bs[kb] = get_s(kb);
-      floatx4 acc[2] = {z4, z4};
+      // one accumulator per K block (chains of one block's products), summed as a tree
+      floatx4 acc[KB];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) acc[kb & 1] = F::mma(acc[kb & 1], cur.w[kb], bs[kb]);
+      for (int kb = 0; kb < KB; ++kb) acc[kb] = F::mma(z4, cur.w[kb], bs[kb]);
+      floatx4 ws = acc[0] + acc[1];
+      if constexpr (KB == 4) ws = ws + (acc[2] + acc[3]);
       floatx4 u;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) u[v] = cur.ut[v] - (acc[0][v] + acc[1][v]);
+      for (int v = 0; v < 4; ++v) u[v] = cur.ut[v] - ws[v];
       put_u(16 * w4 + 4 * g4, u);
       __builtin_amdgcn_sched_barrier(0);
       ahead.load_ug(nrec, rl, w4, lane, split);
@@ -1442,9 +1445,14 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillArgs p, int grou
       typename F::B bs[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) bs[kb] = get_s(kb);
-      floatx4 ao[2] = {z4, z4};
+      floatx4 aq[KB];  // one accumulator per K block, summed in pairs
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) ao[kb & 1] = F::mma_t(ao[kb & 1], bs[kb], cur.q[kb]);
+      for (int kb = 0; kb < KB; ++kb) aq[kb] = F::mma_t(z4, bs[kb], cur.q[kb]);
+      floatx4 ao[2] = {aq[0], aq[1]};
+      if constexpr (KB == 4) {
+        ao[0] = ao[0] + aq[2];
+        ao[1] = ao[1] + aq[3];
+      }
       __syncthreads();  // B
       const typename F::B u0 = get_u(0);
       ao[0] = F::mma_t(ao[0], u0, cur.pp[0]);
