@@ -165,6 +165,19 @@ struct Frag<POL_BF16X3> {
     *reinterpret_cast<bf16x8*>(p) = b.hi;
     *reinterpret_cast<bf16x8*>(p + 16) = b.lo;
   }
+  // elements 4 half .. 4 half + 3 of an A fragment (two lanes write one fragment)
+  __device__ static void store_a_half(uint8_t* p, int half, const float (&x)[4]) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    bf16x4 h, l;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      __bf16 a, b;
+      split_bf16(x[e], a, b);
+      h[e] = a; l[e] = b;
+    }
+    *reinterpret_cast<bf16x4*>(p + 8 * half) = h;
+    *reinterpret_cast<bf16x4*>(p + 16 + 8 * half) = l;
+  }
   __device__ static floatx4 mma(floatx4 acc, const A& a, const B& b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, acc, 0, 0, 0);
@@ -214,6 +227,14 @@ struct Frag<POL_FP16> {
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = static_cast<_Float16>(x[e]);
     *reinterpret_cast<f16x8*>(p) = v;
+  }
+  // elements 4 half .. 4 half + 3 of an A fragment (two lanes write one fragment)
+  __device__ static void store_a_half(uint8_t* p, int half, const float (&x)[4]) {
+    typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+    f16x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = static_cast<_Float16>(x[e]);
+    *reinterpret_cast<f16x4*>(p + 8 * half) = v;
   }
   __device__ static B make_b(const float (&x)[8]) {
     B b;
@@ -635,8 +656,8 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
   };
   const bool seq_first = start == t0;  // uniform over the workgroup
   // Fused: the v rows are loaded with the preamble's rows and land long before step 7
-  // (staged over A there where they fit; fp32 rows read their taps from HBM)
-  constexpr bool kVStaged = FUSED && (L + 3) * DV * sizeof(RawT) <= (size_t)L * PL * sizeof(float);
+  // (staged over T1 there where they fit; fp32 rows read their taps from HBM)
+  constexpr bool kVStaged = FUSED && (L + 3) * DV * sizeof(RawT) <= (size_t)L * PK * sizeof(float);
   constexpr int NSV = kVStaged ? ((L + 3) * (DV / VE) + NT - 1) / NT : 1;
   const int64_t chv = 2 * (int64_t)H * DK + (int64_t)h * DV;
   uint4 xv[NSV];
@@ -881,6 +902,12 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
   //    k e^{T_I - gl} = (k e^{-gl}) e^{T_I}, one product.
   if (!exact) {
     float* sRk = sA;  // [48][PK] k e^{T_I - gl}, over the A and P tiles until the products are done
+    // With record fragments of 8 consecutive key dims (fp16 and split-bf16 records), the two
+    // lanes that hold the 4-dim halves of a group write its Q^gamma = e^{G_{16R}} (q e^{gl})
+    // fragment from their registers, half each; fp32 records (strided K order) go through the
+    // factor tile later.
+    using FR = Frag<POL>;
+    constexpr bool kQfDirect = FR::kof(1, 0) == 8;
     for (int idx = t; idx < L * (DK / 4); idx += NT) {
       const int r = idx / (DK / 4), d4 = 4 * (idx % (DK / 4));
       const float4 kk = *reinterpret_cast<const float4*>(&sK[r * PK + d4]);
@@ -902,14 +929,14 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
       FT::store4(sQ, r, d4, lq);
       FT::store4(sG, r, d4, rd);
       if (r < 48) FT::store4(sRk, r, d4, rk);
+      if constexpr (kQfDirect) {  // A fragment (row tile r / 16, K block d4 / 32), lane (r % 16) + 16 (d4 % 32) / 8
+        const float4 gf = *reinterpret_cast<const float4*>(&sGFe[(r >> 4) * DK + d4]);
+        const float qf[4] = {gf.x * lq[0], gf.y * lq[1], gf.z * lq[2], gf.w * lq[3]};
+        const int item = ((r >> 4) * (DK / 32) + (d4 >> 5)) * 64 + (r & 15) + 16 * ((d4 & 31) >> 3);
+        FR::store_a_half(rec + rl.Qf + (size_t)item * FR::BYTES, (d4 >> 2) & 1, qf);
+      }
     }
     __syncthreads();
-    write_afrags<POL, NT>(rec + rl.Qf, 4, DK / 32, [&](int r, int d) {
-      return sGFe[(r / 16) * DK + d] * FT::load1(sQ, r, d);
-    });
-    write_afrags<POL, NT>(rec + rl.Kf, DK / 16, 2, [&](int d, int r) {
-      return sXe[(r / 16) * DK + d] * FT::load1(r < 48 ? sRk : sG, r, d);
-    });
     constexpr int NJ = (10 + NW - 1) / NW;  // block pairs per wavefront
     // pair indices in order (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3);
     // the three that carry a scale, (2,0) (3,0) (3,1), go to wavefronts 0..2
@@ -930,6 +957,30 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
         pair_mma<IP, DK, PK>(acc[j][0], acc[j][1], &sK[16 * R * PK], &sQ[16 * R * PK], right, scale);
       }
     }
+    // the record's K_<^T (and, for fp32 records, Q^gamma) fragments from the same factors,
+    // while the products run
+    if constexpr (!kQfDirect)
+      write_afrags<POL, NT>(rec + rl.Qf, 4, DK / 32, [&](int r, int d) {
+        return sGFe[(r / 16) * DK + d] * FT::load1(sQ, r, d);
+      });
+    if constexpr (kQfDirect) {
+      // an item's 8 chunk rows r0 .. r0 + 7 lie in one 16-row block: its factor e^{G_last - G_16I}
+      // and its source tile are taken once
+      for (int item = t; item < (DK / 16) * 2 * 64; item += NT) {
+        const int ln = item & 63, blk = item >> 6;
+        const int d = 16 * (blk >> 1) + (ln & 15), r0 = 32 * (blk & 1) + 8 * (ln >> 4), R = r0 >> 4;
+        const float* src = R < 3 ? sRk : sG;
+        const float xe = sXe[R * DK + d];
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = xe * FT::load1(src, r0 + e, d);
+        FR::store_a(rec + rl.Kf + (size_t)item * FR::BYTES, x);
+      }
+    } else {
+      write_afrags<POL, NT>(rec + rl.Kf, DK / 16, 2, [&](int d, int r) {
+        return sXe[(r / 16) * DK + d] * FT::load1(r < 48 ? sRk : sG, r, d);
+      });
+    }
     __syncthreads();  // every wavefront is done with the factors over A and P
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
@@ -946,9 +997,11 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
         }
       }
     }
-    for (int idx = t; idx < L * L; idx += NT) {  // strictly-upper blocks are zero
-      const int rr = idx / L, ii = idx % L;
-      if ((ii >> 4) > (rr >> 4)) { sA[rr * PL + ii] = 0.f; sP[rr * PL + ii] = 0.f; }
+    // P's strictly-upper blocks (0,1) (0,2) (0,3) (1,2) (1,3) (2,3) are zero in its record
+    // fragments; A's are never read (the solve reads its diagonal and lower blocks only)
+    for (int idx = t; idx < 6 * 256; idx += NT) {
+      const int b = idx >> 8, R = b < 3 ? 0 : b < 5 ? 1 : 2, I = b < 3 ? b + 1 : b < 5 ? b - 1 : 3;
+      sP[(16 * R + ((idx >> 4) & 15)) * PL + 16 * I + (idx & 15)] = 0.f;
     }
   } else {
     // exact path: every pair (r, i <= r) with one exponential of G_r - G_i per key dim, the
@@ -979,126 +1032,17 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
       }
     }
   }
-  __syncthreads();
-  write_afrags<POL, NT>(rec + rl.Pf, 4, 2, [&](int r, int i) { return sP[r * PL + i]; });
-  __syncthreads();
-
-  // 6. X = (I + A)^{-1} into the P tile
-  float* sXi = sP;
-  for (int idx = t; idx < L * L; idx += NT) sXi[(idx / L) * PL + idx % L] = 0.f;
-  __syncthreads();
-  if (wave < 4) {  // diagonal block R = wavefront, by forward substitution
-    // lane 4 cc + qq owns column cc, rows 4 qq .. 4 qq + 3 of the block.  Right-looking:
-    // once x_r is final it is broadcast in the lane quad and every later row takes its
-    // term, in the order r = 0, 1, ... (rows at or above r see a zero of A's strictly
-    // lower block and keep their value).
-    const int R = wave, b0 = 16 * R, cc = lane >> 2, qq = lane & 3;
-    float xv[4];
+  // the v rows for step 7 go to T1, which nothing reads any more: fused, the staged raw rows
+  // (16-byte pieces, loaded with the preamble's rows); unfused, the rows b_r v_r in fp32
+  if constexpr (kVStaged) {
+    static_assert((L + 3) * DV * sizeof(RawT) <= (size_t)L * PK * sizeof(float), "staged v rows fit in T1");
+    RawT* stv = reinterpret_cast<RawT*>(sQ);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xv[j] = (4 * qq + j == cc) ? 1.f : 0.f;
+    for (int i = 0; i < NSV; ++i) store_staged(stv, DV, t + i * NT, xv[i]);
+    if (seq_first)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      constexpr int kQuad[4] = {0x00, 0x55, 0xAA, 0xFF};  // quad_perm broadcast of lane 0..3 of each quad
-      float x = xv[r & 3];
-      if ((r >> 2) == 0) x = dpp_partner<kQuad[0]>(x);
-      else if ((r >> 2) == 1) x = dpp_partner<kQuad[1]>(x);
-      else if ((r >> 2) == 2) x = dpp_partner<kQuad[2]>(x);
-      else x = dpp_partner<kQuad[3]>(x);
-      x = (r >= cc) ? x : 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) xv[j] = fmaf(-sA[(b0 + 4 * qq + j) * PL + b0 + r], x, xv[j]);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sXi[(b0 + 4 * qq + j) * PL + b0 + cc] = xv[j];
-  }
-  __syncthreads();  // X_RR of every diagonal block is complete: block (R, I) reads it from wavefront R
-  // off-diagonal blocks, nearest diagonals first, one wavefront per block on the matrix cores (fp32):
-  //   Y = sum_{J=I}^{R-1} A_RJ X_JI,  X_RI = -X_RR Y
-  for (int dist = 1; dist < 4; ++dist) {
-    if (wave < 4 - dist) {
-      const int I = wave, R = I + dist, col = lane & 15, g4 = lane >> 4;
-      floatx4 y = {0.f, 0.f, 0.f, 0.f};
-      for (int k0 = 16 * I; k0 < 16 * R; k0 += 4)
-        y = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[(16 * R + col) * PL + k0 + g4], sXi[(k0 + g4) * PL + 16 * I + col],
-                                                 y, 0, 0, 0);
-      float* yb = sY + wave * 16 * 17;  // this wavefront's own scratch: written, then read back in order
-#pragma unroll
-      for (int v = 0; v < 4; ++v) yb[(4 * g4 + v) * 17 + col] = y[v];
-      floatx4 x = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k0 = 0; k0 < 16; k0 += 4)
-        x = __builtin_amdgcn_mfma_f32_16x16x4f32(sXi[(16 * R + col) * PL + 16 * R + k0 + g4], yb[(k0 + g4) * 17 + col],
-                                                 x, 0, 0, 0);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) sXi[(16 * R + 4 * g4 + v) * PL + 16 * I + col] = -x[v];
-    }
-    __syncthreads();
-  }
-
-  // 7. right-hand sides as B-operand fragments of the intra products:
-  //    b_r e^{G_r} k_r into T2, b_r v_r into T0 (through T1).  A fragment item is
-  //    (column tile c, 32-row block kb, lane): 8 rows of one column.  e^{G_r} k_r
-  //    is e^{G_{16R}} (k_r e^{gl_r}) from the factors of step 5, or formed
-  //    directly from the chunk prefix G_r on the exact path.
-  using FI = Frag<IP>;
-  using FB = typename FI::B;
-  constexpr int NFK = (DK / 16) * 2 * 64, PFK = (NFK + NT - 1) / NT;
-  constexpr int NFV = (DV / 16) * 2 * 64, PFV = (NFV + NT - 1) / NT;
-  {
-    FB fk[PFK];
-#pragma unroll
-    for (int i = 0; i < PFK; ++i) {
-      const int item = t + i * NT;
-      if (item < NFK) {
-        const int ln = item & 63, kb = (item >> 6) & 1, c = item >> 7;
-        const int d = 16 * c + (ln & 15), g = ln >> 4;
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = 32 * kb + FI::kof(g, e);
-          // exact path: T2 holds the chunk prefix G_r (its high part); else e^{G_{16R}} times the factor k e^{gl}
-          if (exact) x[e] = sBeta[r] * (sK[r * PK + d] * pexp<POL>(sG[r * PK + d]));
-          else x[e] = sBeta[r] * (FT::load1(sK, r, d) * sGFe[(r / 16) * DK + d]);
-        }
-        fk[i] = FI::make_b(x);
-      }
-    }
-    __syncthreads();  // every read of T2 is done
-#pragma unroll
-    for (int i = 0; i < PFK; ++i)
-      if (t + i * NT < NFK) put_frag(sG, NFK, t + i * NT, fk[i]);
-  }
-  if constexpr (FUSED) {
-    // v rows: conv (no norm), RW rows per wavefront side by side, b_r v_r into T1
-    constexpr int EV = DV / 64;
-    float x[RW][EV];
-    if constexpr (kVStaged) {
-      RawT* stv = reinterpret_cast<RawT*>(sA);  // [67][DV] staged v rows over A, which the solve no longer reads
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < NSV; ++i) store_staged(stv, DV, t + i * NT, xv[i]);
-      if (seq_first)
-#pragma unroll
-        for (int i = 0; i < NSV; ++i) store_halo(stv, DV, chv, t + i * NT);
-      __syncthreads();
-      conv_rows<DV, false, RW>([&](int rr, int j, int d) { return to_f32(stv[(RW * wave + rr + j) * DV + d]); },
-                                  cwv, p.raw.act, x);
-    } else {
-      const RawT* rv = static_cast<const RawT*>(p.raw.v);
-      const int64_t wv = (int64_t)H * DV, rel0 = start - t0 + RW * wave;
-      conv_rows<DV, false, RW>([&](int rr, int j, int d) {
-        const int64_t pos = rel0 + rr - 3 + j;
-        if (RW * wave + rr >= len) return 0.f;
-        return pos >= 0 ? to_f32(rv[(t0 + pos) * wv + (int64_t)h * DV + d]) : to_f32(raw_cs[(3 + pos) * Cch + chv + d]);
-      }, cwv, p.raw.act, x);
-    }
-#pragma unroll
-    for (int rr = 0; rr < RW; ++rr) {
-      const int r = RW * wave + rr;
-#pragma unroll
-      for (int e = 0; e < EV; ++e) sQ[r * PK + EV * lane + e] = r < len ? sBeta[r] * x[rr][e] : 0.f;
-    }
-  } else {
+      for (int i = 0; i < NSV; ++i) store_halo(stv, DV, chv, t + i * NT);
+  } else if constexpr (!FUSED) {
     for (int idx = t; idx < L * (DV / 4); idx += NT) {
       const int r = idx / (DV / 4), c4 = 4 * (idx % (DV / 4));
       float4 vv = {0.f, 0.f, 0.f, 0.f};
@@ -1109,25 +1053,169 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
     }
   }
   __syncthreads();
+  write_afrags<POL, NT>(rec + rl.Pf, 4, 2, [&](int r, int i) { return sP[r * PL + i]; });
+  __syncthreads();  // P's last read: X takes its tile
 
-  {
-    FB fv[PFV];
+  // 6 and 7 side by side.  X = (I + A)^{-1} goes into the P tile.  Only wavefronts 0..3 take
+  // part in the solve, so the right-hand sides of step 8, which do not depend on X, are formed
+  // by the other wavefronts meanwhile, as B-operand fragments of the intra products (an item
+  // (column tile c, 32-row block kb, lane) holds 8 rows of one column):
+  //   b_r e^{G_r} k_r (wavefronts 4..15, while the diagonal blocks are solved) into T2,
+  //   b_r v_r (wavefronts 8..15, while the blocks below the diagonal are solved) into T0.
+  // e^{G_r} k_r is e^{G_{16R}} (k_r e^{gl_r}) from the factors of step 5, or formed directly
+  // from the chunk prefix G_r on the exact path.
+  // X's strictly-upper blocks keep the zeros of P's (step 8 reads blocks (0,1) and (2,3));
+  // the solve writes the diagonal and lower blocks only.
+  float* sXi = sP;
+  using FI = Frag<IP>;
+  using FB = typename FI::B;
+  constexpr int NFK = (DK / 16) * 2 * 64, NFV = (DV / 16) * 2 * 64;
+  constexpr int EV = DV / 64, NKT = NT - 4 * 64, PFK = (NFK + NKT - 1) / NKT;  // b e^G k items per thread
+  static_assert(NW == 16, "wavefront roles: 4 solve, 12 b e^G k, 8 of them b v");
+  FB fk[PFK];
+  if (wave < 4) {  // diagonal block R = wavefront, by forward substitution
+    // lane 4 cc + qq owns column cc, rows 4 qq .. 4 qq + 3 of the block.  Right-looking:
+    // once x_r is final it is broadcast in the lane quad and every later row takes its
+    // term, in the order r = 0, 1, ... (rows at or above r see a zero of A's strictly
+    // lower block and keep their value).
+    const int R = wave, b0 = 16 * R, cc = lane >> 2, qq = lane & 3;
+    float xv4[4];
 #pragma unroll
-    for (int i = 0; i < PFV; ++i) {
-      const int item = t + i * NT;
-      if (item < NFV) {
-        const int ln = item & 63, kb = (item >> 6) & 1, c = item >> 7;
-        const int d = 16 * c + (ln & 15), g = ln >> 4;
-        float x[8];
+    for (int j = 0; j < 4; ++j) xv4[j] = (4 * qq + j == cc) ? 1.f : 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = sQ[(32 * kb + FI::kof(g, e)) * PK + d];
-        fv[i] = FI::make_b(x);
+    for (int r = 0; r < 16; ++r) {
+      constexpr int kQuad[4] = {0x00, 0x55, 0xAA, 0xFF};  // quad_perm broadcast of lane 0..3 of each quad
+      float x = xv4[r & 3];
+      if ((r >> 2) == 0) x = dpp_partner<kQuad[0]>(x);
+      else if ((r >> 2) == 1) x = dpp_partner<kQuad[1]>(x);
+      else if ((r >> 2) == 2) x = dpp_partner<kQuad[2]>(x);
+      else x = dpp_partner<kQuad[3]>(x);
+      x = (r >= cc) ? x : 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xv4[j] = fmaf(-sA[(b0 + 4 * qq + j) * PL + b0 + r], x, xv4[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sXi[(b0 + 4 * qq + j) * PL + b0 + cc] = xv4[j];
+  } else {
+    // exact path: T2 holds the chunk prefix G_r (its high part); else e^{G_{16R}} times the factor k e^{gl}
+    auto fk_item = [&](int item, auto&& elem) {
+      const int ln = item & 63, kb = (item >> 6) & 1, c = item >> 7;
+      const int d = 16 * c + (ln & 15), g = ln >> 4;
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = elem(32 * kb + FI::kof(g, e), d);
+      return FI::make_b(x);
+    };
+    if (exact) {
+#pragma unroll
+      for (int i = 0; i < PFK; ++i)
+        if ((t - 256) + i * NKT < NFK)
+          fk[i] = fk_item((t - 256) + i * NKT, [&](int r, int d) {
+            return sBeta[r] * (sK[r * PK + d] * pexp<POL>(sG[r * PK + d]));
+          });
+    } else if constexpr (FI::kof(1, 0) == 8) {
+      // an item's 8 rows r0 .. r0 + 7 are consecutive and lie in one 16-row block: its b_r
+      // load as two 16-byte vectors and e^{G_{16R}} once
+#pragma unroll
+      for (int i = 0; i < PFK; ++i) {
+        const int item = (t - 256) + i * NKT;
+        if (item < NFK) {
+          const int ln = item & 63, kb = (item >> 6) & 1, c = item >> 7;
+          const int d = 16 * c + (ln & 15), r0 = 32 * kb + 8 * (ln >> 4);
+          const float4 b0 = *reinterpret_cast<const float4*>(&sBeta[r0]);
+          const float4 b1 = *reinterpret_cast<const float4*>(&sBeta[r0 + 4]);
+          const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+          const float ge = sGFe[(r0 >> 4) * DK + d];
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = bb[e] * (FT::load1(sK, r0 + e, d) * ge);
+          fk[i] = FI::make_b(x);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < PFK; ++i)
+        if ((t - 256) + i * NKT < NFK)
+          fk[i] = fk_item((t - 256) + i * NKT, [&](int r, int d) {
+            return sBeta[r] * (FT::load1(sK, r, d) * sGFe[(r >> 4) * DK + d]);
+          });
+    }
+  }
+  __syncthreads();  // the diagonal blocks of X are final; every read of T0 and T2 is done
+  if (wave < 3) {
+    // column I = wavefront of X below the diagonal, on the matrix cores (fp32), nearest block first:
+    //   Y = sum_{J=I}^{R-1} A_RJ X_JI,  X_RI = -X_RR Y
+    // Block (R, I) reads the blocks above it in its own column, which this wavefront wrote
+    // (a wavefront's LDS accesses take effect in program order), and X_RR, final at the barrier.
+    const int I = wave, col = lane & 15, g4 = lane >> 4;
+    float* yb = sY + wave * 16 * 17;  // this wavefront's own scratch: written, then read back in order
+    for (int R = I + 1; R < 4; ++R) {
+      floatx4 y = {0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 16 * I; k0 < 16 * R; k0 += 4)
+        y = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[(16 * R + col) * PL + k0 + g4], sXi[(k0 + g4) * PL + 16 * I + col],
+                                                 y, 0, 0, 0);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) yb[(4 * g4 + v) * 17 + col] = y[v];
+      floatx4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k0 = 0; k0 < 16; k0 += 4)
+        x = __builtin_amdgcn_mfma_f32_16x16x4f32(sXi[(16 * R + col) * PL + 16 * R + k0 + g4], yb[(k0 + g4) * 17 + col],
+                                                 x, 0, 0, 0);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sXi[(16 * R + 4 * g4 + v) * PL + 16 * I + col] = -x[v];
+    }
+  } else if (wave >= 4) {
+#pragma unroll
+    for (int i = 0; i < PFK; ++i)
+      if ((t - 256) + i * NKT < NFK) put_frag(sG, NFK, (t - 256) + i * NKT, fk[i]);
+    if (wave >= 8) {
+      // v wavefront 8 + 4 kb + g takes chunk rows 32 kb + kof(g, e), e < 8, and writes one
+      // fragment per column; lane l holds columns EV l .. EV l + EV - 1
+      const int vkb = (wave - 8) >> 2, vg = wave & 3;
+      auto vrow = [&](int e) { return 32 * vkb + FI::kof(vg, e); };
+      float x[8][EV];
+      if constexpr (FUSED) {  // conv (no norm) of the wavefront's 8 rows, then b_r v_r
+        if constexpr (kVStaged) {
+          const RawT* stv = reinterpret_cast<const RawT*>(sQ);
+          conv_rows<DV, false, 8>([&](int rr, int j, int d) { return to_f32(stv[(vrow(rr) + j) * DV + d]); }, cwv,
+                                  p.raw.act, x);
+        } else {
+          const RawT* rv = static_cast<const RawT*>(p.raw.v);
+          const int64_t wv = (int64_t)H * DV, rel0 = start - t0;
+          conv_rows<DV, false, 8>([&](int rr, int j, int d) {
+            const int64_t pos = rel0 + vrow(rr) - 3 + j;
+            if (vrow(rr) >= len) return 0.f;
+            return pos >= 0 ? to_f32(rv[(t0 + pos) * wv + (int64_t)h * DV + d]) : to_f32(raw_cs[(3 + pos) * Cch + chv + d]);
+          }, cwv, p.raw.act, x);
+        }
+        float bb[8];
+        if constexpr (FI::kof(1, 0) == 8) {  // 8 consecutive rows: b_r as two 16-byte vectors
+          const float4 b0 = *reinterpret_cast<const float4*>(&sBeta[vrow(0)]);
+          const float4 b1 = *reinterpret_cast<const float4*>(&sBeta[vrow(4)]);
+          bb[0] = b0.x; bb[1] = b0.y; bb[2] = b0.z; bb[3] = b0.w; bb[4] = b1.x; bb[5] = b1.y; bb[6] = b1.z; bb[7] = b1.w;
+        } else {
+#pragma unroll
+          for (int rr = 0; rr < 8; ++rr) bb[rr] = sBeta[vrow(rr)];
+        }
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr)
+#pragma unroll
+          for (int e = 0; e < EV; ++e) x[rr][e] = vrow(rr) < len ? bb[rr] * x[rr][e] : 0.f;
+      } else {
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr)
+#pragma unroll
+          for (int e = 0; e < EV; ++e) x[rr][e] = sQ[vrow(rr) * PK + EV * lane + e];
+      }
+#pragma unroll
+      for (int e = 0; e < EV; ++e) {
+        float y[8];
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) y[rr] = x[rr][e];
+        const int d = EV * lane + e;
+        put_frag(sK, NFV, ((d >> 4) * 2 + vkb) * 64 + (d & 15) + 16 * vg, FI::make_b(y));
       }
     }
-    // T0 (k e^{gl}, or k) was last read before the barrier above
-#pragma unroll
-    for (int i = 0; i < PFV; ++i)
-      if (t + i * NT < NFV) put_frag(sK, NFV, t + i * NT, fv[i]);
   }
   __syncthreads();
 
@@ -1138,7 +1226,7 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
   {
     constexpr int NTW = DK / 16, NTU = DV / 16, NTT = NTW + NTU;
     // right-hand side fragments: b e^{G} k in T2 (NFK items), b v in T0 (NFV items)
-    float* sW = sQ;  // b v rows in T1 are consumed
+    float* sW = sQ;  // the v rows in T1 are consumed
     constexpr int WPR = NW / 4, TPW = NTT / WPR;  // wavefronts per row block, column tiles per wavefront
     static_assert(NTT % WPR == 0, "column tiles split evenly");
     const int R = 3 - wave / WPR, part = wave % WPR, KBR = (16 * (R + 1) + 31) / 32;
