@@ -36,6 +36,7 @@
 //   FP16    A operands (W, Q^gamma, P, K_<^T: every entry bounded by 1) rounded
 //           once to fp16; B operands (state, U) split into fp16 hi + lo
 #include <mutex>
+#include <type_traits>
 
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
@@ -1149,21 +1150,37 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
     // (a wavefront's LDS accesses take effect in program order), and X_RR, final at the barrier.
     const int I = wave, col = lane & 15, g4 = lane >> 4;
     float* yb = sY + wave * 16 * 17;  // this wavefront's own scratch: written, then read back in order
-    for (int R = I + 1; R < 4; ++R) {
+    // block (I + D, I) with a compile-time K = 16 D, so that all of its operands are read from
+    // LDS before the products that use them
+    auto block = [&](auto dist) {
+      constexpr int D = decltype(dist)::value;
+      const int R = I + D;
+      float ao[4 * D], xo[4 * D];
+#pragma unroll
+      for (int j = 0; j < 4 * D; ++j) {
+        ao[j] = sA[(16 * R + col) * PL + 16 * I + 4 * j + g4];
+        xo[j] = sXi[(16 * I + 4 * j + g4) * PL + 16 * I + col];
+      }
       floatx4 y = {0.f, 0.f, 0.f, 0.f};
-      for (int k0 = 16 * I; k0 < 16 * R; k0 += 4)
-        y = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[(16 * R + col) * PL + k0 + g4], sXi[(k0 + g4) * PL + 16 * I + col],
-                                                 y, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 4 * D; ++j) y = __builtin_amdgcn_mfma_f32_16x16x4f32(ao[j], xo[j], y, 0, 0, 0);
 #pragma unroll
       for (int v = 0; v < 4; ++v) yb[(4 * g4 + v) * 17 + col] = y[v];
+      float xr[4], yr[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        xr[j] = sXi[(16 * R + col) * PL + 16 * R + 4 * j + g4];
+        yr[j] = yb[(4 * j + g4) * 17 + col];
+      }
       floatx4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k0 = 0; k0 < 16; k0 += 4)
-        x = __builtin_amdgcn_mfma_f32_16x16x4f32(sXi[(16 * R + col) * PL + 16 * R + k0 + g4], yb[(k0 + g4) * 17 + col],
-                                                 x, 0, 0, 0);
+      for (int j = 0; j < 4; ++j) x = __builtin_amdgcn_mfma_f32_16x16x4f32(xr[j], yr[j], x, 0, 0, 0);
 #pragma unroll
       for (int v = 0; v < 4; ++v) sXi[(16 * R + 4 * g4 + v) * PL + 16 * I + col] = -x[v];
-    }
+    };
+    block(std::integral_constant<int, 1>{});
+    if (I < 2) block(std::integral_constant<int, 2>{});
+    if (I < 1) block(std::integral_constant<int, 3>{});
   } else if (wave >= 4) {
 #pragma unroll
     for (int i = 0; i < PFK; ++i)
