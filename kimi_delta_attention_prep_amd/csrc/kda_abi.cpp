@@ -126,6 +126,24 @@ hipError_t ensure_dynamic_lds(const void* kernel, size_t bytes) {
   return e;
 }
 
+hipError_t device_cus(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::mutex mu;
+  static std::map<int, int> known;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = known.find(dev);
+  if (it == known.end()) {
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    it = known.emplace(dev, n > 0 ? n : 1).first;
+  }
+  *cus = it->second;
+  return hipSuccess;
+}
+
 static_assert(kNoAllocScratchBytes == KDA_NOALLOC_SCRATCH_BYTES, "scratch size as the header states it");
 
 }  // namespace kda

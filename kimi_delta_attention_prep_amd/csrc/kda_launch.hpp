@@ -13,6 +13,8 @@ namespace kda {
 // the process, under a lock, so host threads that make their first calls at the
 // same time, or calls on several devices, each find it set before they launch.
 hipError_t ensure_dynamic_lds(const void* kernel, size_t bytes);
+// number of compute units of the calling thread's current device (queried once per device)
+hipError_t device_cus(int* cus);
 
 struct RowsLaunch {
   int H, dk, dv, in_dtype, act, gate_mode, batch, window;

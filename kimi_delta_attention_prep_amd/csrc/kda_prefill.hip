@@ -387,6 +387,8 @@ struct PrefillArgs {
   float* sink;         // [256] target of stores that must not land in o
   uint8_t* recs;       // [max_chunks][H][rec bytes]
   int64_t rec_bytes;
+  int lookahead;       // intra-chunk workgroups resident at once (one per CU): item b + lookahead
+                       // runs after item b, on the same XCD
 };
 
 // ---------------------------------------------------------------------------
@@ -1181,56 +1183,85 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
     block(std::integral_constant<int, 1>{});
     if (I < 2) block(std::integral_constant<int, 2>{});
     if (I < 1) block(std::integral_constant<int, 3>{});
-  } else if (wave >= 4) {
-#pragma unroll
-    for (int i = 0; i < PFK; ++i)
-      if ((t - 256) + i * NKT < NFK) put_frag(sG, NFK, (t - 256) + i * NKT, fk[i]);
-    if (wave >= 8) {
-      // v wavefront 8 + 4 kb + g takes chunk rows 32 kb + kof(g, e), e < 8, and writes one
-      // fragment per column; lane l holds columns EV l .. EV l + EV - 1
-      const int vkb = (wave - 8) >> 2, vg = wave & 3;
-      auto vrow = [&](int e) { return 32 * vkb + FI::kof(vg, e); };
-      float x[8][EV];
-      if constexpr (FUSED) {  // conv (no norm) of the wavefront's 8 rows, then b_r v_r
-        if constexpr (kVStaged) {
-          const RawT* stv = reinterpret_cast<const RawT*>(sQ);
-          conv_rows<DV, false, 8>([&](int rr, int j, int d) { return to_f32(stv[(vrow(rr) + j) * DV + d]); }, cwv,
-                                  p.raw.act, x);
-        } else {
-          const RawT* rv = static_cast<const RawT*>(p.raw.v);
-          const int64_t wv = (int64_t)H * DV, rel0 = start - t0;
-          conv_rows<DV, false, 8>([&](int rr, int j, int d) {
-            const int64_t pos = rel0 + vrow(rr) - 3 + j;
-            if (vrow(rr) >= len) return 0.f;
-            return pos >= 0 ? to_f32(rv[(t0 + pos) * wv + (int64_t)h * DV + d]) : to_f32(raw_cs[(3 + pos) * Cch + chv + d]);
-          }, cwv, p.raw.act, x);
+  } else {
+    if constexpr (FUSED) {
+      // Wavefronts 3..7 have little to do here: they read one word of every 128-byte line of
+      // the raw q and k rows that item b + lookahead (the next to run on this XCD) reads
+      // first, so that those rows wait in the XCD's L2 when its workgroup starts, instead
+      // of every CU's first loads meeting in HBM at once.  The words are waited for here,
+      // inside this interval, so no later wait on the in-order memory counter includes them.
+      const int64_t it2 = (int64_t)blockIdx.x + p.lookahead;
+      if (wave < 8 && p.lookahead > 0 && it2 < (int64_t)gridDim.x) {
+        const int c2 = (int)(it2 / H), h2 = (int)(it2 % H);
+        const int n2 = slot_seq(p.cu, p.num_seqs, c2);
+        const int64_t t02 = p.cu[n2], s2 = t02 + (c2 - slot_base(p.cu, n2)) * L, e2 = p.cu[n2 + 1];
+        if (s2 < e2) {
+          constexpr int LPR = (int)(DK * sizeof(RawT) / 128);  // 128-byte lines per row of a stream
+          constexpr int NL = 2 * (L + 3) * LPR;
+          uint32_t acc = 0;
+          for (int li = t - 192; li < NL; li += 320) {
+            const int st = li / ((L + 3) * LPR), rem = li % ((L + 3) * LPR), sr = rem / LPR, part = rem % LPR;
+            int64_t pos = s2 - 3 + sr;
+            pos = pos < t02 ? t02 : (pos >= e2 ? e2 - 1 : pos);  // within the sequence's rows
+            const RawT* src = static_cast<const RawT*>(st ? p.raw.k : p.raw.q);
+            acc += *reinterpret_cast<const uint32_t*>(src + pos * ((int64_t)H * DK) + (int64_t)h2 * DK +
+                                                      part * (128 / (int)sizeof(RawT)));
+          }
+          asm volatile("" ::"v"(acc));
         }
-        float bb[8];
-        if constexpr (FI::kof(1, 0) == 8) {  // 8 consecutive rows: b_r as two 16-byte vectors
-          const float4 b0 = *reinterpret_cast<const float4*>(&sBeta[vrow(0)]);
-          const float4 b1 = *reinterpret_cast<const float4*>(&sBeta[vrow(4)]);
-          bb[0] = b0.x; bb[1] = b0.y; bb[2] = b0.z; bb[3] = b0.w; bb[4] = b1.x; bb[5] = b1.y; bb[6] = b1.z; bb[7] = b1.w;
-        } else {
-#pragma unroll
-          for (int rr = 0; rr < 8; ++rr) bb[rr] = sBeta[vrow(rr)];
-        }
-#pragma unroll
-        for (int rr = 0; rr < 8; ++rr)
-#pragma unroll
-          for (int e = 0; e < EV; ++e) x[rr][e] = vrow(rr) < len ? bb[rr] * x[rr][e] : 0.f;
-      } else {
-#pragma unroll
-        for (int rr = 0; rr < 8; ++rr)
-#pragma unroll
-          for (int e = 0; e < EV; ++e) x[rr][e] = sQ[vrow(rr) * PK + EV * lane + e];
       }
+    }
+    if (wave >= 4) {
 #pragma unroll
-      for (int e = 0; e < EV; ++e) {
-        float y[8];
+      for (int i = 0; i < PFK; ++i)
+        if ((t - 256) + i * NKT < NFK) put_frag(sG, NFK, (t - 256) + i * NKT, fk[i]);
+      if (wave >= 8) {
+        // v wavefront 8 + 4 kb + g takes chunk rows 32 kb + kof(g, e), e < 8, and writes one
+        // fragment per column; lane l holds columns EV l .. EV l + EV - 1
+        const int vkb = (wave - 8) >> 2, vg = wave & 3;
+        auto vrow = [&](int e) { return 32 * vkb + FI::kof(vg, e); };
+        float x[8][EV];
+        if constexpr (FUSED) {  // conv (no norm) of the wavefront's 8 rows, then b_r v_r
+          if constexpr (kVStaged) {
+            const RawT* stv = reinterpret_cast<const RawT*>(sQ);
+            conv_rows<DV, false, 8>([&](int rr, int j, int d) { return to_f32(stv[(vrow(rr) + j) * DV + d]); }, cwv,
+                                    p.raw.act, x);
+          } else {
+            const RawT* rv = static_cast<const RawT*>(p.raw.v);
+            const int64_t wv = (int64_t)H * DV, rel0 = start - t0;
+            conv_rows<DV, false, 8>([&](int rr, int j, int d) {
+              const int64_t pos = rel0 + vrow(rr) - 3 + j;
+              if (vrow(rr) >= len) return 0.f;
+              return pos >= 0 ? to_f32(rv[(t0 + pos) * wv + (int64_t)h * DV + d]) : to_f32(raw_cs[(3 + pos) * Cch + chv + d]);
+            }, cwv, p.raw.act, x);
+          }
+          float bb[8];
+          if constexpr (FI::kof(1, 0) == 8) {  // 8 consecutive rows: b_r as two 16-byte vectors
+            const float4 b0 = *reinterpret_cast<const float4*>(&sBeta[vrow(0)]);
+            const float4 b1 = *reinterpret_cast<const float4*>(&sBeta[vrow(4)]);
+            bb[0] = b0.x; bb[1] = b0.y; bb[2] = b0.z; bb[3] = b0.w; bb[4] = b1.x; bb[5] = b1.y; bb[6] = b1.z; bb[7] = b1.w;
+          } else {
 #pragma unroll
-        for (int rr = 0; rr < 8; ++rr) y[rr] = x[rr][e];
-        const int d = EV * lane + e;
-        put_frag(sK, NFV, ((d >> 4) * 2 + vkb) * 64 + (d & 15) + 16 * vg, FI::make_b(y));
+            for (int rr = 0; rr < 8; ++rr) bb[rr] = sBeta[vrow(rr)];
+          }
+#pragma unroll
+          for (int rr = 0; rr < 8; ++rr)
+#pragma unroll
+            for (int e = 0; e < EV; ++e) x[rr][e] = vrow(rr) < len ? bb[rr] * x[rr][e] : 0.f;
+        } else {
+#pragma unroll
+          for (int rr = 0; rr < 8; ++rr)
+#pragma unroll
+            for (int e = 0; e < EV; ++e) x[rr][e] = sQ[vrow(rr) * PK + EV * lane + e];
+        }
+#pragma unroll
+        for (int e = 0; e < EV; ++e) {
+          float y[8];
+#pragma unroll
+          for (int rr = 0; rr < 8; ++rr) y[rr] = x[rr][e];
+          const int d = EV * lane + e;
+          put_frag(sK, NFV, ((d >> 4) * 2 + vkb) * 64 + (d & 15) + 16 * vg, FI::make_b(y));
+        }
       }
     }
   }
@@ -1593,6 +1624,11 @@ static hipError_t launch_prefill_t(const PrefillLaunch& Lc, hipStream_t s) {
   p.raw = {Lc.raw_q, Lc.raw_k, Lc.raw_v, Lc.raw_g, Lc.raw_beta, Lc.conv_w, Lc.cs_in, Lc.cs_out,
            Lc.act, Lc.gate_mode, Lc.lb, FUSED ? (int)sizeof(RawT) : 0, Lc.g_per_head};
   p.sink = static_cast<float*>(Lc.workspace);
+  p.lookahead = 0;
+  if (FUSED) {
+    const hipError_t ec = device_cus(&p.lookahead);
+    if (ec != hipSuccess) return ec;
+  }
   p.recs = static_cast<uint8_t*>(Lc.workspace) + kSinkBytes;
   p.rec_bytes = rec_layout(DK, DV, Frag<POL>::BYTES).bytes;
   // measurement hook: an event just before / after kernel i
