@@ -24,6 +24,7 @@ pass also give their fraction of it.
 Modes besides the default run:
   --copy-calibration   also time a plain 1 GiB device copy (for counter runs:
                        the copy's FETCH_SIZE / WRITE_SIZE scale the kernels')
+  --verify-only        only the verify-window line (for profiler runs of its kernel)
   --pmc-summary F W    turn two rocprofv3 --pmc runs (FETCH_SIZE, then
                        WRITE_SIZE; their counter_collection.csv files) into
                        the committed traffic summary
@@ -230,6 +231,8 @@ def main():
     ap.add_argument("--workload", choices=("prefill", "varlen"), default="prefill",
                     help="the timed prompt workload: T=4096 H=16 (the metric's), or the 8 packed sequences at H=32 "
                          "(for profiler runs of that workload's kernels)")
+    ap.add_argument("--verify-only", action="store_true",
+                    help="only the verify-window line (B=64, window <= 4, H=32), for profiler runs of its kernel")
     ap.add_argument("--copy-calibration", action="store_true", help="also run a plain 1 GiB device copy")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--pmc-command", default="", help="the counter command, stored in the summary")
@@ -253,6 +256,10 @@ def main():
     K.load_library()
     dev = "cuda"
     stream = torch.cuda.current_stream()
+
+    if args.verify_only:
+        print(json.dumps({"verify_window": verify_windows(stream, args.steps, args.warmup)}))
+        return
 
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)

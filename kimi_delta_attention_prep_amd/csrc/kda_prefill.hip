@@ -675,14 +675,14 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
     RawT* stk = stq + (L + 3) * DK;
     const int64_t wk = (int64_t)H * DK;
     const int64_t chq = (int64_t)h * DK, chk = wk + (int64_t)h * DK;
-    // q loads first and alone; k loads once q has landed and lands while q is
-    // convolved; g and beta load while k is convolved.  The workgroups of a round
-    // start together, so the first load of every CU meets the others' in HBM:
-    // keeping that burst to the q rows gets q in sooner.
+    // q and k load first (the workgroup that ran before on this XCD touched them
+    // into L2, below); g, beta and v load once q is convolved and land while k is.
     uint4 xq[NSK], xk[NSK], xg[NGK];
     RawT xgh[NGK];
 #pragma unroll
     for (int i = 0; i < NSK; ++i) xq[i] = load_staged(static_cast<const RawT*>(p.raw.q), DK, t + i * NT);
+#pragma unroll
+    for (int i = 0; i < NSK; ++i) xk[i] = load_staged(static_cast<const RawT*>(p.raw.k), DK, t + i * NT);
     // each stream's conv weights load right after its rows (a wait for them is then no
     // longer than the wait for the rows)
     const ConvW<DK> cwq = load_conv_w<DK>(p.raw.conv_w + chq * 4);
@@ -705,8 +705,6 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
 #pragma unroll
       for (int i = 0; i < NSK; ++i) store_halo(stq, DK, chq, t + i * NT);
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < NSK; ++i) xk[i] = load_staged(static_cast<const RawT*>(p.raw.k), DK, t + i * NT);
     const ConvW<DK> cwk = load_conv_w<DK>(p.raw.conv_w + chk * 4);
     conv_stream(stq, sQ, cwq);
 #pragma unroll
