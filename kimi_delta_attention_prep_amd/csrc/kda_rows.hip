@@ -75,31 +75,51 @@ struct RowStep {
   float* s_pq;   // [NW][DV]
   float* s_scal; // [4]: beta
 
+  // The raw inputs of one row that this thread uses: q, k, g of channel t (t < DK),
+  // v of channel t - DK (DK <= t < DK + DV), beta (t = 0).  Every thread loads all
+  // five, from clamped indices, so that no load sits in a branch (a load inside a
+  // branch is waited for where the branches join) and a row's inputs can be
+  // loaded while the previous row computes.
+  struct RowIn {
+    RawT q, k, g, v, beta;
+  };
+  __device__ RowIn load_in(const RowsArgs<RawT>& p, int64_t row_hd_k, int64_t row_hd_v, int64_t row_h) {
+    const int t = threadIdx.x;
+    const int tk = t < DK ? t : 0, tv = (t >= DK && t < DK + DV) ? t - DK : 0;
+    RowIn in;
+    in.q = p.q[row_hd_k + tk];
+    in.k = p.k[row_hd_k + tk];
+    in.g = p.g[p.g_per_head ? row_h : row_hd_k + tk];
+    in.v = p.v[row_hd_v + tv];
+    in.beta = p.beta[row_h];
+    return in;
+  }
+
   // Preamble of one row: conv step (history shifts by the new raw row), gates,
   // norms.  Leaves normalised q, k, conv v, decay a and beta in LDS and returns q.k.
-  __device__ float preamble(const RowsArgs<RawT>& p, ChanHist<RawT>& ch, int64_t row_hd_k, int64_t row_hd_v,
-                            int64_t row_h, RawT& raw_q, RawT& raw_k) {
+  __device__ float preamble(const RowsArgs<RawT>& p, ChanHist<RawT>& ch, const RowIn& in, RawT& raw_q,
+                            RawT& raw_k) {
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     float cq = 0.f, ck = 0.f;
     if (t < DK) {
-      raw_q = p.q[row_hd_k + t];
-      raw_k = p.k[row_hd_k + t];
+      raw_q = in.q;
+      raw_k = in.k;
       cq = conv4_act(ch.wq[0], ch.wq[1], ch.wq[2], ch.wq[3], to_f32(ch.hq[0]), to_f32(ch.hq[1]),
                      to_f32(ch.hq[2]), to_f32(raw_q), p.act);
       ck = conv4_act(ch.wk[0], ch.wk[1], ch.wk[2], ch.wk[3], to_f32(ch.hk[0]), to_f32(ch.hk[1]),
                      to_f32(ch.hk[2]), to_f32(raw_k), p.act);
       ch.hq[0] = ch.hq[1]; ch.hq[1] = ch.hq[2]; ch.hq[2] = raw_q;
       ch.hk[0] = ch.hk[1]; ch.hk[1] = ch.hk[2]; ch.hk[2] = raw_k;
-      s_a[t] = expf(log_decay(to_f32(p.g[p.g_per_head ? row_h : row_hd_k + t]), p.gate_mode, p.lb));
+      s_a[t] = expf(log_decay(to_f32(in.g), p.gate_mode, p.lb));
     } else if (t < DK + DV) {
       const int j = t - DK;
-      raw_q = p.v[row_hd_v + j];
+      raw_q = in.v;
       const float cv = conv4_act(ch.wq[0], ch.wq[1], ch.wq[2], ch.wq[3], to_f32(ch.hq[0]), to_f32(ch.hq[1]),
                                  to_f32(ch.hq[2]), to_f32(raw_q), p.act);
       ch.hq[0] = ch.hq[1]; ch.hq[1] = ch.hq[2]; ch.hq[2] = raw_q;
       s_v[j] = cv;
     }
-    if (t == 0) s_scal[0] = sigmoid(to_f32(p.beta[row_h]));
+    if (t == 0) s_scal[0] = sigmoid(to_f32(in.beta));
     // L2 norms over d_k (only the DK/64 wavefronts holding q/k channels contribute)
     const float sq = wave_sum(cq * cq), sk = wave_sum(ck * ck);
     if (lane == 0) { s_red[wave * 8 + 0] = sq; s_red[wave * 8 + 1] = sk; }
@@ -197,7 +217,10 @@ __global__ __launch_bounds__(256) void kda_rows_kernel(RowsArgs<RawT> p) {
   const int64_t C = (int64_t)H * (2 * DK + DV);
   const int cg = t % SH::CG, rg = t / SH::CG;
 
-  __shared__ float s_q[DK], s_k[DK], s_v[DV], s_a[DK];
+  __shared__ __align__(16) float s_q[DK];
+  __shared__ __align__(16) float s_k[DK];
+  __shared__ __align__(16) float s_v[DV];
+  __shared__ __align__(16) float s_a[DK];
   __shared__ float s_red[SH::NW * 8];
   __shared__ __align__(16) float s_pk[SH::NW * DV];
   __shared__ __align__(16) float s_pq[SH::NW * DV];
@@ -235,25 +258,50 @@ __global__ __launch_bounds__(256) void kda_rows_kernel(RowsArgs<RawT> p) {
   }
 
   if constexpr (VERIFY) {
-    // 3. commit n_commit rows of the previous window from its log
+    // 3. commit n_commit rows of the previous window from its log.  A row's decay
+    //    and key (one element per thread) and update (16 bytes per thread) go
+    //    through LDS, and every thread reads back the entries of its state rows;
+    //    the next row's log entries load while the current row is applied.
     int nc = (p.n_commit && p.in_window > 0) ? p.n_commit[b] : 0;
     nc = nc < 0 ? 0 : (nc > p.in_window ? p.in_window : nc);
-    for (int r = 0; r < nc; ++r) {
-      const int64_t base_k = (((int64_t)b * p.in_window + r) * H + h) * DK;
-      const int64_t base_v = (((int64_t)b * p.in_window + r) * H + h) * DV;
-      const float4 u = *reinterpret_cast<const float4*>(p.in_u + base_v + 4 * cg);
+    {
+      const int tk = t < DK ? t : (t < 2 * DK ? t - DK : 0);  // a (t < DK) or k (DK <= t < 2 DK) of channel tk
+      const int tu = t < DV / 4 ? t : 0;                      // 4 entries of u
+      auto log_row = [&](int r, float& av, float4& uv, RawT& rq, RawT& rk) {
+        const int rr = r < nc ? r : (nc > 0 ? nc - 1 : 0);  // clamped: every load is unconditional
+        const int64_t base_k = (((int64_t)b * p.in_window + rr) * H + h) * DK;
+        const int64_t base_v = (((int64_t)b * p.in_window + rr) * H + h) * DV;
+        av = (t < DK ? p.in_a : p.in_k)[base_k + tk];
+        uv = *reinterpret_cast<const float4*>(p.in_u + base_v + 4 * tu);
+        const RawT* rows = p.in_rows + ((int64_t)b * p.in_window + rr) * C;
+        rq = rows[cq_ch >= 0 ? cq_ch : 0];
+        rk = rows[ck_ch >= 0 ? ck_ch : 0];
+      };
+      float av;
+      float4 uv;
+      RawT rq, rk;
+      if (nc > 0) log_row(0, av, uv, rq, rk);
+      for (int r = 0; r < nc; ++r) {
+        if (t < DK) s_a[t] = av;
+        else if (t < 2 * DK) s_k[t - DK] = av;
+        if (t < DV / 4) *reinterpret_cast<float4*>(&s_v[4 * t]) = uv;
+        const RawT cur_q = rq, cur_k = rk;
+        log_row(r + 1, av, uv, rq, rk);
+        __syncthreads();
+        const float4 u = *reinterpret_cast<const float4*>(&s_v[4 * cg]);
 #pragma unroll
-      for (int m = 0; m < SH::RPT; ++m) {
-        const int i = rg + SH::RG * m;
-        const float a = p.in_a[base_k + i], ki = p.in_k[base_k + i];
-        float4 s = S[m];
-        s.x = rank1(decay(s.x, a), ki, u.x); s.y = rank1(decay(s.y, a), ki, u.y);
-        s.z = rank1(decay(s.z, a), ki, u.z); s.w = rank1(decay(s.w, a), ki, u.w);
-        S[m] = s;
+        for (int m = 0; m < SH::RPT; ++m) {
+          const int i = rg + SH::RG * m;
+          const float a = s_a[i], ki = s_k[i];
+          float4 s = S[m];
+          s.x = rank1(decay(s.x, a), ki, u.x); s.y = rank1(decay(s.y, a), ki, u.y);
+          s.z = rank1(decay(s.z, a), ki, u.z); s.w = rank1(decay(s.w, a), ki, u.w);
+          S[m] = s;
+        }
+        if (cq_ch >= 0) { ch.hq[0] = ch.hq[1]; ch.hq[1] = ch.hq[2]; ch.hq[2] = cur_q; }
+        if (ck_ch >= 0) { ch.hk[0] = ch.hk[1]; ch.hk[1] = ch.hk[2]; ch.hk[2] = cur_k; }
+        __syncthreads();  // the next row overwrites the LDS entries this row read
       }
-      const RawT* rows = p.in_rows + ((int64_t)b * p.in_window + r) * C;
-      if (cq_ch >= 0) { ch.hq[0] = ch.hq[1]; ch.hq[1] = ch.hq[2]; ch.hq[2] = rows[cq_ch]; }
-      if (ck_ch >= 0) { ch.hk[0] = ch.hk[1]; ch.hk[1] = ch.hk[2]; ch.hk[2] = rows[ck_ch]; }
     }
     if (nc > 0) {
 #pragma unroll
@@ -270,10 +318,18 @@ __global__ __launch_bounds__(256) void kda_rows_kernel(RowsArgs<RawT> p) {
       const int wl = p.wlen[b];
       nrow = wl < 0 ? 0 : (wl > p.window ? p.window : wl);
     }
+    auto row_in = [&](int r) {  // clamped: every load is unconditional
+      const int64_t row_h = ((int64_t)b * p.window + (r < nrow ? r : (nrow > 0 ? nrow - 1 : 0))) * H + h;
+      return rs.load_in(p, row_h * DK, row_h * DV, row_h);
+    };
+    typename RowStep<DK, DV, RawT>::RowIn nx{};
+    if (nrow > 0) nx = row_in(0);
     for (int r = 0; r < nrow; ++r) {
       const int64_t row_h = ((int64_t)b * p.window + r) * H + h;
+      const typename RowStep<DK, DV, RawT>::RowIn in = nx;
+      nx = row_in(r + 1);  // the next row's inputs load while this row computes
       RawT raw_q{}, raw_k{};
-      const float qk = rs.preamble(p, ch, row_h * DK, row_h * DV, row_h, raw_q, raw_k);
+      const float qk = rs.preamble(p, ch, in, raw_q, raw_k);
       float4 u, o;
       rs.step(S, qk, u, o);
       if (rg == 0) {
@@ -295,7 +351,7 @@ __global__ __launch_bounds__(256) void kda_rows_kernel(RowsArgs<RawT> p) {
     // decode: one row, committed at once
     const int64_t row_h = (int64_t)b * H + h;
     RawT raw_q{}, raw_k{};
-    const float qk = rs.preamble(p, ch, row_h * DK, row_h * DV, row_h, raw_q, raw_k);
+    const float qk = rs.preamble(p, ch, rs.load_in(p, row_h * DK, row_h * DV, row_h), raw_q, raw_k);
     float4 u, o;
     rs.step(S, qk, u, o);
 #pragma unroll
