@@ -51,10 +51,14 @@ __device__ __forceinline__ float sigmoid(float x) {
 }
 
 // per-key-dim log decay g: softplus gate g = -softplus(x) = -(max(x,0) + log1p(e^-|x|));
-// safe gate g = lb * sigmoid(x), so a = e^g lies in (e^lb, 1)
+// safe gate g = lb * sigmoid(x), so a = e^g lies in (e^lb, 1).  The softplus term uses
+// the hardware exp2 and log2 (each within about one ulp): with y = e^-|x| in (0, 1],
+// log1p(y) = log2(1 + y) ln 2, whose only loss beyond those is the rounding of 1 + y,
+// at most 2^-24 absolute in g
 __device__ __forceinline__ float log_decay(float x, int gate_mode, float lb) {
   if (gate_mode == 1) return lb * sigmoid(x);
-  return -(fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x))));
+  const float y = __builtin_amdgcn_exp2f(fabsf(x) * -1.4426950408889634f);
+  return -(fmaxf(x, 0.0f) + __builtin_amdgcn_logf(1.0f + y) * 0.6931471805599453f);
 }
 
 // depthwise causal conv over 4 taps (x0 oldest, x3 current row), then SiLU when ACT
