@@ -226,7 +226,7 @@ def main():
                     help="only the prompt pass and B=256 decode (for profiler runs: the extra lines launch the same "
                          "kernels on other shapes)")
     ap.add_argument("--unfused", action="store_true", help="run kda_prep separately instead of inside the prompt pass")
-    ap.add_argument("--precision", choices=("fp16", "bf16x3", "fp32"), default="fp16",
+    ap.add_argument("--precision", choices=("fp16", "bf16x2", "bf16x3", "fp32"), default="fp16",
                     help="arithmetic of the prompt path's matrix products (see kda_precision)")
     ap.add_argument("--workload", choices=("prefill", "varlen"), default="prefill",
                     help="the timed prompt workload: T=4096 H=16 (the metric's), or the 8 packed sequences at H=32 "
@@ -371,8 +371,9 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-PRECISIONS = {"fp16": lambda K: K.PREC_FP16, "bf16x3": lambda K: K.PREC_BF16X3, "fp32": lambda K: K.PREC_FP32}
-DTYPE_NAMES = {"fp16": "fp16", "bf16x3": "bf16", "fp32": "f32"}
+PRECISIONS = {"fp16": lambda K: K.PREC_FP16, "bf16x2": lambda K: K.PREC_BF16X2, "bf16x3": lambda K: K.PREC_BF16X3,
+              "fp32": lambda K: K.PREC_FP32}
+DTYPE_NAMES = {"fp16": "fp16", "bf16x2": "bf16", "bf16x3": "bf16", "fp32": "f32"}
 
 
 def time_prompt_pass(stream, w, prec, steps, warmup, unfused=False):

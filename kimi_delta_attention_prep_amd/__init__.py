@@ -27,7 +27,7 @@ KDA_OK, KDA_E_ARG, KDA_E_GEOMETRY, KDA_E_ALIGN, KDA_E_GATE, KDA_E_DTYPE, KDA_E_W
 DTYPE_F32, DTYPE_BF16 = 0, 1
 GATE_SOFTPLUS, GATE_SAFE = 0, 1
 ACT_NONE, ACT_SILU = 0, 1
-PREC_FP32, PREC_BF16X3, PREC_FP16 = 0, 1, 2
+PREC_FP32, PREC_BF16X3, PREC_FP16, PREC_BF16X2 = 0, 1, 2, 3
 DECAY_PER_DIM, DECAY_PER_HEAD = 0, 1
 EXPORTS = ("kda_prep", "kda_prefill_workspace_bytes", "kda_prefill_varlen", "kda_prefill_varlen_noalloc",
            "kda_decode", "kda_verify_window", "gated_rmsnorm_out", "kda_last_error", "kda_set_timing_events")

@@ -65,7 +65,8 @@ int check_dims(const kda_dims* d) {
     return fail(KDA_E_DTYPE, "unknown in_dtype %d", d->in_dtype);
   if (d->conv_act != KDA_ACT_NONE && d->conv_act != KDA_ACT_SILU)
     return fail(KDA_E_DTYPE, "unknown conv_act %d", d->conv_act);
-  if (d->precision != KDA_PREC_FP32 && d->precision != KDA_PREC_BF16X3 && d->precision != KDA_PREC_FP16)
+  if (d->precision != KDA_PREC_FP32 && d->precision != KDA_PREC_BF16X3 && d->precision != KDA_PREC_FP16 &&
+      d->precision != KDA_PREC_BF16X2)
     return fail(KDA_E_DTYPE, "unknown precision %d", d->precision);
   if (d->decay_shape != KDA_DECAY_PER_DIM && d->decay_shape != KDA_DECAY_PER_HEAD)
     return fail(KDA_E_GEOMETRY, "unknown decay shape %d", d->decay_shape);

@@ -35,6 +35,8 @@
 //   BF16X3  operands split into bf16 hi + lo, hi*hi + hi*lo + lo*hi
 //   FP16    A operands (W, Q^gamma, P, K_<^T: every entry bounded by 1) rounded
 //           once to fp16; B operands (state, U) split into fp16 hi + lo
+//   BF16X2  as FP16 with bf16 in place of fp16: A operands rounded once to bf16,
+//           B operands split into bf16 hi + lo, so state and U keep the fp32 range
 #include <mutex>
 #include <type_traits>
 
@@ -43,7 +45,7 @@
 
 namespace kda {
 
-enum { POL_FP32 = 0, POL_BF16X3 = 1, POL_FP16 = 2 };
+enum { POL_FP32 = 0, POL_BF16X3 = 1, POL_FP16 = 2, POL_BF16X2 = 3 };
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
@@ -278,6 +280,76 @@ struct Frag<POL_FP16> {
   }
 };
 
+// One-part bf16 A operands and two-part bf16 B operands: the record layout and the
+// product count of FP16, with the fp32 range (bf16 keeps fp32's exponent) for the
+// state and U; A entries are bounded by 1, so one bf16 part costs only precision
+// (2^-9 relative, against fp16's 2^-11).
+template <>
+struct Frag<POL_BF16X2> {
+  static constexpr int BYTES = 16;
+  __device__ static constexpr int kof(int g, int e) { return 8 * g + e; }
+  struct A { bf16x8 v; };
+  struct B { bf16x8 hi, lo; };
+  __device__ static A load_a(const uint8_t* p) {
+    A a;
+    a.v = *reinterpret_cast<const bf16x8*>(p);
+    return a;
+  }
+  __device__ static void store_a(uint8_t* p, const float (&x)[8]) {
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = static_cast<__bf16>(x[e]);
+    *reinterpret_cast<bf16x8*>(p) = v;
+  }
+  // elements 4 half .. 4 half + 3 of an A fragment (two lanes write one fragment)
+  __device__ static void store_a_half(uint8_t* p, int half, const float (&x)[4]) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    bf16x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = static_cast<__bf16>(x[e]);
+    *reinterpret_cast<bf16x4*>(p + 8 * half) = v;
+  }
+  __device__ static B make_b(const float (&x)[8]) {
+    B b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      __bf16 h, l;
+      split_bf16(x[e], h, l);
+      b.hi[e] = h; b.lo[e] = l;
+    }
+    return b;
+  }
+  __device__ static floatx4 mma(floatx4 acc, const A& a, const B& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.lo, acc, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.hi, acc, 0, 0, 0);
+  }
+  __device__ static floatx4 mma_t(floatx4 acc, const B& b, const A& a) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b.lo, a.v, acc, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(b.hi, a.v, acc, 0, 0, 0);
+  }
+  // B operand kept in LDS already split: hi and lo planes [16 columns][K] of bf16
+  using P = __bf16;
+  static constexpr int PLANES = 2;
+  __device__ static void store_b4(P* hi, P* lo, const floatx4& x) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    bf16x4 h, l;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      __bf16 a, b;
+      split_bf16(x[e], a, b);
+      h[e] = a; l[e] = b;
+    }
+    *reinterpret_cast<bf16x4*>(hi) = h;
+    *reinterpret_cast<bf16x4*>(lo) = l;
+  }
+  __device__ static B load_b(const P* hi, const P* lo, int g) {
+    B b;
+    b.hi = *reinterpret_cast<const bf16x8*>(hi + 8 * g);
+    b.lo = *reinterpret_cast<const bf16x8*>(lo + 8 * g);
+    return b;
+  }
+};
+
 // the intra-chunk kernel's own products: fp32 for the FP32 policy, split bf16 otherwise
 template <int POL>
 struct IntraPol { static constexpr int value = POL == POL_FP32 ? POL_FP32 : POL_BF16X3; };
@@ -330,7 +402,7 @@ __host__ __device__ inline RecLayout rec_layout(int dk, int dv, int fb) {
   r.bytes = (r.gL + (int64_t)dk * 4 + 255) / 256 * 256;
   return r;
 }
-static inline int frag_bytes(int precision) { return precision == POL_FP16 ? 16 : 32; }
+static inline int frag_bytes(int precision) { return precision == POL_FP16 || precision == POL_BF16X2 ? 16 : 32; }
 // workspace: a 1 KiB sink that absorbs stores of rows past a sequence's end, then the records
 constexpr size_t kSinkBytes = 1024;
 
@@ -1674,6 +1746,7 @@ hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t s) {
   if (L.dk == DK_ && L.dv == DV_) {                                                 \
     if (L.precision == POL_FP32) return launch_prefill_pol<DK_, DV_, POL_FP32>(L, s); \
     if (L.precision == POL_FP16) return launch_prefill_pol<DK_, DV_, POL_FP16>(L, s); \
+    if (L.precision == POL_BF16X2) return launch_prefill_pol<DK_, DV_, POL_BF16X2>(L, s); \
     return launch_prefill_pol<DK_, DV_, POL_BF16X3>(L, s);                          \
   }
   KDA_PF_CASE(64, 64)

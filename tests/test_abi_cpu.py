@@ -64,6 +64,17 @@ def test_geometry_and_dtype_rejected_before_launch(lib, d, code):
     assert lib.kda_last_error()  # a message is left
 
 
+def test_every_precision_policy_accepted(lib):
+    """The four policies pass the argument checks; 4 is refused. FP16 and BF16X2 keep one 16-byte
+    fragment per A operand, BF16X3 and FP32 two, so their workspaces are the larger."""
+    ws = {p: lib.kda_prefill_workspace_bytes(ctypes.byref(dims(prec=p)), 2, 1000)
+          for p in (K.PREC_FP32, K.PREC_BF16X3, K.PREC_FP16, K.PREC_BF16X2)}
+    assert all(v > 0 for v in ws.values())
+    assert ws[K.PREC_FP16] == ws[K.PREC_BF16X2] < ws[K.PREC_BF16X3] == ws[K.PREC_FP32]
+    assert lib.kda_prefill_workspace_bytes(ctypes.byref(dims(prec=4)), 2, 1000) == 0
+    assert decode(lib, dims(prec=4)) == K.KDA_E_DTYPE
+
+
 @pytest.mark.parametrize("gate,lb,code", [
     (9, -5.0, K.KDA_E_GATE), (K.GATE_SAFE, 0.0, K.KDA_E_GATE), (K.GATE_SAFE, 1.0, K.KDA_E_GATE),
     (K.GATE_SAFE, float("nan"), K.KDA_E_GATE), (K.GATE_SAFE, -math.inf, K.KDA_E_GATE),

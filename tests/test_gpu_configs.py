@@ -25,7 +25,8 @@ def prefill_ref():
     return w, oracle_layer(w)
 
 
-@pytest.mark.parametrize("precision,fused", [(K.PREC_BF16X3, False), (K.PREC_FP16, True), (K.PREC_FP32, False)])
+@pytest.mark.parametrize("precision,fused", [(K.PREC_BF16X3, False), (K.PREC_FP16, True), (K.PREC_FP32, False),
+                                             (K.PREC_BF16X2, True)])
 def test_prefill_T4096_H16_full_oracle(prefill_ref, precision, fused):
     w, ref = prefill_ref
     print(f"prefill workload T={w.T} H={w.H} precision={precision} fused={fused}", flush=True)
@@ -35,7 +36,7 @@ def test_prefill_T4096_H16_full_oracle(prefill_ref, precision, fused):
     assert all(e < TOL_BF16 for e in errs.values()), errs
 
 
-@pytest.mark.parametrize("precision,fused", [(K.PREC_BF16X3, False), (K.PREC_FP16, True)])
+@pytest.mark.parametrize("precision,fused", [(K.PREC_BF16X3, False), (K.PREC_FP16, True), (K.PREC_BF16X2, True)])
 def test_varlen_8_sequences_H32_head_subset(precision, fused):
     w = I.varlen()
     print(f"varlen workload T={w.T} lengths={torch.diff(w.cu_seqlens).tolist()}", flush=True)

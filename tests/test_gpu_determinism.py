@@ -25,7 +25,7 @@ def _poison(kind):
     del x
 
 
-@pytest.mark.parametrize("precision", [K.PREC_FP16, K.PREC_BF16X3])
+@pytest.mark.parametrize("precision", [K.PREC_FP16, K.PREC_BF16X2, K.PREC_BF16X3])
 @pytest.mark.parametrize("fused", [False, True])
 def test_prompt_pass_repeats_bitwise(precision, fused):
     lens = [1500, 64, 1, 2531]  # 4096 rows, ragged chunk tails

@@ -319,7 +319,7 @@ def test_prefill_many_ragged_sequences(dk, dv, precision, fused):
         assert per_seq[n] < TOL_BF16, f"sequence {n} (length {lens[n]})"
 
 
-@pytest.mark.parametrize("precision", [K.PREC_FP32, K.PREC_BF16X3, K.PREC_FP16])
+@pytest.mark.parametrize("precision", [K.PREC_FP32, K.PREC_BF16X3, K.PREC_FP16, K.PREC_BF16X2])
 def test_prefill_precision_policies_on_bf16_rows(precision):
     w = small(torch.bfloat16, lens=(300, 77), H=2, d=128, gate=I.GATE_SAFE, seed=21)
     r = gpu_layer_prefill(w, precision=precision)

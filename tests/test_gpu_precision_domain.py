@@ -3,7 +3,7 @@
 FP16 rounds the per-chunk operands (every entry bounded by 1) once to fp16 and splits each state and
 update entry x into fp16 hi + lo.  While |x| < 65504 (the largest finite fp16 value) the pair keeps x to
 within max(2^-22 |x|, 2^-25); beyond it the split overflows, and the call's outputs are then not finite
-(the failure is loud, never a finite wrong value).  BF16X3 and FP32 keep the fp32 range.  The layer is
+(the failure is loud, never a finite wrong value).  BF16X2, BF16X3 and FP32 keep the fp32 range.  The layer is
 linear in (S0, v) only up to the conv activation, so the tests scale S0 directly and scale v's raw rows
 by powers of two (exact in bf16)."""
 import pytest
@@ -37,7 +37,7 @@ def _errs(w, precision):
     return r, {"o": rel(r["o"], ref.o), "state": rel(r["state"], ref.state)}
 
 
-@pytest.mark.parametrize("precision", [K.PREC_FP16, K.PREC_BF16X3, K.PREC_FP32])
+@pytest.mark.parametrize("precision", [K.PREC_FP16, K.PREC_BF16X2, K.PREC_BF16X3, K.PREC_FP32])
 @pytest.mark.parametrize("state_std,v_scale", [(300.0, 1.0), (0.0, 2.0 ** -8)])
 def test_state_magnitudes_inside_the_fp16_range(precision, state_std, v_scale):
     """Entries far from unit magnitude but inside FP16's range: S0 ~ N(0, 300^2) (state and update
@@ -47,7 +47,7 @@ def test_state_magnitudes_inside_the_fp16_range(precision, state_std, v_scale):
     assert all(e < TOL_BF16 for e in errs.values()), errs
 
 
-@pytest.mark.parametrize("precision", [K.PREC_BF16X3, K.PREC_FP32])
+@pytest.mark.parametrize("precision", [K.PREC_BF16X2, K.PREC_BF16X3, K.PREC_FP32])
 def test_state_beyond_the_fp16_range_under_fp32_range_policies(precision):
     r, errs = _errs(_workload(1e6), precision)
     print(f"precision {precision} S0 std 1e6: {errs}", flush=True)

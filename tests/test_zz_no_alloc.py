@@ -32,7 +32,7 @@ def _pass(w, precision, noalloc):
     return {"o": o, "state": state, "conv_state": cs, "y": y}
 
 
-@pytest.mark.parametrize("precision", [K.PREC_FP16, K.PREC_BF16X3])
+@pytest.mark.parametrize("precision", [K.PREC_FP16, K.PREC_BF16X2, K.PREC_BF16X3])
 def test_noalloc_prompt_call_twice_then_smaller(precision):
     assert torch.cuda.is_available()
     K.load_library()
