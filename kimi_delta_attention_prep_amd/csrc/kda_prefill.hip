@@ -1380,8 +1380,9 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
 // ---------------------------------------------------------------------------
 // inter-chunk scan
 //
-// Workgroup = (sequence, head, 16 state columns j0..j0+15), 8 wavefronts in two
-// roles, so that only the state recurrence sits on the serial path.  State
+// Workgroup = (sequence, head, CB blocks of 16 state columns from j0), 8
+// wavefronts in two roles, so that only the state recurrence sits on the serial
+// path.  State
 // wavefront w (0..3) owns chunk rows 16w..16w+15 of U and state rows
 // 16*(w*DK/64 + s) + 0..15 (s < DK/64), kept as fp32 matrix-core accumulators;
 // output wavefront 4 + w owns chunk rows 16w..16w+15 of O.  Per chunk c, with
@@ -1392,26 +1393,33 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
 // barriers per chunk order every write after the last read of the old
 // contents, so one buffer of each suffices.  Each wavefront keeps NS register
 // sets of its operand fragments and loads chunk c+NS-1 while chunk c computes.
+//
+// With CB = 2 a workgroup takes two column blocks and each wavefront applies
+// its W, K_<^T, Q^gamma and P fragments to both: half the operand traffic per
+// state column, for a chain twice as long per chunk.  Each column's arithmetic
+// is the same as with CB = 1, so both give the same bits.  It pays where the
+// operand loads bound the scan, that is where the workgroups fill every CU.
 // ---------------------------------------------------------------------------
-template <int DK, int POL>
+template <int DK, int POL, int CB>
 struct ScanSmem {
   using P = typename Frag<POL>::P;
   static constexpr int NP = Frag<POL>::PLANES;
   // row strides padded by 32 bytes (16 bytes measured slower on the LDS)
   static constexpr int PS = DK + 32 / sizeof(P);  // S^T row stride (one row per state column)
   static constexpr int PU = 64 + 32 / sizeof(P);  // U^T row stride
-  static constexpr int S_PLANE = 16 * PS, U_PLANE = 16 * PU;
+  static constexpr int S_PLANE = 16 * CB * PS, U_PLANE = 16 * CB * PU;
   static constexpr size_t BYTES = (size_t)(NP * S_PLANE + NP * U_PLANE) * sizeof(P);
+  static_assert(BYTES <= 65536, "the scan runs with the default LDS limit");
 };
 
 // one chunk's operand fragments of a state wavefront: the state chain's
 // operands (W, U~, K_<^T, gamma_L)
-template <int DK, int POL>
+template <int DK, int POL, int CB>
 struct StateFrags {
   using F = Frag<POL>;
   static constexpr int KB = DK / 32, MS = DK / 64;
   typename F::A w[KB], k[MS][2];
-  floatx4 ut;
+  floatx4 ut[CB];
   float4 gl[MS];
   // in three groups, so that each iteration can spread its loads over the chunk
   __device__ void load_w(const uint8_t* rec, const RecLayout& rl, int w4, int lane) {
@@ -1419,8 +1427,11 @@ struct StateFrags {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) w[kb] = F::load_a(rec + rl.Wf + ((int64_t)(w4 * KB + kb) * 64 + lane) * FB);
   }
-  __device__ void load_ug(const uint8_t* rec, const RecLayout& rl, int w4, int lane, int split) {
-    ut = *reinterpret_cast<const floatx4*>(rec + rl.Ut + ((int64_t)(split * 4 + w4) * 64 + lane) * 16);
+  // split0: the workgroup's first 16-column block
+  __device__ void load_ug(const uint8_t* rec, const RecLayout& rl, int w4, int lane, int split0) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+      ut[cb] = *reinterpret_cast<const floatx4*>(rec + rl.Ut + ((int64_t)((split0 + cb) * 4 + w4) * 64 + lane) * 16);
 #pragma unroll
     for (int s = 0; s < MS; ++s)
       gl[s] = *reinterpret_cast<const float4*>(rec + rl.gL + (int64_t)(16 * (w4 * MS + s) + 4 * (lane >> 4)) * 4);
@@ -1433,9 +1444,9 @@ struct StateFrags {
       for (int kb = 0; kb < 2; ++kb)
         k[s][kb] = F::load_a(rec + rl.Kf + ((int64_t)((w4 * MS + s) * 2 + kb) * 64 + lane) * FB);
   }
-  __device__ void load(const uint8_t* rec, const RecLayout& rl, int w4, int lane, int split) {
+  __device__ void load(const uint8_t* rec, const RecLayout& rl, int w4, int lane, int split0) {
     load_w(rec, rl, w4, lane);
-    load_ug(rec, rl, w4, lane, split);
+    load_ug(rec, rl, w4, lane, split0);
     load_k(rec, rl, w4, lane);
   }
 };
@@ -1514,14 +1525,14 @@ __device__ __forceinline__ void carry_conv_state(const PrefillArgs& p, int n, in
   }
 }
 
-template <int DK, int DV, int POL>
+template <int DK, int DV, int POL, int CB>
 __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillArgs p, int groups) {
-  using SM = ScanSmem<DK, POL>;
+  using SM = ScanSmem<DK, POL, CB>;
   using F = Frag<POL>;
   using P = typename F::P;
   constexpr int L = kChunk, PS = SM::PS, PU = SM::PU;
-  constexpr int NSPLIT = DV / 16, KB = DK / 32, MS = DK / 64;
-  constexpr int NS = F::BYTES == 16 ? 3 : 2;  // register sets of operand fragments
+  constexpr int NSPLIT = DV / (16 * CB), KB = DK / 32, MS = DK / 64;
+  constexpr int NS = F::BYTES == 16 && CB == 1 ? 3 : 2;  // register sets of operand fragments
   extern __shared__ __align__(16) float smem_f[];
   P* smem = reinterpret_cast<P*>(smem_f);
 
@@ -1535,7 +1546,7 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillArgs p, int grou
   if (slot < 0) return;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, w4 = wave & 3;
   const int col = lane & 15, g4 = lane >> 4;
-  const int j0 = 16 * split;
+  const int j0 = 16 * CB * split;
   if (p.raw.esize) carry_conv_state<DK, DV>(p, n_seq, slot, h * NSPLIT + split, H * NSPLIT);
   const RecLayout rl = rec_layout(DK, DV, F::BYTES);
   float* Sg = p.state + ((int64_t)slot * H + h) * DK * DV;
@@ -1543,10 +1554,24 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillArgs p, int grou
   P* sS1 = smem + (SM::NP - 1) * SM::S_PLANE;
   P* sU0 = smem + SM::NP * SM::S_PLANE;
   P* sU1 = sU0 + (SM::NP - 1) * SM::U_PLANE;
-  auto put_s = [&](int row0, const floatx4& x) { F::store_b4(sS0 + col * PS + row0, sS1 + col * PS + row0, x); };
-  auto put_u = [&](int row0, const floatx4& x) { F::store_b4(sU0 + col * PU + row0, sU1 + col * PU + row0, x); };
-  auto get_s = [&](int kb) { return F::load_b(sS0 + col * PS + 32 * kb, sS1 + col * PS + 32 * kb, g4); };
-  auto get_u = [&](int kb) { return F::load_b(sU0 + col * PU + 32 * kb, sU1 + col * PU + 32 * kb, g4); };
+  // S^T and U^T rows per state column: column 16 cb + col of the workgroup's block (the row
+  // offsets stay separate pointer steps, so that they fold into the LDS instructions' offsets)
+  P* const sSc0 = sS0 + col * PS;
+  P* const sSc1 = sS1 + col * PS;
+  P* const sUc0 = sU0 + col * PU;
+  P* const sUc1 = sU1 + col * PU;
+  auto put_s = [&](int cb, int row0, const floatx4& x) {
+    F::store_b4(sSc0 + 16 * cb * PS + row0, sSc1 + 16 * cb * PS + row0, x);
+  };
+  auto put_u = [&](int cb, int row0, const floatx4& x) {
+    F::store_b4(sUc0 + 16 * cb * PU + row0, sUc1 + 16 * cb * PU + row0, x);
+  };
+  auto get_s = [&](int cb, int kb) {
+    return F::load_b(sSc0 + 16 * cb * PS + 32 * kb, sSc1 + 16 * cb * PS + 32 * kb, g4);
+  };
+  auto get_u = [&](int cb, int kb) {
+    return F::load_b(sUc0 + 16 * cb * PU + 32 * kb, sUc1 + 16 * cb * PU + 32 * kb, g4);
+  };
 
   const int64_t c_begin = slot_base(p.cu, n_seq);
   const int n = (int)((p.cu[n_seq + 1] - p.cu[n_seq] + L - 1) / L);
@@ -1565,20 +1590,22 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillArgs p, int grou
   const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
   if (wave < 4) {
     // state wavefronts: U_c = U~_c - W_c S_c, then S_{c+1} = gamma_L . S_c + K_<^T U_c
-    floatx4 Sacc[MS];
+    floatx4 Sacc[CB][MS];
 #pragma unroll
-    for (int s = 0; s < MS; ++s) {
-      const int r0 = 16 * (w4 * MS + s) + 4 * g4;
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) Sacc[s][v] = Sg[(int64_t)(r0 + v) * DV + j0 + col];
-      put_s(r0, Sacc[s]);
-    }
-    StateFrags<DK, POL> fr[NS];
+      for (int s = 0; s < MS; ++s) {
+        const int r0 = 16 * (w4 * MS + s) + 4 * g4;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) Sacc[cb][s][v] = Sg[(int64_t)(r0 + v) * DV + j0 + 16 * cb + col];
+        put_s(cb, r0, Sacc[cb][s]);
+      }
+    StateFrags<DK, POL, CB> fr[NS];
     if (n > 0) {
 #pragma unroll
-      for (int j = 0; j < NS - 1; ++j) fr[j].load(rec_of(clampc(j)), rl, w4, lane, split);
+      for (int j = 0; j < NS - 1; ++j) fr[j].load(rec_of(clampc(j)), rl, w4, lane, CB * split);
     }
-    auto iter = [&](int c, const StateFrags<DK, POL>& cur, StateFrags<DK, POL>& ahead) {
+    auto iter = [&](int c, const StateFrags<DK, POL, CB>& cur, StateFrags<DK, POL, CB>& ahead) {
       // the next-but-one chunk's operands load in three groups (W right after A,
       // U~ and gamma after U is written, K_<^T while U_c^T is read), so no group
       // waits long for the CU's load path
@@ -1586,39 +1613,52 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillArgs p, int grou
       __syncthreads();  // A
       ahead.load_w(nrec, rl, w4, lane);
       __builtin_amdgcn_sched_barrier(0);
-      typename F::B bs[KB];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) bs[kb] = get_s(kb);
-      // one accumulator per K block (chains of one block's products), summed as a tree
-      floatx4 acc[KB];
+      for (int cb = 0; cb < CB; ++cb) {
+        typename F::B bs[KB];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) acc[kb] = F::mma(z4, cur.w[kb], bs[kb]);
-      floatx4 ws = acc[0] + acc[1];
-      if constexpr (KB == 4) ws = ws + (acc[2] + acc[3]);
-      floatx4 u;
+        for (int kb = 0; kb < KB; ++kb) bs[kb] = get_s(cb, kb);
+        // one accumulator per K block (chains of one block's products), summed as a tree
+        floatx4 acc[KB];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) u[v] = cur.ut[v] - ws[v];
-      put_u(16 * w4 + 4 * g4, u);
+        for (int kb = 0; kb < KB; ++kb) acc[kb] = F::mma(z4, cur.w[kb], bs[kb]);
+        floatx4 ws = acc[0] + acc[1];
+        if constexpr (KB == 4) ws = ws + (acc[2] + acc[3]);
+        floatx4 u;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) u[v] = cur.ut[cb][v] - ws[v];
+        put_u(cb, 16 * w4 + 4 * g4, u);
+      }
       __builtin_amdgcn_sched_barrier(0);
-      ahead.load_ug(nrec, rl, w4, lane, split);
+      ahead.load_ug(nrec, rl, w4, lane, CB * split);
       __syncthreads();  // B
-      const typename F::B u0 = get_u(0), u1 = get_u(1);
+      typename F::B u0[CB], u1[CB];
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        u0[cb] = get_u(cb, 0);
+        u1[cb] = get_u(cb, 1);
+      }
       ahead.load_k(nrec, rl, w4, lane);
       __builtin_amdgcn_sched_barrier(0);
-      floatx4 sk[MS];
+      floatx4 sk[CB][MS];
 #pragma unroll
-      for (int s = 0; s < MS; ++s) {
-        const float4 gl = cur.gl[s];
-        Sacc[s][0] *= gl.x; Sacc[s][1] *= gl.y; Sacc[s][2] *= gl.z; Sacc[s][3] *= gl.w;
-        Sacc[s] = F::mma(Sacc[s], cur.k[s][0], u0);
-        sk[s] = F::mma(z4, cur.k[s][1], u1);
-      }
+      for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int s = 0; s < MS; ++s) {
+        for (int s = 0; s < MS; ++s) {
+          const float4 gl = cur.gl[s];
+          floatx4& a = Sacc[cb][s];
+          a[0] *= gl.x; a[1] *= gl.y; a[2] *= gl.z; a[3] *= gl.w;
+          a = F::mma(a, cur.k[s][0], u0[cb]);
+          sk[cb][s] = F::mma(z4, cur.k[s][1], u1[cb]);
+        }
 #pragma unroll
-        for (int v = 0; v < 4; ++v) Sacc[s][v] += sk[s][v];
-        put_s(16 * (w4 * MS + s) + 4 * g4, Sacc[s]);
-      }
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int s = 0; s < MS; ++s) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) Sacc[cb][s][v] += sk[cb][s][v];
+          put_s(cb, 16 * (w4 * MS + s) + 4 * g4, Sacc[cb][s]);
+        }
     };
     const int full = n / NS * NS;
     for (int base = 0; base < full; base += NS) {
@@ -1629,11 +1669,13 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillArgs p, int grou
     for (int u = 0; u < NS - 1; ++u)
       if (full + u < n) iter(full + u, fr[u], fr[(u + NS - 1) % NS]);
 #pragma unroll
-    for (int s = 0; s < MS; ++s) {
-      const int r0 = 16 * (w4 * MS + s) + 4 * g4;
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) Sg[(int64_t)(r0 + v) * DV + j0 + col] = Sacc[s][v];
-    }
+      for (int s = 0; s < MS; ++s) {
+        const int r0 = 16 * (w4 * MS + s) + 4 * g4;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) Sg[(int64_t)(r0 + v) * DV + j0 + 16 * cb + col] = Sacc[cb][s][v];
+      }
   } else {
     // output wavefronts: O_c = Q^gamma_c S_c + P_c U_c for chunk rows 16 w4 .. 16 w4 + 15,
     // formed transposed, O^T = S^T Q^gamma^T + U^T P^T, from the same fragments: lane l
@@ -1648,27 +1690,38 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillArgs p, int grou
       __syncthreads();  // A
       ahead.load_q(nrec, rl, w4, lane);  // the next-but-one chunk's Q^gamma right after A
       __builtin_amdgcn_sched_barrier(0);
-      typename F::B bs[KB];
+      floatx4 ao[CB][2];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) bs[kb] = get_s(kb);
-      floatx4 aq[KB];  // one accumulator per K block, summed in pairs
+      for (int cb = 0; cb < CB; ++cb) {
+        typename F::B bs[KB];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) aq[kb] = F::mma_t(z4, bs[kb], cur.q[kb]);
-      floatx4 ao[2] = {aq[0], aq[1]};
-      if constexpr (KB == 4) {
-        ao[0] = ao[0] + aq[2];
-        ao[1] = ao[1] + aq[3];
+        for (int kb = 0; kb < KB; ++kb) bs[kb] = get_s(cb, kb);
+        floatx4 aq[KB];  // one accumulator per K block, summed in pairs
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) aq[kb] = F::mma_t(z4, bs[kb], cur.q[kb]);
+        ao[cb][0] = aq[0];
+        ao[cb][1] = aq[1];
+        if constexpr (KB == 4) {
+          ao[cb][0] = ao[cb][0] + aq[2];
+          ao[cb][1] = ao[cb][1] + aq[3];
+        }
       }
       __syncthreads();  // B
-      const typename F::B u0 = get_u(0);
-      ao[0] = F::mma_t(ao[0], u0, cur.pp[0]);
-      if (w4 >= 2) ao[1] = F::mma_t(ao[1], get_u(1), cur.pp[1]);  // P is lower triangular
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const typename F::B u0 = get_u(cb, 0);
+        ao[cb][0] = F::mma_t(ao[cb][0], u0, cur.pp[0]);
+        if (w4 >= 2) ao[cb][1] = F::mma_t(ao[cb][1], get_u(cb, 1), cur.pp[1]);  // P is lower triangular
+      }
       const int64_t start = seq_start + (int64_t)c * L;
       const int len = (int)min((int64_t)L, seq_end - start);
       // stores are unconditional: rows past the sequence go to the sink
       const int rr = 16 * w4 + col;
-      float* dst = rr < len ? &p.o[((start + rr) * H + h) * DV + j0 + 4 * g4] : &p.sink[lane * 4];
-      *reinterpret_cast<floatx4*>(dst) = ao[0] + ao[1];
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        float* dst = rr < len ? &p.o[((start + rr) * H + h) * DV + j0 + 16 * cb + 4 * g4] : &p.sink[lane * 4];
+        *reinterpret_cast<floatx4*>(dst) = ao[cb][0] + ao[cb][1];
+      }
       __builtin_amdgcn_sched_barrier(0);
       ahead.load_p(nrec, rl, w4, lane);
     };
@@ -1708,7 +1761,6 @@ static hipError_t launch_prefill_t(const PrefillLaunch& Lc, hipStream_t s) {
   hipError_t e = hipSuccess;
   const int64_t mc = max_chunks(Lc.num_seqs, Lc.t_tot);
   constexpr size_t intra_bytes = IntraSmem<DK, DV>::BYTES;
-  constexpr size_t scan_bytes = ScanSmem<DK, POL>::BYTES;
   e = ensure_dynamic_lds(reinterpret_cast<const void*>(&chunk_intra_kernel<DK, DV, POL, RawT, FUSED>), intra_bytes);
   if (e != hipSuccess) return e;
   e = mark(0, 0);
@@ -1725,9 +1777,20 @@ static hipError_t launch_prefill_t(const PrefillLaunch& Lc, hipStream_t s) {
   e = mark(1, 0);
   if (e != hipSuccess) return e;
   if (groups > 0) {
-    const int nsplit = DV / 16;
-    const int wgs = (groups + 7) / 8 * 8 * nsplit;
-    hipLaunchKernelGGL((chunk_scan_kernel<DK, DV, POL>), dim3((unsigned)wgs), dim3(512), scan_bytes, s, p, groups);
+    // two column blocks per workgroup where the workgroups would still fill every CU
+    // (the scan is then bound by its operand loads); one where they leave CUs idle
+    // (it is then bound by the chain's latency)
+    int cus = 0;
+    e = device_cus(&cus);
+    if (e != hipSuccess) return e;
+    const int padded = (groups + 7) / 8 * 8;
+    if (4 * groups >= cus) {
+      hipLaunchKernelGGL((chunk_scan_kernel<DK, DV, POL, 2>), dim3((unsigned)(padded * (DV / 32))), dim3(512),
+                         (ScanSmem<DK, POL, 2>::BYTES), s, p, groups);
+    } else {
+      hipLaunchKernelGGL((chunk_scan_kernel<DK, DV, POL, 1>), dim3((unsigned)(padded * (DV / 16))), dim3(512),
+                         (ScanSmem<DK, POL, 1>::BYTES), s, p, groups);
+    }
     e = hipGetLastError();
   }
   if (e == hipSuccess) e = mark(1, 1);

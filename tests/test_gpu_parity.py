@@ -414,6 +414,32 @@ def test_prefill_packed_equals_alone_bitwise(precision):
         assert torch.equal(alone["state"][0], full["state"][n])
 
 
+@pytest.mark.parametrize("dk,dv,precision", [(128, 128, K.PREC_FP16), (128, 128, K.PREC_BF16X3),
+                                              (128, 128, K.PREC_BF16X2), (64, 128, K.PREC_FP32),
+                                              (128, 64, K.PREC_FP16)])
+def test_prefill_wide_scan_equals_narrow_bitwise(dk, dv, precision):
+    """With (sequences x heads) at least a quarter of the CU count the scan gives each workgroup two 16-column
+    blocks, otherwise one: 64 sequences x 2 heads (128 groups) packed in one call take the two-block scan, each
+    sequence alone (2 groups) the one-block scan, and every column's arithmetic is the same in both, so o, the
+    state and the conv state agree bit for bit (fused preamble, so the conv-state carry runs in both)."""
+    rng = np.random.default_rng(dk * 3 + dv)
+    lens = rng.integers(1, 200, 64).tolist()
+    lens[5], lens[17] = 64, 128  # chunk multiples
+    w = small(torch.bfloat16, lens=lens, H=2, d=dk, dv=dv, gate=I.GATE_SOFTPLUS, seed=dk + dv + precision)
+    print(f"wide vs narrow scan N={w.N} T={w.T} dk={dk} dv={dv} precision={precision}", flush=True)
+    full = gpu_layer_prefill(w, precision=precision, fused=True)
+    cu = w.cu_seqlens.tolist()
+    for n in range(w.N):
+        sl = slice(cu[n], cu[n + 1])
+        one = I.Workload("one", w.H, w.dk, w.dv, torch.tensor([0, cu[n + 1] - cu[n]], dtype=torch.int32),
+                         w.q[sl], w.k[sl], w.v[sl], w.g[sl], w.beta[sl], w.z[sl], w.conv_w, w.norm_w,
+                         w.state0[n:n + 1], w.conv_state0[n:n + 1], w.gate_mode, w.lower_bound)
+        alone = gpu_layer_prefill(one, precision=precision, fused=True)
+        assert torch.equal(alone["o"], full["o"][sl]), f"sequence {n} (length {lens[n]})"
+        assert torch.equal(alone["state"][0], full["state"][n]), f"sequence {n} (length {lens[n]})"
+        assert torch.equal(alone["prep"]["conv_state"][0], full["prep"]["conv_state"][n])
+
+
 @pytest.mark.parametrize("cut,precision", [(64, K.PREC_BF16X3), (128, K.PREC_BF16X3), (128, K.PREC_FP16)])
 def test_prefill_cut_at_chunk_multiple_is_bitwise(cut, precision):
     w = small(torch.bfloat16, lens=(300,), H=2, d=128, seed=51)
