@@ -1394,11 +1394,12 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
 // contents, so one buffer of each suffices.  Each wavefront keeps NS register
 // sets of its operand fragments and loads chunk c+NS-1 while chunk c computes.
 //
-// With CB = 2 a workgroup takes two column blocks and each wavefront applies
-// its W, K_<^T, Q^gamma and P fragments to both: half the operand traffic per
-// state column, for a chain twice as long per chunk.  Each column's arithmetic
-// is the same as with CB = 1, so both give the same bits.  It pays where the
-// operand loads bound the scan, that is where the workgroups fill every CU.
+// With CB = 2 or 4 a workgroup takes that many column blocks and each wavefront
+// applies its W, K_<^T, Q^gamma and P fragments to all of them: 1/CB of the
+// operand traffic per state column, for a chain CB times as long per chunk.
+// Each column's arithmetic is the same for every CB, so all give the same bits.
+// It pays where the operand loads bound the scan, that is where the workgroups
+// fill every CU.
 // ---------------------------------------------------------------------------
 template <int DK, int POL, int CB>
 struct ScanSmem {
@@ -1777,20 +1778,24 @@ static hipError_t launch_prefill_t(const PrefillLaunch& Lc, hipStream_t s) {
   e = mark(1, 0);
   if (e != hipSuccess) return e;
   if (groups > 0) {
-    // two column blocks per workgroup where the workgroups would still fill every CU
-    // (the scan is then bound by its operand loads); one where they leave CUs idle
-    // (it is then bound by the chain's latency)
+    // several column blocks per workgroup where the workgroups would still fill every
+    // CU (the scan is then bound by its operand loads), one where they leave CUs idle
+    // (it is then bound by the chain's latency); four blocks only with one-part A
+    // fragments, whose registers leave room for them
     int cus = 0;
     e = device_cus(&cus);
     if (e != hipSuccess) return e;
     const int padded = (groups + 7) / 8 * 8;
-    if (4 * groups >= cus) {
-      hipLaunchKernelGGL((chunk_scan_kernel<DK, DV, POL, 2>), dim3((unsigned)(padded * (DV / 32))), dim3(512),
-                         (ScanSmem<DK, POL, 2>::BYTES), s, p, groups);
-    } else {
-      hipLaunchKernelGGL((chunk_scan_kernel<DK, DV, POL, 1>), dim3((unsigned)(padded * (DV / 16))), dim3(512),
-                         (ScanSmem<DK, POL, 1>::BYTES), s, p, groups);
-    }
+    auto launch_scan = [&](auto blocks) {
+      constexpr int CB = decltype(blocks)::value;
+      hipLaunchKernelGGL((chunk_scan_kernel<DK, DV, POL, CB>), dim3((unsigned)(padded * (DV / (16 * CB)))),
+                         dim3(512), (ScanSmem<DK, POL, CB>::BYTES), s, p, groups);
+    };
+    constexpr bool kFour = Frag<POL>::BYTES == 16 && DV % 64 == 0;
+    const int cb = kFour && 2 * groups >= cus ? 4 : 4 * groups >= cus ? 2 : 1;
+    if (cb == 1) launch_scan(std::integral_constant<int, 1>{});
+    else if (cb == 2) launch_scan(std::integral_constant<int, 2>{});
+    else if constexpr (kFour) launch_scan(std::integral_constant<int, 4>{});
     e = hipGetLastError();
   }
   if (e == hipSuccess) e = mark(1, 1);

@@ -414,19 +414,25 @@ def test_prefill_packed_equals_alone_bitwise(precision):
         assert torch.equal(alone["state"][0], full["state"][n])
 
 
-@pytest.mark.parametrize("dk,dv,precision", [(128, 128, K.PREC_FP16), (128, 128, K.PREC_BF16X3),
-                                              (128, 128, K.PREC_BF16X2), (64, 128, K.PREC_FP32),
-                                              (128, 64, K.PREC_FP16)])
-def test_prefill_wide_scan_equals_narrow_bitwise(dk, dv, precision):
-    """With (sequences x heads) at least a quarter of the CU count the scan gives each workgroup two 16-column
-    blocks, otherwise one: 64 sequences x 2 heads (128 groups) packed in one call take the two-block scan, each
-    sequence alone (2 groups) the one-block scan, and every column's arithmetic is the same in both, so o, the
-    state and the conv state agree bit for bit (fused preamble, so the conv-state carry runs in both)."""
-    rng = np.random.default_rng(dk * 3 + dv)
-    lens = rng.integers(1, 200, 64).tolist()
+@pytest.mark.parametrize("dk,dv,precision,blocks", [
+    (128, 128, K.PREC_FP16, 2), (128, 128, K.PREC_FP16, 4), (128, 128, K.PREC_BF16X2, 4),
+    (128, 128, K.PREC_BF16X3, 2), (64, 128, K.PREC_FP32, 2), (128, 64, K.PREC_FP16, 4), (128, 64, K.PREC_BF16X3, 2)])
+def test_prefill_wide_scan_equals_narrow_bitwise(dk, dv, precision, blocks):
+    """The scan gives each workgroup 1, 2 or 4 blocks of 16 state columns: 4 (FP16 and BF16X2 only) where
+    groups = sequences x heads reach half the CU count, 2 where they reach a quarter, else 1.  Enough
+    sequences x 2 heads packed in one call take the `blocks` shape, each sequence alone (2 groups) the one-block
+    shape; every column's arithmetic is the same in all shapes, so o, the state and the conv state agree bit for
+    bit (fused preamble, so the conv-state carry runs in both)."""
+    H = 2
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    N = cus // (4 * H) + 4 if blocks == 2 else cus // (2 * H) + 2
+    assert 4 * N * H >= cus and (blocks == 4) == (2 * N * H >= cus) and 4 * H < cus
+    rng = np.random.default_rng(dk * 3 + dv + blocks)
+    lens = rng.integers(1, 200, N).tolist()
     lens[5], lens[17] = 64, 128  # chunk multiples
-    w = small(torch.bfloat16, lens=lens, H=2, d=dk, dv=dv, gate=I.GATE_SOFTPLUS, seed=dk + dv + precision)
-    print(f"wide vs narrow scan N={w.N} T={w.T} dk={dk} dv={dv} precision={precision}", flush=True)
+    w = small(torch.bfloat16, lens=lens, H=H, d=dk, dv=dv, gate=I.GATE_SOFTPLUS, seed=dk + dv + precision)
+    print(f"scan shapes: {blocks} blocks (N={w.N}, {cus} CUs) vs 1, T={w.T} dk={dk} dv={dv} precision={precision}",
+          flush=True)
     full = gpu_layer_prefill(w, precision=precision, fused=True)
     cu = w.cu_seqlens.tolist()
     for n in range(w.N):
