@@ -1382,10 +1382,9 @@ __global__ __launch_bounds__(kIntraThreads) void chunk_intra_kernel(PrefillArgs 
 //
 // Workgroup = (sequence, head, CB blocks of 16 state columns from j0), 8
 // wavefronts in two roles, so that only the state recurrence sits on the serial
-// path.  State
-// wavefront w (0..3) owns chunk rows 16w..16w+15 of U and state rows
-// 16*(w*DK/64 + s) + 0..15 (s < DK/64), kept as fp32 matrix-core accumulators;
-// output wavefront 4 + w owns chunk rows 16w..16w+15 of O.  Per chunk c, with
+// path.  State wavefront w (0..3) owns chunk rows 16w..16w+15 of U and state
+// rows 16*(w*DK/64 + s) + 0..15 (s < DK/64), kept as fp32 matrix-core
+// accumulators; output wavefront 4 + w owns chunk rows 16w..16w+15 of O.  Per chunk c, with
 // S_c^T and U_c^T slices shared through LDS:
 //   phase 1 (S_c complete):  U_c = U~_c - W_c S_c  (state),  O_c = Q^gamma_c S_c  (output)
 //   phase 2 (U_c complete):  S_{c+1} = gamma_L . S_c + K_<^T U_c  (state),  O_c += P_c U_c  (output)
@@ -1585,9 +1584,9 @@ __global__ __launch_bounds__(512) void chunk_scan_kernel(PrefillArgs p, int grou
   // Both roles walk the chunks in step, two barriers per chunk:
   //   A: S_c^T complete (and every read of U_{c-1}^T done),
   //   B: U_c^T complete (and every read of S_c^T done).
-  // Accumulation chains are split in two (even and odd K blocks, or the two
-  // halves of a sum) and the independent chains are interleaved, so the matrix
-  // cores always have a product to issue while a chain waits on its last one.
+  // Each K block of a product accumulates on its own and the blocks are summed
+  // as a tree, so a chain holds at most two dependent products and the matrix
+  // cores have independent products to issue while one waits.
   const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
   if (wave < 4) {
     // state wavefronts: U_c = U~_c - W_c S_c, then S_{c+1} = gamma_L . S_c + K_<^T U_c
