@@ -196,8 +196,9 @@ typedef struct kda_norm_args {
  *           and the conv state is carried as kda_prep would carry it
  *   norm    NULL, or the output norm (part 5) as the call's epilogue: y gets
  *           the same bits as gated_rmsnorm_out on o would give.  A row's norm
- *           spans all d_v columns, which the scan spreads over several
- *           workgroups, so the epilogue is one more launch on the stream, after
+ *           spans all d_v columns, which the scan spreads over up to eight
+ *           workgroups (16, 32 or 64 columns each, by how many workgroups the
+ *           call has), so the epilogue is one more launch on the stream, after
  *           the scan; rows of a skipped sequence (negative slot) keep their y.
  *   state   fp32 [slots, H, d_k, d_v], read as the initial state and
  *           overwritten with the final state of each sequence
