@@ -446,6 +446,29 @@ def test_prefill_wide_scan_equals_narrow_bitwise(dk, dv, precision, blocks):
         assert torch.equal(alone["prep"]["conv_state"][0], full["prep"]["conv_state"][n])
 
 
+@pytest.mark.parametrize("H,d,precision", [(5, 128, K.PREC_FP16), (3, 64, K.PREC_BF16X3), (5, 64, K.PREC_BF16X2)])
+def test_prefill_odd_heads_against_oracle(H, d, precision):
+    """Head counts that are not powers of two and (sequences x heads) groups that are not a multiple of the
+    eight XCD groups, with enough groups that the scan takes a several-column-block shape (four blocks for
+    the one-part policies at 5 heads, two for BF16X3), ragged lengths: o, y and the state of every sequence
+    against the oracle."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    N = cus // (2 * H) + 3
+    rng = np.random.default_rng(H * 100 + d)
+    lens = rng.integers(1, 150, N).tolist()
+    lens[1], lens[2] = 0, 64
+    w = small(torch.bfloat16, lens=lens, H=H, d=d, gate=I.GATE_SOFTPLUS, seed=H + d)
+    print(f"odd heads N={w.N} H={H} groups={w.N * H} T={w.T} d={d} precision={precision}", flush=True)
+    r = gpu_layer_prefill(w, precision=precision, fused=True)
+    ref = oracle_layer(w)
+    assert rel(r["o"], ref.o) < TOL_BF16
+    assert rel(r["y"], ref.y) < TOL_BF16
+    st = r["state"].cpu().double().numpy()
+    for n in range(w.N):
+        assert rel(st[n], ref.state[n]) < TOL_BF16, f"sequence {n} (length {lens[n]})"
+    assert np.array_equal(r["prep"]["conv_state"].cpu().double().numpy(), ref.prep.conv_state)
+
+
 @pytest.mark.parametrize("cut,precision", [(64, K.PREC_BF16X3), (128, K.PREC_BF16X3), (128, K.PREC_FP16)])
 def test_prefill_cut_at_chunk_multiple_is_bitwise(cut, precision):
     w = small(torch.bfloat16, lens=(300,), H=2, d=128, seed=51)
