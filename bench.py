@@ -87,7 +87,9 @@ def pass_bytes_per_token_head(dk, dv, in_bytes=2, y_bytes=2):
 def prompt_roofline(per_kernel, T, H, dk, dv, N, precision):
     """Roofline entry of a prompt pass for its dominant kernel: the pass's algorithmic bytes (per token-head
     figure x T*H) over that kernel's average launch duration, against the HBM peak (the pass is HBM-bound by
-    its arithmetic intensity).  The kernel's own share of the bytes and FLOPs is reported beside it."""
+    its arithmetic intensity).  The kernel's own share of the bytes and FLOPs is reported beside it.  The
+    counter traffic is the committed summary's, taken on the T=4096, H=16 prompt pass: other workloads get
+    none."""
     dom = max(per_kernel, key=per_kernel.get)
     dom_ms = per_kernel[dom]
     per_unit = pass_bytes_per_token_head(dk, dv)
@@ -95,7 +97,8 @@ def prompt_roofline(per_kernel, T, H, dk, dv, N, precision):
     achieved = per_unit * units / (dom_ms * 1e-3) / 1e9
     kf, kb = kernel_algorithmic(dom, T, H, dk, dv, N=N)
     return {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": committed_traffic(dom, precision),
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": committed_traffic(dom, precision) if (N, T, H, dk, dv) == (1, 4096, 16, 128, 128) else None,
             "basis": "whole-pass algorithmic bytes per token-head x token-heads / dominant kernel launch",
             "bytes_per_token_head": per_unit, "token_heads": units, "ms_per_launch": dom_ms,
             "kernel_share": {"algorithmic_bytes": kb, "algorithmic_flops": kf,
