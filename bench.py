@@ -26,8 +26,8 @@ Modes besides the default run:
                        the copy's FETCH_SIZE / WRITE_SIZE scale the kernels')
   --verify-only        only the verify-window line (for profiler runs of its kernel)
   --pmc-summary F W    turn two rocprofv3 --pmc runs (FETCH_SIZE, then
-                       WRITE_SIZE; their counter_collection.csv files) into
-                       the committed traffic summary
+                       WRITE_SIZE; their counter_collection.csv files) of the
+                       --workload's prompt pass into its committed traffic summary
 """
 from __future__ import annotations
 
@@ -84,12 +84,11 @@ def pass_bytes_per_token_head(dk, dv, in_bytes=2, y_bytes=2):
     return in_bytes * (3 * dk + 2 * dv) + in_bytes + y_bytes * dv
 
 
-def prompt_roofline(per_kernel, T, H, dk, dv, N, precision):
+def prompt_roofline(per_kernel, T, H, dk, dv, N, precision, workload=None):
     """Roofline entry of a prompt pass for its dominant kernel: the pass's algorithmic bytes (per token-head
     figure x T*H) over that kernel's average launch duration, against the HBM peak (the pass is HBM-bound by
     its arithmetic intensity).  The kernel's own share of the bytes and FLOPs is reported beside it.  The
-    counter traffic is the committed summary's, taken on the T=4096, H=16 prompt pass: other workloads get
-    none."""
+    counter traffic is that of the committed summary of the same workload (name and shape), if any."""
     dom = max(per_kernel, key=per_kernel.get)
     dom_ms = per_kernel[dom]
     per_unit = pass_bytes_per_token_head(dk, dv)
@@ -98,7 +97,7 @@ def prompt_roofline(per_kernel, T, H, dk, dv, N, precision):
     kf, kb = kernel_algorithmic(dom, T, H, dk, dv, N=N)
     return {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": committed_traffic(dom, precision) if (N, T, H, dk, dv) == (1, 4096, 16, 128, 128) else None,
+            "traffic": committed_traffic(dom, precision, workload, (N, T, H, dk, dv)),
             "basis": "whole-pass algorithmic bytes per token-head x token-heads / dominant kernel launch",
             "bytes_per_token_head": per_unit, "token_heads": units, "ms_per_launch": dom_ms,
             "kernel_share": {"algorithmic_bytes": kb, "algorithmic_flops": kf,
@@ -118,42 +117,47 @@ def source_digest():
     return h.hexdigest()
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_T4096_H16_decode_B256.json")
+# committed counter summaries per prompt workload (the prefill one also holds decode's kernel)
+TRAFFIC_FILES = {"prefill": os.path.join(ROOT, "profiles", "traffic_prefill_T4096_H16_decode_B256.json"),
+                 "varlen": os.path.join(ROOT, "profiles", "traffic_prefill_varlen_8seq_H32.json")}
 
 
-def committed_traffic(kernel, precision):
-    """HBM bytes per launch of `kernel` from the committed counter summary, or
-    None if there is none, it was taken at another precision policy, or the
-    kernel sources changed since it was taken."""
+def committed_traffic(kernel, precision, workload="prefill", shape=None):
+    """HBM bytes per launch of `kernel` from the workload's committed counter summary, or
+    None if there is none, it was taken on another shape (sequences, rows, heads, d_k, d_v)
+    or at another precision policy, or the kernel sources changed since it was taken."""
     try:
-        t = json.load(open(TRAFFIC_FILE))
-    except (OSError, ValueError):
+        t = json.load(open(TRAFFIC_FILES[workload]))
+    except (KeyError, OSError, ValueError):
         return None
     if t.get("source_sha256") != source_digest() or t.get("precision") != precision:
+        return None
+    if shape is not None and t.get("shape") != list(shape):
         return None
     k = t.get("kernels", {}).get(kernel)
     return None if k is None else k["hbm_bytes_per_launch"]
 
 
-def pmc_summary(fetch_csv, write_csv, command, precision):
+def pmc_summary(fetch_csv, write_csv, command, precision, workload, shape):
     """Per-kernel FETCH_SIZE / WRITE_SIZE (KiB per dispatch) from two rocprofv3
     counter runs, scaled by what the same counters read for the 1 GiB copy."""
     import csv
     from collections import defaultdict
 
     def per_kernel(path, counter):
-        # average per dispatch of each kernel; for the copy, only the dispatches
-        # of the largest grid (the 1 GiB calibration copy)
+        # average per dispatch of each kernel; for the copy, only the 1 GiB calibration copies (the
+        # dispatches within half of the largest count: the workloads' own tensor copies can share
+        # their grid size but move far fewer bytes)
         acc = defaultdict(list)
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] == counter:
-                acc[r["Kernel_Name"]].append((int(r["Grid_Size"]), float(r["Counter_Value"])))
+                acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
         out = {}
         for k, v in acc.items():
             if "copyBuffer" in k:
-                g = max(x[0] for x in v)
-                v = [x for x in v if x[0] == g]
-            out[k] = sum(x[1] for x in v) / len(v)
+                top = max(v)
+                v = [x for x in v if x >= 0.5 * top]
+            out[k] = sum(v) / len(v)
         return out
 
     f, w = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
@@ -169,6 +173,7 @@ def pmc_summary(fetch_csv, write_csv, command, precision):
     keys = {"chunk_intra": "chunk_intra_kernel", "chunk_scan": "chunk_scan_kernel",
             "gated_rmsnorm": "gated_rmsnorm_kernel", "kda_rows (decode)": "kda_rows_kernel"}
     out = {"command": command, "source_sha256": source_digest(), "precision": precision,
+           "workload": workload, "shape": list(shape),
            "copy_calibration": {"kernel": copy, "bytes": COPY_BYTES, "fetch_kib": f.get(copy), "write_kib":
                                 w.get(find(w, "copyBuffer")), "fetch_scale": ff, "write_scale": fw},
            "kernels": {}}
@@ -243,13 +248,16 @@ def main():
     ap.add_argument("--pmc-command", default="", help="the counter command, stored in the summary")
     args = ap.parse_args()
     if args.pmc_summary:
-        out = pmc_summary(*args.pmc_summary, args.pmc_command, args.precision)
-        with open(TRAFFIC_FILE, "w") as fh:
+        from kimi_delta_attention_prep_amd import inputs as I
+        w = I.prefill() if args.workload == "prefill" else I.varlen()
+        out = pmc_summary(*args.pmc_summary, args.pmc_command, args.precision, args.workload,
+                          (w.N, w.T, w.H, w.dk, w.dv))
+        with open(TRAFFIC_FILES[args.workload], "w") as fh:
             json.dump(out, fh, indent=1)
         print(json.dumps(out, indent=1))
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+        print(f"bench.py measures one GPU: there is no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
 
@@ -282,7 +290,7 @@ def main():
     ms = pp["ms_per_step"]
     tokens_per_s = T / (ms * 1e-3)
     flops, bytes_ = prefill_algorithmic(T, H, dk, dv, y_bytes=2)
-    roof = prompt_roofline(pp["kernels_ms"], T, H, dk, dv, w.N, args.precision)
+    roof = prompt_roofline(pp["kernels_ms"], T, H, dk, dv, w.N, args.precision, args.workload)
     out = {
         "metric": "KDA tokens/s: prefill (T=4096,H=16) and decode (B=256); % MFMA/HBM peak",
         "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -460,7 +468,7 @@ def prompt_line(stream, w, precision, steps, warmup, K):
                         f"{'softplus' if w.gate_mode == 0 else 'safe'} gate",
             "matrix_products": precision, "value": T / (pp["ms_per_step"] * 1e-3), "unit": "tokens/s",
             "ms_per_step": pp["ms_per_step"], "steps": steps, "kernels_ms": pp["kernels_ms"],
-            "roofline": prompt_roofline(pp["kernels_ms"], T, H, w.dk, w.dv, w.N, precision)}
+            "roofline": prompt_roofline(pp["kernels_ms"], T, H, w.dk, w.dv, w.N, precision, w.name)}
 
 
 def scalar_decay_prefill(stream, w, prec, steps, warmup):
