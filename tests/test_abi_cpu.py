@@ -296,3 +296,20 @@ def test_noalloc_prompt_call_checks(lib):
     assert call(2, 1000, MIS4) == K.KDA_E_ALIGN  # o is written with 16-byte stores
     assert call(-1, 10) == K.KDA_E_ARG
     assert call(0, 0) == K.KDA_OK  # nothing to do, nothing launched
+
+
+def test_header_and_library_from_plain_c(lib, tmp_path):
+    """include/kda.h compiles as C99 with every warning an error, and a C program linked against libkda.so
+    gets the workspace sizes and the pre-launch argument checks (tests/abi_from_c.c; no GPU needed)."""
+    import shutil
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    exe = tmp_path / "abi_from_c"
+    libdir = os.path.dirname(K.LIB_PATH)
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"),
+                        os.path.join(ROOT, "tests", "abi_from_c.c"), "-o", str(exe), "-L", libdir, "-lkda",
+                        f"-Wl,-rpath,{libdir}"], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
