@@ -142,11 +142,14 @@ def _decode_rows(w, rows, d, state, cs, row_ids, active):
     return torch.stack(outs, 1)  # [B, steps, H, dv]
 
 
-def test_verify_window_replay_is_bitwise_serial_decode():
-    B, W = 5, 4
-    w, rows = _verify_setup(B, W)
+@pytest.mark.parametrize("W,accepted,dk", [(4, [0, 3, 1, 2, 3], 128), (8, [0, 7, 3, 5, 2], 128), (8, [7, 0, 6, 1, 4], 64),
+                                            (1, [0, 0, 0, 0, 0], 128)])
+def test_verify_window_replay_is_bitwise_serial_decode(W, accepted, dk):
+    """Windows of 1, 4 and 8 rows (8 is the longest the library takes)."""
+    B = 5
+    w, rows = _verify_setup(B, W, d=dk)
     d = dims_for(w)
-    accept = torch.tensor([0, 3, 1, 2, 3], dtype=torch.int32)  # rows 0..j kept
+    accept = torch.tensor(accepted, dtype=torch.int32)  # rows 0..j kept
     n_commit = (accept + 1).cuda()
     # verify path: window, then commit-only
     st_v, cs_v = w.state0.cuda().clone(), w.conv_state0.cuda().clone()
